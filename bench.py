@@ -1,0 +1,207 @@
+"""Decode-attention throughput over a low-rank compressed, paged KV cache.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+One step = the whole decode hot path for one layer of one GPU's head share:
+append-encode of each sequence's new token(s), query projection, page routing
+(routed workloads), attention over the chosen pages, and the up-projection.
+Inputs are seeded synthetic caches already resident in HBM. Prints one JSON
+line: KV-tokens/s (sum of context lengths / step time), the roofline of the
+dominant kernel (timed live with HIP events on its own stream), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from decode_attention_rank_amd.session import DecodeSession  # noqa: E402
+from decode_attention_rank_amd.workloads import DEFAULT_BENCH_WORKLOAD, WORKLOADS  # noqa: E402
+
+METRIC = "decode-attn KV-tokens/s over compressed cache + % of HBM peak GB/s (1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+ROUTE_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_route.hip")
+ATTN_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from a committed counter summary, if it is current."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256_16") != source_hash(src):
+        return None  # kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(sess, budget_s: float):
+    """The oracle as it stands, on whole (sequence, KV head) pairs until the
+    time budget is spent; rate scaled to KV-tokens/s of the full step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from tests import gpu_harness as H
+    import oracle as O
+
+    wl = sess.wl
+    order = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    spent, tokens, pairs = 0.0, 0, 0
+    for b, g in order:
+        st_rows = sess.prefix_rows(b)
+        prefix = {k: H.f64(v[g]) for k, v in st_rows.items()}
+        off = sum(sess.n_new[:b])
+        n = sess.n_new[b]
+        Kn = H.f64(sess.k_new[off:off + n, g])
+        Vn = H.f64(sess.v_new[off:off + n, g])
+        f = H.factors_np(sess, g)
+        q = H.q_group(sess, b, g)
+        t0 = time.perf_counter()
+        st = O.append_tokens(prefix, sess.lens_before[b], Kn, Vn, f["A_v"], f["A_k"], f["W_pred"],
+                             key_mode=wl.key_mode, storage=wl.storage)
+        res = O.decode_pair(q, st, f, sess.seq_lens[b], wl.page_size, key_mode=wl.key_mode,
+                            scale=sess.scale, topk=(wl.topk_num, wl.topk_den))
+        O.upproject(res["z"], f["B_v"])
+        spent += time.perf_counter() - t0
+        tokens += sess.seq_lens[b]
+        pairs += 1
+        if spent >= budget_s:
+            break
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    value = tokens / wl.num_kv_heads / spent
+    return {
+        "value": value, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"{pairs} of {wl.batch * wl.num_kv_heads} (sequence, KV head) pairs, "
+                   f"{tokens} context tokens, {spent:.1f} s of float64 numpy on the host; "
+                   f"rate = tokens / H_kv / seconds"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_BENCH_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] staging workload {wl.name}")
+    t0 = time.time()
+    sess = DecodeSession(wl, "cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] staged in {time.time() - t0:.1f}s; KV tokens/step {sess.kv_tokens()}")
+
+    stream = torch.cuda.current_stream()
+    dominant = "route" if wl.routed else "attn"
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        sess.append()
+        sess.project_queries()
+        if wl.routed:
+            if i is not None:
+                ev[i][0].record(stream)
+            sess.route()
+            if i is not None:
+                ev[i][1].record(stream)
+            sess.attend()
+        else:
+            if i is not None:
+                ev[i][0].record(stream)
+            sess.attend()
+            if i is not None:
+                ev[i][1].record(stream)
+        sess.upproject()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f}s")
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = sess.kv_tokens() * args.steps / elapsed
+    dom_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    if wl.routed:
+        dom_bytes = sess.route_bytes()
+        dom_name = "route_kernel"
+        dom_src = ROUTE_SOURCE
+    else:
+        dom_bytes = sess.attend_bytes()
+        dom_name = "attn_kernel"
+        dom_src = ATTN_SOURCE
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    step_bytes = sess.append_bytes() + (sess.route_bytes() if wl.routed else 0) + sess.attend_bytes()
+    roof = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": measured_traffic(dom_name, wl.name, dom_src),
+        "kernel": dom_name, "algo_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 2),
+    }
+    cfg = {
+        "workload": wl.name, "batch": wl.batch, "context": (sum(sess.seq_lens) // wl.batch),
+        "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+        "page_size": wl.page_size, "rank_v": wl.rank_v, "rank_k": wl.rank_k,
+        "storage": wl.storage, "keys": wl.key_mode,
+        "topk": f"{wl.topk_num}/{wl.topk_den}" if wl.routed else "all",
+        "append_per_seq": wl.append_per_seq, "parallelism": "single-gpu",
+    }
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "KV-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": cfg,
+        "step_algo_bytes": step_bytes,
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(sess, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

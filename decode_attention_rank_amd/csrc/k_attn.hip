@@ -1,0 +1,337 @@
+// Decode attention over the compressed cache, value side in latent space.
+//
+// BasisKV: Value Latents for Communication and Key Routing, English abstract:
+// the original keys are read only for the selected pages and give exact QK
+// scores; the value cache holds rank-r_v latents and value compression is
+// tied to the output projection, so the softmax-weighted sum stays in latent
+// space, z = sum_t p_t v_t, and B_v is applied once per head afterwards.
+// In the dense low-rank mode the keys are latents too: s_t = scale q B_k^T . k_t.
+//
+// Work split: grid (split, pair). A workgroup of 4 waves takes a range of
+// 64-token rows of the pair's page list (selected pages, or all pages). Per row:
+//   scores  - one lane per token; the token's key row is read as 16-byte
+//             chunks (contiguous across the row's tokens), the wave-uniform
+//             query is read with scalar loads; G heads share each load;
+//   softmax - online (running max and sum per head, base-2 exponent);
+//   P.V     - lanes regroup as (latent chunk c, tokens l/CV + k*64/CV), the
+//             probabilities are exchanged through LDS, each lane accumulates
+//             G x CH latent outputs;
+// then waves and workgroups merge their (max, sum, z) partials; the last
+// workgroup of a pair (atomic ticket) merges the splits into z and lse.
+
+#include "kvlr_device.h"
+#include "kvlr_internal.h"
+
+namespace kvlr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ inline void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <class S, int G, int KW, int RV>
+__global__ __launch_bounds__(kThreads) void attn_kernel(
+    const uint8_t* __restrict__ keys, const uint8_t* __restrict__ v_lat,
+    const float* __restrict__ qsrc, int q_stride, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ sel,
+    float* __restrict__ partials, uint32_t* __restrict__ counters, float* __restrict__ z_out,
+    float* __restrict__ lse_out, int Hq, int Hkv, int P, int log2P, int max_pages, int k_max,
+    float scale_log2e, int rows_per_split, int num_splits) {
+  constexpr int CH = S::CH;
+  constexpr int CKW = KW / CH;   // key chunks per token
+  constexpr int CV = RV / CH;    // value-latent chunks per token
+  constexpr int TPL = kWave / CV;  // token stride between a lane's P.V tokens
+  constexpr int PW = RV + 2;     // partial record: m, l, z[RV]
+
+  __shared__ float s_p[kWaves][kWave][G];
+  __shared__ float s_ml[kWaves][G][2];
+  __shared__ float s_z[kWaves][G][RV];
+  __shared__ int s_last;
+
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv;
+  const int g = pair - b * Hkv;
+  const int L = seq_lens[b];
+  const int N = (L + P - 1) >> log2P;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ipr_log2 = 6 - log2P;  // items (pages) per row = 64 / P
+  const int n_items = sel ? k_max : N;
+  const int nrows = (n_items + (1 << ipr_log2) - 1) >> ipr_log2;
+  const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
+  const int32_t* __restrict__ sl = sel ? sel + static_cast<size_t>(pair) * k_max : nullptr;
+  const float* __restrict__ qg = qsrc + static_cast<size_t>(b * Hq + g * G) * q_stride;
+  const size_t slab_k = static_cast<size_t>(CKW) * P * 16;
+  const size_t slab_v = static_cast<size_t>(CV) * P * 16;
+
+  float m[G], lsum[G], z[G][CH];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegInf;
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) z[h][e] = 0.f;
+  }
+  const int my_c = lane % CV;
+
+  const int row0 = blockIdx.x * rows_per_split;
+  const int row1 = min(row0 + rows_per_split, nrows);
+  for (int row = row0 + wave; row < row1; row += kWaves) {
+    // ---- this lane's token: item row*IPR + lane/P, slot lane%P
+    const int item = (row << ipr_log2) + (lane >> log2P);
+    const int slot = lane & (P - 1);
+    int page = -1;
+    if (item < n_items) page = sl ? sl[item] : item;
+    const bool valid = page >= 0 && page < N && (page << log2P) + slot < L;
+    const int phys = valid ? pt[page] : 0;
+
+    // ---- scores: one lane per token, query in scalar registers
+    float s[G];
+    {
+      uint4 kc[CKW];
+      if (valid) {
+        const uint8_t* kb = keys + (static_cast<size_t>(phys) * Hkv + g) * slab_k + slot * 16;
+#pragma unroll
+        for (int c = 0; c < CKW; ++c) kc[c] = load16(kb + static_cast<size_t>(c) * P * 16);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CKW; ++c) kc[c] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = 0.f;
+      static_for<0, CKW>([&](auto cc) {
+        constexpr int C = decltype(cc)::value;
+        float x[CH];
+        S::unpack(kc[C], x);
+        fma_heads<G, CH, KW, C * CH>(qg, x, s);
+      });
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = valid ? s[h] * scale_log2e : kNegInf;
+    }
+
+    // ---- online softmax (base 2); running max is wave-uniform
+    bool any = false;
+    float p[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mx = wave_max_u(s[h]);
+      const float mn = fmaxf(m[h], mx);
+      any = any || (mn != kNegInf);
+      const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
+      p[h] = (mn == kNegInf) ? 0.f : fast_exp2(s[h] - mn);
+      lsum[h] = lsum[h] * alpha + p[h];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) z[h][e] *= alpha;
+      m[h] = mn;
+    }
+    if (!any) continue;  // wave-uniform: nothing valid so far
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_p[wave][lane][h] = p[h];
+    wave_lds_sync();
+
+    // ---- P . V_latent: lane owns chunk my_c of tokens lane/CV + k*TPL
+    if (P == kWave) {
+      // the row is one page: its physical page and valid length are uniform
+      const int upage = __builtin_amdgcn_readfirstlane(page);
+      const bool prow = upage >= 0 && upage < N;
+      const int nvalid = prow ? min(L - upage * kWave, kWave) : 0;
+      const size_t uphys = prow ? static_cast<size_t>(pt[upage]) : 0;
+      const uint8_t* vb = v_lat + (uphys * Hkv + g) * slab_v + static_cast<size_t>(my_c) * P * 16;
+      uint4 vc[CV];
+#pragma unroll
+      for (int k = 0; k < CV; ++k) {
+        const int tok = lane / CV + k * TPL;
+        vc[k] = (tok < nvalid) ? load16(vb + tok * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < CV; ++k) {
+        const int tok = lane / CV + k * TPL;
+        float x[CH];
+        S::unpack(vc[k], x);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pp = s_p[wave][tok][h];
+#pragma unroll
+          for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, x[e], z[h][e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < CV; ++k) {
+        const int tok = lane / CV + k * TPL;
+        const int tphys = __shfl(phys, tok, kWave);
+        const int tvalid = __shfl(static_cast<int>(valid), tok, kWave);
+        uint4 vc = make_uint4(0, 0, 0, 0);
+        if (tvalid) {
+          const int tslot = tok & (P - 1);
+          vc = load16(v_lat + (static_cast<size_t>(tphys) * Hkv + g) * slab_v +
+                      static_cast<size_t>(my_c) * P * 16 + tslot * 16);
+        }
+        float x[CH];
+        S::unpack(vc, x);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pp = s_p[wave][tok][h];
+#pragma unroll
+          for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, x[e], z[h][e]);
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- wave reduction: lanes with the same chunk hold disjoint token sets
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int off = CV; off < kWave; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) z[h][e] += __shfl_xor(z[h][e], off, kWave);
+    lsum[h] = wave_sum_u(lsum[h]);
+  }
+  if (lane < CV) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) s_z[wave][h][lane * CH + e] = z[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_ml[wave][h][0] = m[h];
+      s_ml[wave][h][1] = lsum[h];
+    }
+  }
+  __syncthreads();
+
+  // ---- workgroup partial (max, sum, z) per head
+  float* part = partials + (static_cast<size_t>(pair) * num_splits + blockIdx.x) * G * PW;
+  for (int i = threadIdx.x; i < G * RV; i += kThreads) {
+    const int h = i / RV, e = i - h * RV;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    float Z = 0.f, Ls = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = fast_exp2(s_ml[w][h][0] - M);
+        Z += f * s_z[w][h][e];
+        Ls += f * s_ml[w][h][1];
+      }
+    }
+    part[h * PW + 2 + e] = Z;
+    if (e == 0) {
+      part[h * PW] = M;
+      part[h * PW + 1] = Ls;
+    }
+  }
+
+  // ---- ticket: the last workgroup of the pair merges the splits
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(&counters[pair], 1u);
+    s_last = (prev == static_cast<uint32_t>(num_splits - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float* allp = partials + static_cast<size_t>(pair) * num_splits * G * PW;
+  for (int i = threadIdx.x; i < G * RV; i += kThreads) {
+    const int h = i / RV, e = i - h * RV;
+    float M = kNegInf;
+    for (int sp = 0; sp < num_splits; ++sp) M = fmaxf(M, allp[(sp * G + h) * PW]);
+    float Z = 0.f, Ls = 0.f;
+    if (M != kNegInf) {
+      for (int sp = 0; sp < num_splits; ++sp) {
+        const float* r = allp + (sp * G + h) * PW;
+        const float f = fast_exp2(r[0] - M);
+        Z += f * r[2 + e];
+        Ls += f * r[1];
+      }
+    }
+    const int qh = g * G + h;
+    z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = (Ls > 0.f) ? Z / Ls : 0.f;
+    if (e == 0 && lse_out) {
+      lse_out[static_cast<size_t>(b) * Hq + qh] =
+          (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
+    }
+  }
+  if (threadIdx.x == 0) counters[pair] = 0u;
+}
+
+template <class S, int G, int KW, int RV>
+hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  if (a.q_stride != KW) return hipErrorInvalidValue;  // queries are read with stride KW
+  const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
+  dim3 grid(a.num_splits, a.batch * a.dm.Hkv);
+  hipLaunchKernelGGL((attn_kernel<S, G, KW, RV>), grid, dim3(kThreads), 0, s,
+                     static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
+                     a.qsrc, a.q_stride, a.seq_lens, a.page_table, a.sel, a.partials, a.counters,
+                     a.z_out, a.lse_out, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                     a.scale_log2e, a.rows_per_split, a.num_splits);
+  return hipGetLastError();
+}
+
+template <class S, int G, int RV>
+hipError_t by_kw(const AttnArgs& a, hipStream_t s) {
+  // key width: head_dim for original keys, rank_k for key latents
+  switch (a.dm.exact ? a.dm.D : a.dm.RK) {
+    case 16: return launch_t<S, G, 16, RV>(a, s);
+    case 32: return launch_t<S, G, 32, RV>(a, s);
+    case 64: return launch_t<S, G, 64, RV>(a, s);
+    case 128: return launch_t<S, G, 128, RV>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class S, int G>
+hipError_t by_rv(const AttnArgs& a, hipStream_t s) {
+  switch (a.dm.RV) {
+    case 16: return by_kw<S, G, 16>(a, s);
+    case 32: return by_kw<S, G, 32>(a, s);
+    case 64: return by_kw<S, G, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class S>
+hipError_t by_g(const AttnArgs& a, hipStream_t s) {
+  switch (a.dm.G) {
+    case 1: return by_rv<S, 1>(a, s);
+    case 2: return by_rv<S, 2>(a, s);
+    case 4: return by_rv<S, 4>(a, s);
+    case 8: return by_rv<S, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int attn_max_splits(int pairs) {
+  const int target_wgs = 1024;
+  return max(1, (target_wgs + pairs - 1) / pairs);
+}
+
+SplitPlan attn_split_plan(int max_rows, int pairs) {
+  const int groups = max(1, (max_rows + kWaves - 1) / kWaves);
+  const int splits = min(groups, attn_max_splits(pairs));
+  SplitPlan p;
+  p.rows_per_split = kWaves * ((groups + splits - 1) / splits);
+  p.num_splits = max(1, (max_rows + p.rows_per_split - 1) / p.rows_per_split);
+  return p;
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  if (a.dm.dtype == 0) return by_g<BF16>(a, s);
+  return by_g<F32>(a, s);
+}
+
+}  // namespace kvlr

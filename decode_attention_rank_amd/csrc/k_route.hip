@@ -1,0 +1,288 @@
+// Page routing for the routed (exact-key) cache.
+//
+// BasisKV: Value Latents for Communication and Key Routing, English abstract:
+// the stored value latent predicts part of each key, a key-specific residual
+// latent holds the rest, and the two together decide which key pages are
+// read. In latent space the approximate score of token t for query head h is
+//   s[h, t] = q_hat_h . v_t + q_tilde_h . c_t,
+// q_hat = q W_pred^T and q_tilde = q B_k^T (computed once per step by the
+// query-projection kernel). A page's score is the max over its valid tokens
+// and the KV group's heads; the k_b best pages are kept.
+//
+// Work split: one lane per token. A 64-token "row" of one (sequence, KV head)
+// pair is read with 16-byte loads; the page layout puts the P tokens of one
+// 16-byte chunk column next to each other, so a wave's load of one chunk
+// column is one contiguous run. The projected queries are wave-uniform and
+// are read with scalar loads. Each workgroup (4 waves) scores a range of rows;
+// the last workgroup of a pair to finish (an atomic ticket) runs the exact
+// top-k for the pair: a 4-pass radix select on order-preserving 32-bit keys
+// followed by an ascending ballot compaction.
+
+#include "kvlr_device.h"
+#include "kvlr_internal.h"
+
+namespace kvlr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// Exclusive prefix count of `flag` over the workgroup in thread order; also
+// returns the total. Uses one LDS slot per wave; contains two barriers.
+__device__ inline int block_excl_count(bool flag, int* total, int* lds4) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const uint64_t m = __ballot(flag);
+  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) lds4[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = lds4[w];
+    before += (w < wave) ? c : 0;
+    sum += c;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + in_wave;
+}
+
+// Top-k of scores[0..N) into sel[0..k_max): k largest, ties to the lower
+// index, ascending, -1 padding. Also writes -inf to scores[N..max_pages).
+__device__ void select_pages(float* scores, int N, int k, int k_max, int max_pages, int32_t* sel) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_kk;
+  __shared__ int lds4[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+
+  const bool take_all = (k >= N);
+  uint32_t prefix = 0, pmask = 0;
+  int kk = k;
+  if (!take_all && k > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;  // kThreads == 256 bins
+      __syncthreads();
+      for (int j = tid; j < N; j += kThreads) {
+        const uint32_t key = order_key(scores[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t local = h0 + h1 + h2 + h3;
+        uint32_t suf = local;  // sum over lanes >= lane
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const uint32_t o = __shfl_down(suf, off, kWave);
+          if (lane + off < kWave) suf += o;
+        }
+        const uint64_t hit = __ballot(suf >= static_cast<uint32_t>(kk));
+        const int top = 63 - __clzll(hit);  // highest lane whose suffix reaches kk
+        if (lane == top) {
+          uint32_t above = suf - local;  // count in bins above this lane's
+          const uint32_t hs[4] = {h0, h1, h2, h3};
+          int d = 3;
+          for (; d > 0; --d) {
+            if (above + hs[d] >= static_cast<uint32_t>(kk)) break;
+            above += hs[d];
+          }
+          s_digit = static_cast<uint32_t>(4 * lane + d);
+          s_kk = kk - static_cast<int>(above);
+        }
+      }
+      __syncthreads();
+      prefix |= s_digit << shift;
+      pmask |= 255u << shift;
+      kk = s_kk;
+      __syncthreads();
+    }
+  }
+  // prefix = key of the k-th largest score; kk = how many of the equal keys to take
+  int taken = 0, eq_seen = 0;
+  for (int j0 = 0; j0 < N; j0 += kThreads) {
+    const int j = j0 + tid;
+    const bool in = j < N;
+    const uint32_t key = in ? order_key(scores[j]) : 0u;
+    const bool gt = in && (take_all || key > prefix);
+    const bool eq = in && !take_all && k > 0 && key == prefix;
+    int eq_total = 0;
+    const int eq_rank = eq_seen + block_excl_count(eq, &eq_total, lds4);
+    const bool take = gt || (eq && eq_rank < kk);
+    int take_total = 0;
+    const int pos = taken + block_excl_count(take, &take_total, lds4);
+    if (take && pos < k_max) sel[pos] = j;
+    taken += take_total;
+    eq_seen += eq_total;
+  }
+  for (int i = k + tid; i < k_max; i += kThreads) sel[i] = -1;
+  for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
+}
+
+template <class S, int G, int RV, int RK>
+__global__ __launch_bounds__(kThreads) void route_kernel(
+    const uint8_t* __restrict__ v_lat, const uint8_t* __restrict__ k_lat,
+    const float* __restrict__ q_proj, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ page_table, float* __restrict__ scores,
+    uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int Hq, int Hkv, int P,
+    int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_split,
+    int num_splits) {
+  constexpr int CH = S::CH;
+  constexpr int CV = RV / CH;
+  constexpr int CK = RK / CH;
+  constexpr int W = RV + RK;
+  const int pair = blockIdx.y;
+  const int b = pair / Hkv;
+  const int g = pair - b * Hkv;
+  const int L = seq_lens[b];
+  const int nrows = (L + kWave - 1) / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const float* __restrict__ qp = q_proj + static_cast<size_t>(b * Hq + g * G) * W;
+  const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
+  float* __restrict__ sc = scores + static_cast<size_t>(pair) * max_pages;
+  const size_t slab_v = static_cast<size_t>(CV) * P * 16;  // bytes of one head's page
+  const size_t slab_k = static_cast<size_t>(CK) * P * 16;
+
+  const int row0 = blockIdx.x * rows_per_split;
+  const int row1 = min(row0 + rows_per_split, nrows);
+  for (int row = row0 + wave; row < row1; row += kWaves) {
+    const int t = row * kWave + lane;
+    const bool valid = t < L;
+    const int j = t >> log2P;
+    const int slot = t & (P - 1);
+    uint4 vc[CV], kc[CK];
+    if (valid) {
+      const size_t phys = static_cast<size_t>(pt[j]);
+      const uint8_t* vb = v_lat + (phys * Hkv + g) * slab_v + slot * 16;
+      const uint8_t* kb = k_lat + (phys * Hkv + g) * slab_k + slot * 16;
+#pragma unroll
+      for (int c = 0; c < CV; ++c) vc[c] = load16(vb + static_cast<size_t>(c) * P * 16);
+#pragma unroll
+      for (int c = 0; c < CK; ++c) kc[c] = load16(kb + static_cast<size_t>(c) * P * 16);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CV; ++c) vc[c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < CK; ++c) kc[c] = make_uint4(0, 0, 0, 0);
+    }
+    float acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.f;
+    // value-latent part: q_hat . v
+    static_for<0, CV>([&](auto cc) {
+      constexpr int C = decltype(cc)::value;
+      float x[CH];
+      S::unpack(vc[C], x);
+      fma_heads<G, CH, W, C * CH>(qp, x, acc);
+    });
+    // residual part: q_tilde . c
+    static_for<0, CK>([&](auto cc) {
+      constexpr int C = decltype(cc)::value;
+      float x[CH];
+      S::unpack(kc[C], x);
+      fma_heads<G, CH, W, RV + C * CH>(qp, x, acc);
+    });
+    float m = acc[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) m = fmaxf(m, acc[h]);
+    if (!valid) m = -__builtin_huge_valf();
+    if (P == kWave) {
+      m = wave_max_u(m);
+    } else {
+      m = row16_max(m);
+      if (P == 32) m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    }
+    if (slot == 0 && valid) sc[j] = m;
+  }
+
+  // Ticket: the last workgroup of this pair selects its pages.
+  __shared__ int s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(&counters[pair], 1u);
+    s_last = (prev == static_cast<uint32_t>(num_splits - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int N = (L + P - 1) >> log2P;
+  int k = 0;
+  if (N > 0) {
+    const long long want = (static_cast<long long>(N) * topk_num + topk_den - 1) / topk_den;
+    k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
+    k = min(k, k_max);
+  }
+  select_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
+  if (threadIdx.x == 0) counters[pair] = 0u;
+}
+
+template <class S, int G, int RV, int RK>
+hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
+  const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
+  dim3 grid(a.num_splits, a.batch * a.dm.Hkv);
+  hipLaunchKernelGGL((route_kernel<S, G, RV, RK>), grid, dim3(kThreads), 0, s,
+                     static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
+                     a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.dm.Hq,
+                     a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
+                     a.rows_per_split, a.num_splits);
+  return hipGetLastError();
+}
+
+template <class S, int G, int RV>
+hipError_t by_rk(const RouteArgs& a, hipStream_t s) {
+  switch (a.dm.RK) {
+    case 16: return launch_t<S, G, RV, 16>(a, s);
+    case 32: return launch_t<S, G, RV, 32>(a, s);
+    case 64: return launch_t<S, G, RV, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class S, int G>
+hipError_t by_rv(const RouteArgs& a, hipStream_t s) {
+  switch (a.dm.RV) {
+    case 16: return by_rk<S, G, 16>(a, s);
+    case 32: return by_rk<S, G, 32>(a, s);
+    case 64: return by_rk<S, G, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class S>
+hipError_t by_g(const RouteArgs& a, hipStream_t s) {
+  switch (a.dm.G) {
+    case 1: return by_rv<S, 1>(a, s);
+    case 2: return by_rv<S, 2>(a, s);
+    case 4: return by_rv<S, 4>(a, s);
+    case 8: return by_rv<S, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+SplitPlan route_split_plan(int max_rows, int pairs) {
+  // About 8 workgroups per CU over the whole grid, at least one row per wave.
+  const int target_wgs = 2048;
+  const int target = max(1, (target_wgs + pairs - 1) / pairs);
+  const int groups = max(1, (max_rows + kWaves - 1) / kWaves);
+  const int splits = min(groups, target);
+  SplitPlan p;
+  p.rows_per_split = kWaves * ((groups + splits - 1) / splits);
+  p.num_splits = max(1, (max_rows + p.rows_per_split - 1) / p.rows_per_split);
+  return p;
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  if (a.dm.dtype == 0) return by_g<BF16>(a, s);
+  return by_g<F32>(a, s);
+}
+
+}  // namespace kvlr

@@ -1,0 +1,291 @@
+// C-ABI entry points: host-side validation, workspace layout, dispatch.
+// Nothing here touches the GPU before every argument has been checked, so a
+// rejected call enqueues nothing.
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kvlr.h"
+#include "kvlr_internal.h"
+
+namespace {
+
+using kvlr::Dims;
+
+thread_local char g_hip_msg[256] = "no HIP error recorded";
+
+kvlr_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVLR_OK;
+  snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error %d: %s", static_cast<int>(e), hipGetErrorString(e));
+  return KVLR_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool one_of(int v, int a, int b, int c) { return v == a || v == b || v == c; }
+
+// Checks the shape; fills Dims on success.
+kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
+  if (!s) return KVLR_ERR_INVALID_ARGUMENT;
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 || s->page_size < 1 ||
+      s->rank_v < 1 || s->rank_k < 1 || s->num_phys_pages < 1)
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (s->num_q_heads % s->num_kv_heads != 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (s->dtype != KVLR_DTYPE_BF16 && s->dtype != KVLR_DTYPE_F32) return KVLR_ERR_INVALID_ARGUMENT;
+  if (s->key_mode != KVLR_KEYS_LATENT && s->key_mode != KVLR_KEYS_EXACT) return KVLR_ERR_INVALID_ARGUMENT;
+  if (s->rank_v > s->head_dim || s->rank_k > s->head_dim) return KVLR_ERR_INVALID_ARGUMENT;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVLR_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return KVLR_ERR_UNSUPPORTED;
+  if (!one_of(s->rank_v, 16, 32, 64) || !one_of(s->rank_k, 16, 32, 64)) return KVLR_ERR_UNSUPPORTED;
+  if (!one_of(s->page_size, 16, 32, 64)) return KVLR_ERR_UNSUPPORTED;
+  dm->Hq = s->num_q_heads;
+  dm->Hkv = s->num_kv_heads;
+  dm->G = G;
+  dm->D = s->head_dim;
+  dm->P = s->page_size;
+  dm->RV = s->rank_v;
+  dm->RK = s->rank_k;
+  dm->dtype = s->dtype;
+  dm->exact = s->key_mode == KVLR_KEYS_EXACT ? 1 : 0;
+  return KVLR_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
+
+// Workspace plan. Route: [counters | scores]; attention: [counters | partials].
+struct Plan {
+  size_t route_cnt, route_scores, attn_cnt, attn_part, total;
+  int attn_max_splits;
+};
+
+int attn_rows(int n_items, int P) { return ceil_div(n_items, 64 / P); }
+
+Plan plan_for(const Dims& dm, int batch, int max_pages) {
+  Plan p{};
+  const size_t pairs = static_cast<size_t>(batch) * dm.Hkv;
+  size_t off = 0;
+  if (dm.exact) {
+    p.route_cnt = off;
+    off += round_up(pairs * sizeof(uint32_t));
+    p.route_scores = off;
+    off += round_up(pairs * static_cast<size_t>(max_pages) * sizeof(float));
+  }
+  p.attn_max_splits = kvlr::attn_max_splits(static_cast<int>(pairs));
+  p.attn_cnt = off;
+  off += round_up(pairs * sizeof(uint32_t));
+  p.attn_part = off;
+  off += round_up(pairs * p.attn_max_splits * dm.G * static_cast<size_t>(dm.RV + 2) * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvlr_version(void) { return 100; }
+
+const char* kvlr_status_string(kvlr_status st) {
+  switch (st) {
+    case KVLR_OK: return "ok";
+    case KVLR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KVLR_ERR_UNSUPPORTED: return "unsupported shape";
+    case KVLR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KVLR_ERR_HIP: return g_hip_msg;
+  }
+  return "unknown status";
+}
+
+int32_t kvlr_qproj_width(const kvlr_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, &dm) != KVLR_OK) return 0;
+  return dm.exact ? dm.RV + dm.RK : dm.RK;
+}
+
+size_t kvlr_workspace_bytes(const kvlr_shape* shape, int32_t batch, int32_t max_pages_per_seq) {
+  Dims dm;
+  if (check_shape(shape, &dm) != KVLR_OK || batch < 0 || max_pages_per_seq < 1 ||
+      max_pages_per_seq > 65536)
+    return 0;
+  return plan_for(dm, batch, max_pages_per_seq).total;
+}
+
+kvlr_status kvlr_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (ws_bytes == 0) return KVLR_OK;
+  if (!ok_ptr(workspace)) return KVLR_ERR_INVALID_ARGUMENT;
+  return hip_status(kvlr::launch_zero_fill(workspace, ws_bytes, as_stream(stream)));
+}
+
+kvlr_status kvlr_append_encode(const kvlr_shape* shape, const kvlr_factors* factors,
+                               const kvlr_cache* cache, const void* k_new, const void* v_new,
+                               const int32_t* cu_new, const int32_t* seq_lens_before,
+                               const int32_t* page_table, int32_t max_pages_per_seq,
+                               int32_t batch, int32_t total_new, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!factors || !cache || batch < 0 || total_new < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || total_new == 0) return KVLR_OK;
+  if (!ok_ptr(factors->A_v) || !ok_ptr(factors->A_k) || !ok_ptr(cache->v_lat) ||
+      !ok_ptr(cache->k_lat) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(cu_new) ||
+      !ok_ptr(seq_lens_before) || !ok_ptr(page_table))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (dm.exact && (!ok_ptr(factors->W_pred) || !ok_ptr(cache->k_exact))) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::EncodeArgs a{};
+  a.dm = dm;
+  a.A_v = factors->A_v;
+  a.A_k = factors->A_k;
+  a.W_pred = factors->W_pred;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cu_new = cu_new;
+  a.lens_before = seq_lens_before;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.v_lat = cache->v_lat;
+  a.k_lat = cache->k_lat;
+  a.k_exact = cache->k_exact;
+  a.batch = batch;
+  a.total_new = total_new;
+  return hip_status(kvlr::launch_encode(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* factors,
+                                 const float* q, float* q_proj, int32_t batch, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!factors || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return KVLR_OK;
+  if (!ok_ptr(factors->B_k) || !ok_ptr(q) || !ok_ptr(q_proj)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (dm.exact && !ok_ptr(factors->W_pred)) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::QprojArgs a{};
+  a.dm = dm;
+  a.W_pred = factors->W_pred;
+  a.B_k = factors->B_k;
+  a.q = q;
+  a.q_proj = q_proj;
+  a.batch = batch;
+  return hip_status(kvlr::launch_qproj(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
+                             const int32_t* seq_lens, const int32_t* page_table,
+                             int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
+                             int32_t k_max, int32_t* sel_pages, float* page_scores,
+                             void* workspace, size_t ws_bytes, int32_t batch, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!dm.exact) return KVLR_ERR_UNSUPPORTED;
+  if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
+  if (topk_num < 0 || topk_den < 1) return KVLR_ERR_INVALID_ARGUMENT;
+  const long long bound = (static_cast<long long>(max_pages_per_seq) * topk_num + topk_den - 1) / topk_den;
+  const long long need_k = bound < 1 ? 1 : (bound > max_pages_per_seq ? max_pages_per_seq : bound);
+  if (k_max < need_k || k_max > max_pages_per_seq) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return KVLR_OK;
+  if (!ok_ptr(cache->v_lat) || !ok_ptr(cache->k_lat) || !ok_ptr(q_proj) || !ok_ptr(seq_lens) ||
+      !ok_ptr(page_table) || !ok_ptr(sel_pages) || !ok_ptr(workspace))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (page_scores && !aligned16(page_scores)) return KVLR_ERR_INVALID_ARGUMENT;
+  const Plan plan = plan_for(dm, batch, max_pages_per_seq);
+  if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kvlr::RouteArgs a{};
+  a.dm = dm;
+  a.v_lat = cache->v_lat;
+  a.k_lat = cache->k_lat;
+  a.q_proj = q_proj;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.topk_num = topk_num;
+  a.topk_den = topk_den;
+  a.k_max = k_max;
+  a.sel = sel_pages;
+  a.scores = page_scores ? page_scores : reinterpret_cast<float*>(ws + plan.route_scores);
+  a.counters = reinterpret_cast<uint32_t*>(ws + plan.route_cnt);
+  a.batch = batch;
+  const int max_rows = ceil_div(static_cast<long long>(max_pages_per_seq) * dm.P, 64);
+  const kvlr::SplitPlan sp = kvlr::route_split_plan(max_rows, batch * dm.Hkv);
+  a.rows_per_split = sp.rows_per_split;
+  a.num_splits = sp.num_splits;
+  return hip_status(kvlr::launch_route(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
+                             const float* q_proj, const int32_t* seq_lens,
+                             const int32_t* page_table, int32_t max_pages_per_seq,
+                             const int32_t* sel_pages, int32_t k_max, float softmax_scale,
+                             float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
+                             int32_t batch, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_pages && (k_max < 1 || k_max > max_pages_per_seq)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return KVLR_OK;
+  if (!ok_ptr(cache->v_lat) || !ok_ptr(seq_lens) || !ok_ptr(page_table) || !ok_ptr(z_out) ||
+      !ok_ptr(workspace))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_pages && !aligned16(sel_pages)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (lse_out && !aligned16(lse_out)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (dm.exact && (!ok_ptr(cache->k_exact) || !ok_ptr(q))) return KVLR_ERR_INVALID_ARGUMENT;
+  if (!dm.exact && (!ok_ptr(cache->k_lat) || !ok_ptr(q_proj))) return KVLR_ERR_INVALID_ARGUMENT;
+  const Plan plan = plan_for(dm, batch, max_pages_per_seq);
+  if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kvlr::AttnArgs a{};
+  a.dm = dm;
+  a.keys = dm.exact ? cache->k_exact : cache->k_lat;
+  a.v_lat = cache->v_lat;
+  a.qsrc = dm.exact ? q : q_proj;
+  a.q_stride = dm.exact ? dm.D : dm.RK;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.sel = sel_pages;
+  a.k_max = sel_pages ? k_max : 0;
+  a.scale_log2e = softmax_scale * 1.4426950408889634f;
+  a.partials = reinterpret_cast<float*>(ws + plan.attn_part);
+  a.counters = reinterpret_cast<uint32_t*>(ws + plan.attn_cnt);
+  a.z_out = z_out;
+  a.lse_out = lse_out;
+  a.batch = batch;
+  const int rows = attn_rows(sel_pages ? k_max : max_pages_per_seq, dm.P);
+  const kvlr::SplitPlan sp = kvlr::attn_split_plan(rows, batch * dm.Hkv);
+  a.rows_per_split = sp.rows_per_split;
+  a.num_splits = sp.num_splits;
+  if (a.num_splits > plan.attn_max_splits) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(kvlr::launch_attn(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors, const float* z,
+                           float* o_out, int32_t batch, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!factors || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return KVLR_OK;
+  if (!ok_ptr(factors->B_v) || !ok_ptr(z) || !ok_ptr(o_out)) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::UpprojArgs a{};
+  a.dm = dm;
+  a.B_v = factors->B_v;
+  a.z = z;
+  a.o = o_out;
+  a.batch = batch;
+  return hip_status(kvlr::launch_upproject(a, as_stream(stream)));
+}
+
+}  // extern "C"

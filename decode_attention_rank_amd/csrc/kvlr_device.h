@@ -1,0 +1,253 @@
+// Device helpers shared by the kvlr kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace kvlr {
+
+constexpr int kWave = 64;
+
+// Storage policies. A chunk is 16 bytes: 8 bf16 or 4 f32 elements.
+struct BF16 {
+  static constexpr int CH = 8;
+  static constexpr int ELEM_BYTES = 2;
+  // element e of a chunk as float (bf16 -> f32 is a 16-bit shift, exact)
+  __device__ static inline void unpack(const uint4& c, float (&x)[CH]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline float load1(const void* base, long idx) {
+    const uint16_t u = reinterpret_cast<const uint16_t*>(base)[idx];
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+  }
+};
+
+struct F32 {
+  static constexpr int CH = 4;
+  static constexpr int ELEM_BYTES = 4;
+  __device__ static inline void unpack(const uint4& c, float (&x)[CH]) {
+    x[0] = __uint_as_float(c.x);
+    x[1] = __uint_as_float(c.y);
+    x[2] = __uint_as_float(c.z);
+    x[3] = __uint_as_float(c.w);
+  }
+  __device__ static inline float load1(const void* base, long idx) {
+    return reinterpret_cast<const float*>(base)[idx];
+  }
+};
+
+// float32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ inline void store16(void* p, const uint4& v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-uniform operands in scalar registers.
+//
+// Query values are the same for every lane of a wave, so they belong in
+// SGPRs where a VALU FMA reads them for free. Loading them with plain C++
+// lets the compiler hoist every query value of a kernel out of its loop and
+// spill the excess into VGPR lanes (one v_readlane per use). These helpers
+// issue the scalar loads where they are used and wait for them inside the
+// same asm block, so no load is ever in flight when the block ends.
+typedef float sreg8 __attribute__((ext_vector_type(8)));
+typedef float sreg4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+struct SRegs;
+template <>
+struct SRegs<8> {
+  using T = sreg8;
+};
+template <>
+struct SRegs<4> {
+  using T = sreg4;
+};
+
+#define KVLR_SL8 "s_load_dwordx8 "
+#define KVLR_SL4 "s_load_dwordx4 "
+
+// out[h] = p[h * STRIDE + OFF .. + N) for h < G (floats), N = 4 or 8.
+template <int G, int N, int STRIDE, int OFF>
+__device__ inline void sload_heads(const float* p, typename SRegs<N>::T (&out)[G]) {
+  static_assert(N == 4 || N == 8, "chunk of 4 or 8 floats");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  constexpr int B = 4;  // bytes per float
+  if constexpr (N == 8) {
+    if constexpr (G == 1) {
+      asm volatile(KVLR_SL8 "%0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]) : "s"(p), "i"(OFF * B));
+    } else if constexpr (G == 2) {
+      asm volatile(KVLR_SL8 "%0, %2, %3\n\t" KVLR_SL8 "%1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]), "=s"(out[1])
+                   : "s"(p), "i"(OFF * B), "i"((STRIDE + OFF) * B));
+    } else if constexpr (G == 4) {
+      asm volatile(KVLR_SL8 "%0, %4, %5\n\t" KVLR_SL8 "%1, %4, %6\n\t" KVLR_SL8 "%2, %4, %7\n\t"
+                   KVLR_SL8 "%3, %4, %8\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]), "=s"(out[1]), "=s"(out[2]), "=s"(out[3])
+                   : "s"(p), "i"(OFF * B), "i"((STRIDE + OFF) * B), "i"((2 * STRIDE + OFF) * B),
+                     "i"((3 * STRIDE + OFF) * B));
+    } else {
+      asm volatile(KVLR_SL8 "%0, %8, %9\n\t" KVLR_SL8 "%1, %8, %10\n\t" KVLR_SL8 "%2, %8, %11\n\t"
+                   KVLR_SL8 "%3, %8, %12\n\t" KVLR_SL8 "%4, %8, %13\n\t" KVLR_SL8 "%5, %8, %14\n\t"
+                   KVLR_SL8 "%6, %8, %15\n\t" KVLR_SL8 "%7, %8, %16\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]), "=s"(out[1]), "=s"(out[2]), "=s"(out[3]), "=s"(out[4]),
+                     "=s"(out[5]), "=s"(out[6]), "=s"(out[7])
+                   : "s"(p), "i"(OFF * B), "i"((STRIDE + OFF) * B), "i"((2 * STRIDE + OFF) * B),
+                     "i"((3 * STRIDE + OFF) * B), "i"((4 * STRIDE + OFF) * B),
+                     "i"((5 * STRIDE + OFF) * B), "i"((6 * STRIDE + OFF) * B),
+                     "i"((7 * STRIDE + OFF) * B));
+    }
+  } else {
+    if constexpr (G == 1) {
+      asm volatile(KVLR_SL4 "%0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]) : "s"(p), "i"(OFF * B));
+    } else if constexpr (G == 2) {
+      asm volatile(KVLR_SL4 "%0, %2, %3\n\t" KVLR_SL4 "%1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]), "=s"(out[1])
+                   : "s"(p), "i"(OFF * B), "i"((STRIDE + OFF) * B));
+    } else if constexpr (G == 4) {
+      asm volatile(KVLR_SL4 "%0, %4, %5\n\t" KVLR_SL4 "%1, %4, %6\n\t" KVLR_SL4 "%2, %4, %7\n\t"
+                   KVLR_SL4 "%3, %4, %8\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]), "=s"(out[1]), "=s"(out[2]), "=s"(out[3])
+                   : "s"(p), "i"(OFF * B), "i"((STRIDE + OFF) * B), "i"((2 * STRIDE + OFF) * B),
+                     "i"((3 * STRIDE + OFF) * B));
+    } else {
+      asm volatile(KVLR_SL4 "%0, %8, %9\n\t" KVLR_SL4 "%1, %8, %10\n\t" KVLR_SL4 "%2, %8, %11\n\t"
+                   KVLR_SL4 "%3, %8, %12\n\t" KVLR_SL4 "%4, %8, %13\n\t" KVLR_SL4 "%5, %8, %14\n\t"
+                   KVLR_SL4 "%6, %8, %15\n\t" KVLR_SL4 "%7, %8, %16\n\ts_waitcnt lgkmcnt(0)"
+                   : "=s"(out[0]), "=s"(out[1]), "=s"(out[2]), "=s"(out[3]), "=s"(out[4]),
+                     "=s"(out[5]), "=s"(out[6]), "=s"(out[7])
+                   : "s"(p), "i"(OFF * B), "i"((STRIDE + OFF) * B), "i"((2 * STRIDE + OFF) * B),
+                     "i"((3 * STRIDE + OFF) * B), "i"((4 * STRIDE + OFF) * B),
+                     "i"((5 * STRIDE + OFF) * B), "i"((6 * STRIDE + OFF) * B),
+                     "i"((7 * STRIDE + OFF) * B));
+    }
+  }
+}
+
+#undef KVLR_SL8
+#undef KVLR_SL4
+
+// acc[h] += q_h[OFF .. OFF+CH) . x for the G heads of a group, q_h = qp + h*STRIDE.
+// Heads are loaded in blocks of at most 32 scalar registers. The empty asm on
+// the accumulators pins a block's FMAs before the next block's loads, so the
+// scheduler cannot batch every block's loads first and spill the registers.
+template <int G, int CH, int STRIDE, int OFF>
+__device__ inline void fma_heads(const float* qp, const float (&x)[CH], float (&acc)[G]) {
+  constexpr int HB = (G * CH <= 32) ? G : 32 / CH;
+  static_for<0, G / HB>([&](auto hb) {
+    constexpr int H0 = decltype(hb)::value * HB;
+    typename SRegs<CH>::T q[HB];
+    sload_heads<HB, CH, STRIDE, H0 * STRIDE + OFF>(qp, q);
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[H0 + h] = fmaf(q[h][e], x[e], acc[H0 + h]);
+      asm volatile("" : "+v"(acc[H0 + h]));
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// DPP reductions (no LDS traffic). Steps within a 16-lane row use quad_perm
+// and mirrors; rows are combined with row_bcast, which leaves the full
+// result in lane 63.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline float dpp(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+// Max over each aligned 16-lane row; every lane of the row gets it.
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v, v));
+  v = fmaxf(v, dpp<kDppXor2>(v, v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v, v));
+  v = fmaxf(v, dpp<kDppMirror>(v, v));
+  return v;
+}
+
+// Max over the whole wave, returned as a wave-uniform value.
+__device__ inline float wave_max_u(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, dpp<kDppBcast15, 0xa>(-__builtin_huge_valf(), v));
+  v = fmaxf(v, dpp<kDppBcast31, 0xc>(-__builtin_huge_valf(), v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over the whole wave, returned as a wave-uniform value.
+__device__ inline float wave_sum_u(float v) {
+  v += dpp<kDppXor1>(v, v);
+  v += dpp<kDppXor2>(v, v);
+  v += dpp<kDppHalfMirror>(v, v);
+  v += dpp<kDppMirror>(v, v);
+  v += dpp<kDppBcast15, 0xa>(0.f, v);
+  v += dpp<kDppBcast31, 0xc>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave-wide reductions over all 64 lanes.
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Max over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ inline float group_max(float v, int width) {
+  for (int off = width >> 1; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 == +0.
+__device__ inline uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace kvlr

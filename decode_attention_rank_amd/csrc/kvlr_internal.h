@@ -1,0 +1,109 @@
+// Host-side launch interfaces between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvlr {
+
+// Shape facts every launcher needs, already validated by the API layer.
+struct Dims {
+  int Hq, Hkv, G, D, P, RV, RK;
+  int dtype;      // KVLR_DTYPE_*
+  int exact;      // 1 = routed (residual latent + original keys)
+};
+
+struct QprojArgs {
+  Dims dm;
+  const void* W_pred;  // [Hkv][RV][D] (exact only)
+  const void* B_k;     // [Hkv][RK][D]
+  const float* q;      // [B][Hq][D]
+  float* q_proj;       // [B][Hq][width]
+  int batch;
+};
+hipError_t launch_qproj(const QprojArgs& a, hipStream_t s);
+
+struct RouteArgs {
+  Dims dm;
+  const void* v_lat;
+  const void* k_lat;
+  const float* q_proj;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int max_pages;
+  int topk_num, topk_den, k_max;
+  int32_t* sel;
+  float* scores;        // [B][Hkv][max_pages]
+  uint32_t* counters;   // [B * Hkv], zero between calls
+  int batch;
+  int rows_per_split;   // 64-token rows per workgroup
+  int num_splits;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  Dims dm;
+  const void* keys;      // k_exact (exact) or k_lat (latent)
+  const void* v_lat;
+  const float* qsrc;     // q (exact) or q_proj (latent)
+  int q_stride;          // floats per (b, h) row of qsrc
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* sel;    // NULL = every page
+  int k_max;
+  float scale_log2e;
+  float* partials;       // [B*Hkv][num_splits][G][RV + 2]
+  uint32_t* counters;    // [B * Hkv]
+  float* z_out;
+  float* lse_out;        // may be NULL
+  int batch;
+  int rows_per_split;
+  int num_splits;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+struct UpprojArgs {
+  Dims dm;
+  const void* B_v;
+  const float* z;
+  float* o;
+  int batch;
+};
+hipError_t launch_upproject(const UpprojArgs& a, hipStream_t s);
+
+struct EncodeArgs {
+  Dims dm;
+  const void* A_v;
+  const void* A_k;
+  const void* W_pred;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* cu_new;
+  const int32_t* lens_before;
+  const int32_t* page_table;
+  int max_pages;
+  void* v_lat;
+  void* k_lat;
+  void* k_exact;
+  int batch;
+  int total_new;
+};
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+
+// Launch geometry shared by the workspace sizing and the launches. A pair's
+// rows are cut into at most max_splits(pairs) workgroups of rows_per_split
+// rows (a multiple of the 4 waves); the split count never exceeds the bound,
+// so a workspace sized by the bound fits every call.
+struct SplitPlan {
+  int rows_per_split;
+  int num_splits;
+};
+SplitPlan route_split_plan(int max_rows, int pairs);
+SplitPlan attn_split_plan(int max_rows, int pairs);
+int attn_max_splits(int pairs);
+
+}  // namespace kvlr

@@ -1,0 +1,207 @@
+"""Device buffers for one decode step and the calls that run it.
+
+A DecodeSession owns the paged cache, the factors, the per-step inputs and
+outputs and the workspace for one workload on one GPU, and runs the step as
+the library's five calls in order:
+  append_encode -> project_queries -> route_pages (routed only)
+  -> decode_attn -> upproject.
+It stages seeded synthetic inputs (from `synth`) into device memory; every
+step of the method itself runs in the HIP kernels.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib as K
+from . import layout, synth
+from .workloads import Workload
+
+
+def kvlr_dtype(wl: Workload) -> int:
+    return K.KVLR_DTYPE_BF16 if wl.storage == "bf16" else K.KVLR_DTYPE_F32
+
+
+class DecodeSession:
+    def __init__(self, wl: Workload, device="cuda", *, seq_lens=None, append_per_seq=None,
+                 spare_pages: int = 0, tail_fill: float = 0.0, stage_prefix: bool = True,
+                 page_table=None, num_phys=None):
+        self.wl = wl
+        self.device = torch.device(device)
+        self.tail_fill = tail_fill
+        self.seq_lens = list(seq_lens) if seq_lens is not None else synth.make_seq_lens(wl)
+        B = len(self.seq_lens)
+        if B != wl.batch:
+            raise ValueError("seq_lens must have one entry per sequence")
+        a = wl.append_per_seq if append_per_seq is None else append_per_seq
+        self.n_new = [min(a, L) for L in self.seq_lens]
+        self.lens_before = [L - n for L, n in zip(self.seq_lens, self.n_new)]
+        if page_table is None:
+            page_table, num_phys = synth.make_page_table(wl, self.seq_lens, spare_pages)
+        self.page_table_cpu = page_table
+        self.max_pages = page_table.shape[1]
+        self.num_phys = num_phys
+        dt = synth.storage_dtype(wl)
+        self.dtype = dt
+        self.shape = K.make_shape(
+            num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
+            page_size=wl.page_size, rank_v=wl.rank_v, rank_k=wl.rank_k, dtype=kvlr_dtype(wl),
+            key_mode=K.KVLR_KEYS_EXACT if wl.routed else K.KVLR_KEYS_LATENT,
+            num_phys_pages=num_phys)
+        dev = self.device
+        H, P = wl.num_kv_heads, wl.page_size
+
+        # factors, queries
+        self.factors = synth.make_factors(wl, dev)
+        self.kfactors = K.make_factors(**self.factors)
+        self.q = synth.make_queries(wl, dev)
+        self.Qv, self.Qk = synth.bases(wl)
+
+        # paged cache
+        self.v_lat = layout.alloc_pages(num_phys, H, wl.rank_v, P, dt, dev, tail_fill)
+        self.k_lat = layout.alloc_pages(num_phys, H, wl.rank_k, P, dt, dev, tail_fill)
+        self.k_exact = (layout.alloc_pages(num_phys, H, wl.head_dim, P, dt, dev, tail_fill)
+                        if wl.routed else None)
+        self.kcache = K.make_cache(self.v_lat, self.k_lat, self.k_exact)
+
+        # lengths and page table on the device
+        self.page_table = page_table.to(dev)
+        self.seq_lens_dev = torch.tensor(self.seq_lens, dtype=torch.int32, device=dev)
+        self.lens_before_dev = torch.tensor(self.lens_before, dtype=torch.int32, device=dev)
+        cu = [0]
+        for n in self.n_new:
+            cu.append(cu[-1] + n)
+        self.cu_new = torch.tensor(cu, dtype=torch.int32, device=dev)
+        self.total_new = cu[-1]
+
+        # routing bound and outputs
+        B, Hq, d = wl.batch, wl.num_q_heads, wl.head_dim
+        if wl.routed:
+            bound = -(-(self.max_pages * wl.topk_num) // wl.topk_den)
+            self.k_max = min(self.max_pages, max(1, bound))
+        else:
+            self.k_max = 0
+        self.qp_width = K.kvlr_qproj_width(self.shape)
+        self.q_proj = torch.empty(B, Hq, self.qp_width, dtype=torch.float32, device=dev)
+        self.sel = (torch.empty(B, H, self.k_max, dtype=torch.int32, device=dev)
+                    if wl.routed else None)
+        self.page_scores = (torch.empty(B, H, self.max_pages, dtype=torch.float32, device=dev)
+                            if wl.routed else None)
+        self.z = torch.empty(B, Hq, wl.rank_v, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        self.o = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+        self.ws_bytes = K.kvlr_workspace_bytes(self.shape, B, self.max_pages)
+        self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        K.kvlr_workspace_init(self.workspace, self.ws_bytes)
+        self.scale = 1.0 / math.sqrt(d)
+
+        self.k_new = None
+        self.v_new = None
+        if stage_prefix:
+            self.stage_prefix()
+            self.stage_new_tokens()
+
+    # ------------------------------------------------------------------ staging
+    def prefix_rows(self, b: int):
+        """Seeded pre-existing cache rows of sequence b (device tensors [H, n, R])."""
+        return synth.synth_latent_cache(self.wl, b, self.lens_before[b], self.device,
+                                        q=self.q.cpu(), Qk=self.Qk)
+
+    def stage_prefix(self):
+        for b in range(self.wl.batch):
+            rows = self.prefix_rows(b)
+            self.write_rows(b, rows)
+
+    def write_rows(self, b: int, rows: dict, tail_fill: float | None = None):
+        tail_fill = self.tail_fill if tail_fill is None else tail_fill
+        pages = self.page_table_cpu[b]
+        layout.pack_sequence(self.v_lat, pages, rows["v"], tail_fill)
+        layout.pack_sequence(self.k_lat, pages, rows["k_lat"], tail_fill)
+        if self.wl.routed:
+            layout.pack_sequence(self.k_exact, pages, rows["k_exact"], tail_fill)
+
+    def read_rows(self, b: int, L: int | None = None, start: int = 0) -> dict:
+        L = self.seq_lens[b] if L is None else L
+        pages = self.page_table_cpu[b]
+        out = {"v": layout.unpack_sequence(self.v_lat, pages, L, start),
+               "k_lat": layout.unpack_sequence(self.k_lat, pages, L, start)}
+        if self.wl.routed:
+            out["k_exact"] = layout.unpack_sequence(self.k_exact, pages, L, start)
+        return out
+
+    def stage_new_tokens(self):
+        Ks, Vs = [], []
+        for b in range(self.wl.batch):
+            Kb, Vb = synth.synth_raw_tokens(self.wl, b, self.lens_before[b], self.n_new[b],
+                                            self.device, q=self.q.cpu(), Qv=self.Qv, Qk=self.Qk)
+            Ks.append(Kb)
+            Vs.append(Vb)
+        self.k_new = torch.cat(Ks).contiguous()
+        self.v_new = torch.cat(Vs).contiguous()
+
+    # ------------------------------------------------------------------ the step
+    def append(self, stream=None):
+        K.kvlr_append_encode(self.shape, self.kfactors, self.kcache, self.k_new, self.v_new,
+                             self.cu_new, self.lens_before_dev, self.page_table, self.max_pages,
+                             self.wl.batch, self.total_new, stream)
+
+    def project_queries(self, stream=None):
+        K.kvlr_project_queries(self.shape, self.kfactors, self.q, self.q_proj, self.wl.batch, stream)
+
+    def route(self, stream=None):
+        K.kvlr_route_pages(self.shape, self.kcache, self.q_proj, self.seq_lens_dev, self.page_table,
+                           self.max_pages, self.wl.topk_num, self.wl.topk_den, self.k_max, self.sel,
+                           self.page_scores, self.workspace, self.ws_bytes, self.wl.batch, stream)
+
+    def attend(self, stream=None, sel=True):
+        use_sel = self.sel if (self.wl.routed and sel) else None
+        K.kvlr_decode_attn(self.shape, self.kcache, self.q, self.q_proj, self.seq_lens_dev,
+                           self.page_table, self.max_pages, use_sel,
+                           self.k_max if use_sel is not None else 0, self.scale, self.z, self.lse,
+                           self.workspace, self.ws_bytes, self.wl.batch, stream)
+
+    def upproject(self, stream=None):
+        K.kvlr_upproject(self.shape, self.kfactors, self.z, self.o, self.wl.batch, stream)
+
+    def decode(self, stream=None):
+        self.project_queries(stream)
+        if self.wl.routed:
+            self.route(stream)
+        self.attend(stream)
+        self.upproject(stream)
+
+    def step(self, stream=None):
+        self.append(stream)
+        self.decode(stream)
+
+    # ------------------------------------------------------------------ metrics
+    def kv_tokens(self) -> int:
+        return sum(self.seq_lens)
+
+    def route_bytes(self) -> int:
+        """Algorithmic bytes the routing kernel must read: both latents of every valid token."""
+        eb = torch.empty(0, dtype=self.dtype).element_size()
+        return sum(self.seq_lens) * self.wl.num_kv_heads * (self.wl.rank_v + self.wl.rank_k) * eb
+
+    def attend_bytes(self) -> int:
+        """Algorithmic bytes of attention: keys and value latents of the attended tokens."""
+        wl = self.wl
+        eb = torch.empty(0, dtype=self.dtype).element_size()
+        if not wl.routed:
+            return sum(self.seq_lens) * wl.num_kv_heads * (wl.rank_k + wl.rank_v) * eb
+        tot = 0
+        P = wl.page_size
+        for L in self.seq_lens:
+            N = -(-L // P)
+            k = 0 if N == 0 else min(N, max(1, -(-(N * wl.topk_num) // wl.topk_den)))
+            tot += k * P  # upper bound for a ragged last page; exact when pages are full
+        return tot * wl.num_kv_heads * (wl.head_dim + wl.rank_v) * eb
+
+    def append_bytes(self) -> int:
+        wl = self.wl
+        eb = torch.empty(0, dtype=self.dtype).element_size()
+        read = self.total_new * wl.num_kv_heads * 2 * wl.head_dim * eb
+        write = self.total_new * wl.num_kv_heads * (wl.rank_v + wl.rank_k + (wl.head_dim if wl.routed else 0)) * eb
+        return read + write

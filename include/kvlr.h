@@ -1,0 +1,236 @@
+/*
+ * kvlr -- decode attention read directly from a low-rank compressed, paged
+ * KV cache, in the BasisKV form, for AMD Instinct MI355X (gfx950).
+ *
+ * Source: "BasisKV: Value Latents for Communication and Key Routing"
+ * (English abstract; method-details section). Keys and values are compressed
+ * by low-rank projections; the value cache keeps rank-r_v latents; the stored
+ * value latent predicts part of each key and a key-specific residual latent
+ * holds the rest, and together they rank the key pages; the original keys of
+ * the chosen pages alone give exact QK scores; the value latent is tied to the
+ * output projection, so the up-projection is applied once per head.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a device pointer unless marked "host".
+ *     The caller owns every buffer; the library allocates nothing and keeps
+ *     no mutable global state. Calls are thread-safe.
+ *   - Each call validates its arguments on the host, then enqueues its
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     returns without synchronising. Outputs are valid once the stream has
+ *     reached the call. A non-zero status means nothing was enqueued, except
+ *     KVLR_ERR_HIP, which reports a failed launch.
+ *   - Device arrays must be 16-byte aligned. Integer arrays are int32.
+ *   - Values that only the device holds (sequence lengths, page tables) are
+ *     trusted: the caller keeps every referenced page id inside
+ *     [0, num_phys_pages) and every length inside max_pages_per_seq pages.
+ *
+ * Storage types (kvlr_shape.dtype): KVLR_DTYPE_BF16 or KVLR_DTYPE_F32 for
+ * the latents, the original keys, the factors and the new keys/values.
+ * Queries, projected queries, z, lse and outputs are float32.
+ *
+ * Cache layout (one "chunk" = 16 bytes = CH elements: 8 bf16 or 4 f32):
+ *   v_lat   [num_phys_pages][H_kv][rank_v  / CH][page_size][CH]
+ *   k_lat   [num_phys_pages][H_kv][rank_k  / CH][page_size][CH]
+ *   k_exact [num_phys_pages][H_kv][head_dim/ CH][page_size][CH]
+ * Token slot s of a page holds, for chunk c, elements c*CH .. c*CH+CH-1 of
+ * its row, so the P tokens of one chunk column sit in P*16 contiguous bytes.
+ * Logical page j of sequence b (tokens j*P .. j*P+P-1) lives in physical page
+ * page_table[b * max_pages_per_seq + j].
+ *
+ * Factor layouts (per KV head g, row-major):
+ *   A_v [H_kv][head_dim][rank_v]    v = V . A_v           (value encode)
+ *   B_v [H_kv][rank_v][head_dim]    o = z . B_v           (up-projection)
+ *   A_k [H_kv][head_dim][rank_k]    residual / key-latent encode
+ *   B_k [H_kv][rank_k][head_dim]    residual / key-latent decode
+ *   W_pred [H_kv][rank_v][head_dim] key prediction from the value latent
+ *                                   (KVLR_KEYS_EXACT only)
+ *
+ * Key modes (kvlr_shape.key_mode):
+ *   KVLR_KEYS_EXACT  routed BasisKV: k_lat holds the residual latent
+ *                    c = (K - v . W_pred) . A_k, k_exact the original keys.
+ *   KVLR_KEYS_LATENT dense low-rank keys: k_lat holds k = K . A_k; no
+ *                    routing, no original keys.
+ *
+ * Query-head h belongs to KV head h / G, G = num_q_heads / num_kv_heads.
+ * Supported: head_dim in {64, 128}; rank_v, rank_k in {16, 32, 64} and
+ * <= head_dim (rank 128 also for f32 at head_dim 128); page_size in
+ * {16, 32, 64}; G in {1, 2, 4, 8}; max_pages_per_seq <= 65536.
+ * Other values return KVLR_ERR_UNSUPPORTED.
+ */
+#ifndef KVLR_H
+#define KVLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvlr_status;
+#define KVLR_OK 0
+#define KVLR_ERR_INVALID_ARGUMENT 1
+#define KVLR_ERR_UNSUPPORTED 2
+#define KVLR_ERR_WORKSPACE_TOO_SMALL 3
+#define KVLR_ERR_HIP 4
+
+#define KVLR_DTYPE_BF16 0
+#define KVLR_DTYPE_F32 1
+
+#define KVLR_KEYS_LATENT 0
+#define KVLR_KEYS_EXACT 1
+
+typedef struct kvlr_shape {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t rank_v;
+  int32_t rank_k;
+  int32_t dtype;          /* KVLR_DTYPE_* */
+  int32_t key_mode;       /* KVLR_KEYS_* */
+  int32_t num_phys_pages;
+} kvlr_shape;
+
+typedef struct kvlr_cache {
+  void* v_lat;
+  void* k_lat;
+  void* k_exact;          /* KVLR_KEYS_EXACT only, else NULL */
+} kvlr_cache;
+
+typedef struct kvlr_factors {
+  const void* A_v;
+  const void* B_v;
+  const void* A_k;
+  const void* B_k;
+  const void* W_pred;     /* KVLR_KEYS_EXACT only, else NULL */
+} kvlr_factors;
+
+/*
+ * Append-side encode. BasisKV English abstract: new keys and values are
+ * compressed on write by the low-rank projections; the residual is what the
+ * stored value latent cannot predict of the key.
+ *
+ * For each new token i of sequence b (cu_new[b] <= i < cu_new[b+1]) and KV
+ * head g, at logical position p = seq_lens_before[b] + i - cu_new[b]:
+ *   v = RNE(V_i . A_v)
+ *   EXACT:  c = RNE((K_i - v . W_pred) . A_k) into k_lat, K_i into k_exact
+ *   LATENT: k = RNE(K_i . A_k) into k_lat
+ * RNE = round to nearest even in the storage type; arithmetic in float32
+ * (bf16 operands on matrix cores, float32 accumulation).
+ *   k_new, v_new     [total_new][H_kv][head_dim], storage type
+ *   cu_new           [batch + 1] prefix offsets, cu_new[0] = 0,
+ *                    cu_new[batch] = total_new
+ *   seq_lens_before  [batch]
+ *   page_table       [batch][max_pages_per_seq]; pages that the new tokens
+ *                    land on must already be mapped
+ *   total_new        host; 0 is a no-op
+ * Sequence lengths are not updated: the caller owns them.
+ */
+kvlr_status kvlr_append_encode(const kvlr_shape* shape, const kvlr_factors* factors,
+                               const kvlr_cache* cache, const void* k_new, const void* v_new,
+                               const int32_t* cu_new, const int32_t* seq_lens_before,
+                               const int32_t* page_table, int32_t max_pages_per_seq,
+                               int32_t batch, int32_t total_new, void* stream);
+
+/*
+ * Query images in latent space (the query side of latent-space scoring).
+ * BasisKV English abstract: the value latent stands in for part of the key
+ * and the residual latent for the rest, so scores against latents need the
+ * query mapped through the same factors.
+ *   q       [batch][num_q_heads][head_dim] float32
+ *   q_proj  [batch][num_q_heads][kvlr_qproj_width(shape)] float32, out:
+ *           EXACT:  [q . W_pred^T (rank_v), q . B_k^T (rank_k)]
+ *           LATENT: [q . B_k^T (rank_k)]
+ */
+kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* factors,
+                                 const float* q, float* q_proj, int32_t batch, void* stream);
+
+/* Floats per (sequence, query head) row of q_proj; 0 for an invalid shape. */
+int32_t kvlr_qproj_width(const kvlr_shape* shape);
+
+/*
+ * Page routing (KVLR_KEYS_EXACT only). BasisKV English abstract: the value
+ * latent's key prediction plus the key-specific residual rank the key pages,
+ * and only the chosen pages are read exactly.
+ * For each sequence b and KV head g, with L = seq_lens[b], N = ceil(L / P):
+ *   s[h, t] = q_hat_h . v_t + q_tilde_h . c_t    (t < L, h in the group)
+ *   S[j]    = max over the group's heads and the valid tokens of page j
+ *   k_b     = min(N, max(1, ceil(N * topk_num / topk_den))), 0 if N = 0
+ *   sel     = the k_b pages of largest S, equal scores to the lower index,
+ *             written in ascending order, then -1 up to k_max
+ *   q_proj       from kvlr_project_queries
+ *   seq_lens     [batch]
+ *   page_table   [batch][max_pages_per_seq]
+ *   k_max        host; must be >= min(max_pages_per_seq,
+ *                ceil(max_pages_per_seq * topk_num / topk_den))
+ *   sel_pages    out [batch][H_kv][k_max] logical page ids
+ *   page_scores  optional out [batch][H_kv][max_pages_per_seq] float32
+ *                (S, then -inf past N); NULL keeps them in the workspace
+ *   workspace    >= kvlr_workspace_bytes(...) bytes, zero-filled once
+ *                before its first use (kvlr_workspace_init); every call
+ *                leaves it ready for the next one. Calls sharing one
+ *                workspace must not overlap.
+ * Scores are unscaled; NaN inputs give an unspecified selection.
+ */
+kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
+                             const int32_t* seq_lens, const int32_t* page_table,
+                             int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
+                             int32_t k_max, int32_t* sel_pages, float* page_scores,
+                             void* workspace, size_t ws_bytes, int32_t batch, void* stream);
+
+/*
+ * Decode attention over the compressed cache. BasisKV English abstract:
+ * exact QK on the original keys of the chosen pages; the value side stays
+ * in latent space, z = sum_t p_t v_t, and B_v is applied afterwards
+ * (kvlr_upproject).
+ * For each sequence b, query head h (KV head g = h / G), over the tokens t of
+ * the attended pages with t < seq_lens[b]:
+ *   EXACT:  s_t = scale * q_h . K_t (original keys)
+ *   LATENT: s_t = scale * q_tilde_h . k_t (key latents)
+ *   p = softmax(s);  z_out[b][h] = sum_t p_t v_t;  lse_out = log sum exp s
+ * Attended pages: sel_pages[b][g][0 .. k_max) with -1 entries skipped, or
+ * every page 0 .. N-1 when sel_pages is NULL. An empty set gives z = 0 and
+ * lse = -inf.
+ *   q        [batch][num_q_heads][head_dim] float32 (EXACT; may be NULL in LATENT)
+ *   q_proj   from kvlr_project_queries (LATENT; may be NULL in EXACT)
+ *   z_out    out [batch][num_q_heads][rank_v] float32
+ *   lse_out  optional out [batch][num_q_heads] float32 (natural log)
+ *   workspace, ws_bytes: as for kvlr_route_pages
+ */
+kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
+                             const float* q_proj, const int32_t* seq_lens,
+                             const int32_t* page_table, int32_t max_pages_per_seq,
+                             const int32_t* sel_pages, int32_t k_max, float softmax_scale,
+                             float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
+                             int32_t batch, void* stream);
+
+/*
+ * Up-projection, once per query head. BasisKV English abstract and method
+ * details: value compression is tied to the output projection, so the
+ * decoder B_v is applied to the attention-weighted latent z.
+ *   o_out[b][h] = z[b][h] . B_v[h / G]
+ *   z      [batch][num_q_heads][rank_v] float32
+ *   o_out  out [batch][num_q_heads][head_dim] float32
+ * Float32 matrix cores, float32 accumulation.
+ */
+kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors, const float* z,
+                           float* o_out, int32_t batch, void* stream);
+
+/* Workspace bytes that route and attention need for this shape (host). */
+size_t kvlr_workspace_bytes(const kvlr_shape* shape, int32_t batch, int32_t max_pages_per_seq);
+
+/* Zero-fills a workspace with a kernel (no memset node), once after allocation. */
+kvlr_status kvlr_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* Static text for a status; the last HIP error text for KVLR_ERR_HIP. */
+const char* kvlr_status_string(kvlr_status status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t kvlr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVLR_H */

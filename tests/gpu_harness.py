@@ -1,0 +1,187 @@
+"""Shared checks for the GPU parity tests.
+
+The oracle's inputs are rebuilt from the seeded generator (never read back
+from what the HIP kernels wrote): the synthesized prefix rows plus the raw new
+keys and values, which the oracle encodes itself.
+
+Tolerances (derived in the design notes):
+  * selected pages: bit-exact, except pages whose oracle score lies within
+    tau = 1e-4 * max(1, |s_k|) of the k-th largest score s_k;
+  * z, o: max_i |gpu - ref| / ||ref||_2 <= 5e-3 per (sequence, head), with the
+    reference evaluated on the GPU's own accepted page set;
+  * lse: absolute 2e-3 (natural log units);
+  * encode: bf16 latents within one bf16 unit in the last place of the
+    oracle's correctly rounded value; f32 latents within 1e-5 of the row norm.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+
+OUT_TOL = 5e-3
+LSE_TOL = 2e-3
+TIE_REL = 1e-4
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def factors_np(sess, g: int) -> dict:
+    return {k: (None if v is None else f64(v[g])) for k, v in sess.factors.items()}
+
+
+def oracle_state(sess, b: int, g: int) -> dict:
+    """Oracle cache of (b, g) after the step's append: seeded prefix + oracle encode."""
+    wl = sess.wl
+    L0, n = sess.lens_before[b], sess.n_new[b]
+    rows = sess.prefix_rows(b)
+    st = {k: f64(v[g]) for k, v in rows.items()}
+    if n:
+        off = sum(sess.n_new[:b])
+        Kn = f64(sess.k_new[off:off + n, g])
+        Vn = f64(sess.v_new[off:off + n, g])
+        f = factors_np(sess, g)
+        st = O.append_tokens(st, L0, Kn, Vn, f["A_v"], f["A_k"], f["W_pred"],
+                             key_mode=wl.key_mode, storage=wl.storage)
+    return st
+
+
+def q_group(sess, b: int, g: int) -> np.ndarray:
+    G = sess.wl.group
+    return f64(sess.q[b, g * G:(g + 1) * G])
+
+
+def accepted_selection(S: np.ndarray, k: int, gpu_sel, slack: float = 0.0) -> tuple[bool, int]:
+    """Tie-band acceptance of a GPU page set; returns (ok, pages inside the band)."""
+    gset = [int(j) for j in gpu_sel if j >= 0]
+    if k == 0:
+        return len(gset) == 0, 0
+    if len(gset) != k or len(set(gset)) != k or gset != sorted(gset):
+        return False, 0
+    sk = np.sort(S)[::-1][k - 1]
+    tau = TIE_REL * max(1.0, abs(sk)) + slack
+    must = set(np.nonzero(S > sk + tau)[0].tolist())
+    may = set(np.nonzero(S >= sk - tau)[0].tolist())
+    G = set(gset)
+    band = len(may - must)
+    return must <= G and G <= may, band
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |gpu - ref| / ||ref||_2 over the last axis, worst row."""
+    gpu = np.atleast_2d(gpu)
+    ref = np.atleast_2d(ref)
+    num = np.abs(gpu - ref).max(axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    out = np.where(den > 0, num / np.where(den > 0, den, 1), num)
+    return float(out.max()) if out.size else 0.0
+
+
+def stage_oracle_sequence(sess, b: int) -> list:
+    """Overwrite sequence b's pages with the oracle's own cache (all KV heads),
+    so a following GPU decode reads exactly the oracle's stored values.
+    Returns the per-head oracle states."""
+    states = [oracle_state(sess, b, g) for g in range(sess.wl.num_kv_heads)]
+    rows = {k: torch.from_numpy(np.stack([st[k][:sess.seq_lens[b]] for st in states]))
+            for k in states[0]}
+    sess.write_rows(b, rows)
+    return states
+
+
+def new_token_slack(sess, b: int, g: int, st: dict) -> float:
+    """Bound on how far a routing score can move when the new tokens' latents
+    differ from the oracle's by at most one bf16 unit in the last place:
+    sum_i |q_hat_i| ulp(v_i) + sum_i |q_tilde_i| ulp(c_i), worst token and head."""
+    wl = sess.wl
+    n = sess.n_new[b]
+    if not wl.routed or n == 0 or wl.storage != "bf16":
+        return 0.0
+    f = factors_np(sess, g)
+    qh, qt = O.project_queries(q_group(sess, b, g), f["W_pred"], f["B_k"])
+    L0 = sess.lens_before[b]
+    v = st["v"][L0:L0 + n]
+    c = st["k_lat"][L0:L0 + n]
+    bound = np.abs(qh) @ bf16_ulp(v).T + np.abs(qt) @ bf16_ulp(c).T   # [G, n]
+    return float(bound.max()) * 1.01 + 1e-6
+
+
+def check_pair(sess, b: int, g: int, *, state=None, check_scores=True, slack=0.0) -> dict:
+    """Compare the GPU step's outputs for (b, g) against the oracle. `slack`
+    widens the page-score tolerance and the tie band (end-to-end runs, where
+    the GPU encoded the new tokens itself)."""
+    wl = sess.wl
+    G, P, L = wl.group, wl.page_size, sess.seq_lens[b]
+    st = oracle_state(sess, b, g) if state is None else state
+    f = factors_np(sess, g)
+    q = q_group(sess, b, g)
+    info = {}
+    if wl.routed:
+        N = -(-L // P)
+        S = O.page_scores(q, st["v"], st["k_lat"], f["W_pred"], f["B_k"], L, P)
+        k = O.pages_to_keep(N, wl.topk_num, wl.topk_den)
+        gsel = sess.sel[b, g].cpu().numpy()
+        ok, band = accepted_selection(S, k, gsel, slack)
+        assert ok, f"pair ({b},{g}): GPU pages {sorted(gsel[gsel >= 0].tolist())[:16]}... not accepted"
+        info["tie_band"] = band
+        pages = [int(j) for j in gsel if j >= 0]
+        if check_scores and N:
+            gs = f64(sess.page_scores[b, g, :N])
+            tol = TIE_REL * np.maximum(1.0, np.abs(S)) + slack
+            assert np.all(np.abs(gs - S) <= tol), f"page scores off by {np.abs(gs - S).max()}"
+            assert np.all(np.isneginf(f64(sess.page_scores[b, g, N:])))
+    else:
+        pages = list(range(-(-L // P)))
+    z, o, lse = O.attend_selected(q, st, f, L, P, pages, key_mode=wl.key_mode, scale=sess.scale)
+    zg = f64(sess.z[b, g * G:(g + 1) * G])
+    og = f64(sess.o[b, g * G:(g + 1) * G])
+    lg = f64(sess.lse[b, g * G:(g + 1) * G])
+    info["z_err"] = rel_err(zg, z)
+    info["o_err"] = rel_err(og, o)
+    assert info["z_err"] <= OUT_TOL, f"z rel err {info['z_err']}"
+    assert info["o_err"] <= OUT_TOL, f"o rel err {info['o_err']}"
+    if np.all(np.isinf(lse)):
+        assert np.all(np.isneginf(lg))
+    else:
+        info["lse_err"] = float(np.abs(lg - lse).max())
+        assert info["lse_err"] <= LSE_TOL, f"lse err {info['lse_err']}"
+    return info
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |x| (normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    _, e = np.frexp(ax)
+    return np.ldexp(1.0, e - 8)
+
+
+def check_encode(sess, b: int, g: int) -> dict:
+    """GPU-written latents of (b, g)'s new tokens against the oracle's encode."""
+    wl = sess.wl
+    L0, n = sess.lens_before[b], sess.n_new[b]
+    if n == 0:
+        return {}
+    off = sum(sess.n_new[:b])
+    f = factors_np(sess, g)
+    enc = O.encode_tokens(f64(sess.k_new[off:off + n, g]), f64(sess.v_new[off:off + n, g]),
+                          f["A_v"], f["A_k"], f["W_pred"], key_mode=wl.key_mode, storage=wl.storage)
+    got = {k: f64(v[g]) for k, v in sess.read_rows(b, L0 + n, L0).items()}
+    info = {}
+    for name in ("v", "k_lat"):
+        ref, gv = enc[name], got[name]
+        if wl.storage == "bf16":
+            diff = np.abs(gv - ref) / bf16_ulp(ref)
+            info[name + "_max_ulp"] = float(diff.max())
+            info[name + "_frac_off"] = float((diff > 0).mean())
+            assert diff.max() <= 1.0 + 1e-9, f"{name}: {diff.max()} ulp"
+        else:
+            scale = np.linalg.norm(ref, axis=-1, keepdims=True) + 1e-30
+            err = float((np.abs(gv - ref) / scale).max())
+            info[name + "_rel"] = err
+            assert err <= 1e-5, f"{name}: rel {err}"
+    if wl.routed:
+        assert np.array_equal(got["k_exact"], enc["k_exact"]), "original keys not copied exactly"
+    return info

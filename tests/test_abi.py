@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every function the header declares, and
+rejects bad arguments on the host before touching the GPU. CPU only: no call
+here reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_rank_amd import _lib as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvlr.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from decode_attention_rank_amd import build
+        build.build(verbose=False)
+    return K.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kvlr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("kvlr_append_encode", "kvlr_route_pages", "kvlr_decode_attn", "kvlr_upproject",
+               "kvlr_project_queries"):
+        assert fn in names
+    assert set(names) == set(K.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert K.kvlr_version() >= 100
+    assert K.kvlr_status_string(0) == "ok"
+    assert "invalid" in K.kvlr_status_string(1)
+    assert "unsupported" in K.kvlr_status_string(2)
+    assert "workspace" in K.kvlr_status_string(3)
+
+
+def _shape(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, rank_v=64, rank_k=32,
+                dtype=K.KVLR_DTYPE_BF16, key_mode=K.KVLR_KEYS_EXACT, num_phys_pages=8192)
+    base.update(kw)
+    return K.make_shape(**base)
+
+
+def test_qproj_width_and_workspace_size(lib):
+    assert K.kvlr_qproj_width(_shape()) == 96
+    assert K.kvlr_qproj_width(_shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)) == 64
+    ws = K.kvlr_workspace_bytes(_shape(), 16, 512)
+    # routing scores alone need B * H_kv * max_pages floats
+    assert ws >= 16 * 8 * 512 * 4
+    assert K.kvlr_workspace_bytes(_shape(), 16, 0) == 0
+    assert K.kvlr_workspace_bytes(_shape(head_dim=96), 16, 512) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), K.KVLR_ERR_UNSUPPORTED),
+    (dict(rank_v=48), K.KVLR_ERR_UNSUPPORTED),
+    (dict(page_size=128), K.KVLR_ERR_UNSUPPORTED),
+    (dict(num_q_heads=48, num_kv_heads=3), K.KVLR_ERR_UNSUPPORTED),   # G = 16
+    (dict(num_q_heads=30), K.KVLR_ERR_INVALID_ARGUMENT),              # not a multiple
+    (dict(rank_k=256), K.KVLR_ERR_INVALID_ARGUMENT),                  # above head_dim
+    (dict(dtype=7), K.KVLR_ERR_INVALID_ARGUMENT),
+    (dict(key_mode=3), K.KVLR_ERR_INVALID_ARGUMENT),
+    (dict(num_phys_pages=0), K.KVLR_ERR_INVALID_ARGUMENT),
+])
+def test_bad_shapes_are_rejected(lib, kw, status):
+    s = _shape(**kw)
+    f = K.make_factors()
+    assert lib.kvlr_upproject(ctypes.byref(s), ctypes.byref(f), None, None, 1, None) == status
+
+
+def test_bad_arguments_are_rejected_before_launch(lib):
+    s = _shape()
+    c = K.make_cache()
+    f = K.make_factors()
+    E = K.KVLR_ERR_INVALID_ARGUMENT
+    # null pointers
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c), None, None, None, 512, 1, 8, 64,
+                                None, None, None, 0, 16, None) == E
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c), None, None, None, None, 512, None,
+                                0, 0.1, None, None, None, 0, 16, None) == E
+    assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None, None,
+                                  None, None, None, 512, 16, 16, None) == E
+    assert lib.kvlr_project_queries(ctypes.byref(s), ctypes.byref(f), None, None, 16, None) == E
+    # k_max below the routing bound, or above max pages
+    fake = 1 << 20  # aligned non-null placeholder; never dereferenced on these paths
+    c2 = K.make_cache(fake, fake, fake)
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 63,
+                                fake, None, fake, 1 << 30, 16, None) == E
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 513,
+                                fake, None, fake, 1 << 30, 16, None) == E
+    # topk fraction with a zero denominator
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 0, 64,
+                                fake, None, fake, 1 << 30, 16, None) == E
+    # misaligned pointer
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake + 4, fake, fake, 512, 1, 8,
+                                64, fake, None, fake, 1 << 30, 16, None) == E
+    # workspace too small
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
+                                fake, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, fake,
+                                64, 0.1, fake, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    # non-positive or non-finite softmax scale
+    for sc in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512,
+                                    fake, 64, sc, fake, None, fake, 1 << 30, 16, None) == E
+    # routing needs the routed (exact-key) cache
+    sl = _shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)
+    assert lib.kvlr_route_pages(ctypes.byref(sl), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
+                                fake, None, fake, 1 << 30, 16, None) == K.KVLR_ERR_UNSUPPORTED
+    # negative batch / sizes
+    assert lib.kvlr_upproject(ctypes.byref(s), ctypes.byref(f), fake, fake, -1, None) == E
+    assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
+                                  fake, fake, fake, 512, 16, -5, None) == E
+    assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
+                                  fake, fake, fake, 0, 16, 16, None) == E
+
+
+def test_empty_batches_are_no_ops(lib):
+    s = _shape()
+    c = K.make_cache()
+    f = K.make_factors()
+    assert lib.kvlr_upproject(ctypes.byref(s), ctypes.byref(f), None, None, 0, None) == 0
+    assert lib.kvlr_project_queries(ctypes.byref(s), ctypes.byref(f), None, None, 0, None) == 0
+    assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None, None,
+                                  None, None, None, 512, 16, 0, None) == 0
+    assert lib.kvlr_workspace_init(None, 0, None) == 0
+
+
+def test_python_binding_raises(lib):
+    with pytest.raises(K.KvlrError) as ei:
+        K.kvlr_upproject(_shape(head_dim=96), K.make_factors(), None, None, 1)
+    assert ei.value.status == K.KVLR_ERR_UNSUPPORTED

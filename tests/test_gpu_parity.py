@@ -1,0 +1,230 @@
+"""GPU parity of the whole decode step against the oracle, on small shapes
+that span several tiles and ragged tails, plus edge cases and invariances.
+
+Every case first runs the step end to end (GPU encode, then GPU decode) and
+checks it with the tie band widened by the bound on what one-ulp encode
+differences can do to a score; then it overwrites the sequences' pages with the
+oracle's own encoded cache and checks the decode strictly (bit-exact page sets
+outside the 1e-4 tie band, 5e-3 relative output error).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decode_attention_rank_amd import _lib as K
+from decode_attention_rank_amd.session import DecodeSession
+from decode_attention_rank_amd.workloads import Workload
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def make_wl(*, G, d, rv, rk, P, storage, routed, B=4, Hkv=2, topk=(1, 8), seed=11, planted=0.0):
+    rs = min(48, d // 2)
+    ns = min(rv, rs // 2, d - rk) if routed else 0
+    return Workload(
+        name=f"t-G{G}-d{d}-rv{rv}-rk{rk}-P{P}-{storage}-{'exact' if routed else 'latent'}",
+        batch=B, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, page_size=P, rank_v=rv,
+        rank_k=rk, storage=storage, key_mode="exact" if routed else "latent", context=0,
+        topk_num=topk[0], topk_den=topk[1], signal_rank=rs, shared_rank=ns, noise_std=0.05,
+        planted_frac=planted, planted_boost=4.0 if planted else 0.0, seed=seed)
+
+
+def run_and_check(sess, pairs=None, stage=True):
+    wl = sess.wl
+    sess.step()
+    torch.cuda.synchronize()
+    pairs = pairs or [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    out = []
+    for b, g in pairs:
+        H.check_encode(sess, b, g)
+        st = H.oracle_state(sess, b, g)
+        out.append(H.check_pair(sess, b, g, state=st, slack=H.new_token_slack(sess, b, g, st)))
+    if stage:
+        states = {b: H.stage_oracle_sequence(sess, b) for b in sorted({b for b, _ in pairs})}
+        sess.decode()
+        torch.cuda.synchronize()
+        for b, g in pairs:
+            out.append(H.check_pair(sess, b, g, state=states[b][g]))
+    return out
+
+
+ROUTED = [
+    dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16"),
+    dict(G=8, d=128, rv=32, rk=32, P=64, storage="bf16"),
+    dict(G=1, d=64, rv=16, rk=16, P=16, storage="bf16"),
+    dict(G=2, d=64, rv=32, rk=16, P=32, storage="bf16"),
+    dict(G=4, d=64, rv=16, rk=32, P=16, storage="f32"),
+    dict(G=8, d=128, rv=64, rk=64, P=32, storage="f32"),
+]
+
+DENSE = [
+    dict(G=4, d=128, rv=64, rk=64, P=64, storage="bf16"),
+    dict(G=1, d=64, rv=16, rk=16, P=16, storage="f32"),
+    dict(G=8, d=128, rv=32, rk=16, P=32, storage="bf16"),
+    dict(G=2, d=64, rv=64, rk=64, P=64, storage="f32"),
+]
+
+LENS = [1, 777, 640, 2049]
+
+
+@pytest.mark.parametrize("cfg", ROUTED, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_routed_small(cfg):
+    wl = make_wl(routed=True, **cfg)
+    _say("case", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    run_and_check(sess)
+
+
+@pytest.mark.parametrize("cfg", DENSE, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_dense_small(cfg):
+    wl = make_wl(routed=False, **cfg)
+    _say("case", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    run_and_check(sess)
+
+
+def test_tiny_workload_all_pairs():
+    from decode_attention_rank_amd.workloads import WORKLOADS
+    wl = WORKLOADS["tiny-dense-mha-512"]
+    _say("case", wl.name)
+    sess = DecodeSession(wl, "cuda")
+    run_and_check(sess)
+
+
+@pytest.mark.parametrize("topk", [(1, 1), (1, 10 ** 6), (3, 8)])
+def test_routing_fraction_extremes(topk):
+    # (1, 1): every page kept, so routed attention is dense exact-key attention
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True, topk=topk)
+    _say("case", wl.name, topk)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=5)
+    run_and_check(sess)
+    if topk == (1, 1):
+        for b, L in enumerate(LENS):
+            N = -(-L // 64)
+            sel = sess.sel[b].cpu().numpy()
+            assert (sel[:, :N] == np.arange(N)).all()
+
+
+def test_empty_sequence_in_batch():
+    wl = make_wl(G=4, d=64, rv=32, rk=16, P=16, storage="bf16", routed=True, B=3)
+    _say("case empty sequence")
+    sess = DecodeSession(wl, "cuda", seq_lens=[0, 100, 65], append_per_seq=3)
+    run_and_check(sess)
+    assert (sess.sel[0].cpu() == -1).all()
+    assert torch.isneginf(sess.lse[0]).all()
+    assert (sess.z[0] == 0).all() and (sess.o[0] == 0).all()
+
+
+def test_nan_in_unused_slots_and_pages_is_ignored():
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
+    _say("case NaN tails")
+    sess = DecodeSession(wl, "cuda", seq_lens=[65, 777, 130, 1000], append_per_seq=9,
+                         spare_pages=7, tail_fill=float("nan"))
+    run_and_check(sess)
+    assert torch.isfinite(sess.o).all() and torch.isfinite(sess.z).all()
+
+
+def test_page_table_permutation_invariance():
+    wl = make_wl(G=8, d=128, rv=32, rk=32, P=64, storage="bf16", routed=True)
+    _say("case page-table permutation")
+    a = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=11)
+    pt = a.page_table_cpu.clone()
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(a.num_phys, generator=g).to(torch.int32)
+    pt2 = torch.where(pt >= 0, perm[pt.clamp(min=0).long()], pt)
+    b = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=11, page_table=pt2, num_phys=a.num_phys)
+    a.step()
+    b.step()
+    torch.cuda.synchronize()
+    for name in ("sel", "page_scores", "z", "lse", "o"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_step_is_deterministic():
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
+    _say("case determinism")
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    s.step()
+    torch.cuda.synchronize()
+    first = {n: getattr(s, n).clone() for n in ("sel", "page_scores", "z", "lse", "o", "v_lat", "k_lat")}
+    for _ in range(3):
+        s.step()
+    torch.cuda.synchronize()
+    for n, t in first.items():
+        assert torch.equal(getattr(s, n), t), n
+
+
+@pytest.mark.parametrize("routed", [True, False])
+def test_chunked_append_equals_one_shot(routed):
+    wl = make_wl(G=4, d=128, rv=64, rk=32 if routed else 64, P=64, storage="bf16", routed=routed)
+    _say("case chunked append", routed)
+    lens = [300, 1000, 77, 129]
+    one = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=70)
+    two = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=70)
+    one.append()
+    # the same tokens in two calls: first 29 (or fewer) of each sequence, then the rest
+    n1 = [min(29, n) for n in two.n_new]
+    cu1, cu2, lb2, k1, v1, k2, v2 = [0], [0], [], [], [], [], []
+    off = 0
+    for b, n in enumerate(two.n_new):
+        k1.append(two.k_new[off:off + n1[b]])
+        v1.append(two.v_new[off:off + n1[b]])
+        k2.append(two.k_new[off + n1[b]:off + n])
+        v2.append(two.v_new[off + n1[b]:off + n])
+        cu1.append(cu1[-1] + n1[b])
+        cu2.append(cu2[-1] + n - n1[b])
+        lb2.append(two.lens_before[b] + n1[b])
+        off += n
+    dev = "cuda"
+    for kk, vv, cu, lb in ((k1, v1, cu1, two.lens_before), (k2, v2, cu2, lb2)):
+        kt = torch.cat(kk).contiguous()
+        vt = torch.cat(vv).contiguous()
+        K.kvlr_append_encode(two.shape, two.kfactors, two.kcache, kt, vt,
+                             torch.tensor(cu, dtype=torch.int32, device=dev),
+                             torch.tensor(lb, dtype=torch.int32, device=dev), two.page_table,
+                             two.max_pages, wl.batch, cu[-1])
+    torch.cuda.synchronize()
+    assert torch.equal(one.v_lat, two.v_lat)
+    assert torch.equal(one.k_lat, two.k_lat)
+    if routed:
+        assert torch.equal(one.k_exact, two.k_exact)
+
+
+def test_query_projection_and_upprojection_match_oracle():
+    wl = make_wl(G=8, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
+    _say("case q_proj / upproject")
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=1)
+    s.step()
+    torch.cuda.synchronize()
+    qp = H.f64(s.q_proj)
+    z = H.f64(s.z)
+    o = H.f64(s.o)
+    G = wl.group
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            f = H.factors_np(s, g)
+            qh, qt = O.project_queries(H.q_group(s, b, g), f["W_pred"], f["B_k"])
+            got = qp[b, g * G:(g + 1) * G]
+            assert H.rel_err(got, np.concatenate([qh, qt], axis=1)) < 1e-5
+            ref = O.upproject(z[b, g * G:(g + 1) * G], f["B_v"])
+            assert H.rel_err(o[b, g * G:(g + 1) * G], ref) < 1e-5
+
+
+def test_binding_reports_bad_launch_arguments():
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=1)
+    with pytest.raises(K.KvlrError):
+        K.kvlr_route_pages(s.shape, s.kcache, s.q_proj, s.seq_lens_dev, s.page_table, s.max_pages,
+                           1, 8, s.k_max - 1, s.sel, None, s.workspace, s.ws_bytes, wl.batch)
+    with pytest.raises(K.KvlrError):
+        K.kvlr_decode_attn(s.shape, s.kcache, s.q, s.q_proj, s.seq_lens_dev, s.page_table,
+                           s.max_pages, s.sel, s.k_max, 0.1, s.z, s.lse, s.workspace, 64, wl.batch)

@@ -1,0 +1,68 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the same five library calls on the same buffers).
+
+The GPU runs the whole step for every (sequence, KV head); the oracle checks a
+sample of pairs one by one: the first and last pairs, a middle one, and for
+ragged contexts the longest and shortest sequences.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_rank_amd import synth
+from decode_attention_rank_amd.session import DecodeSession
+from decode_attention_rank_amd.workloads import WORKLOADS
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["llama3-8b-dense-32k", "llama3-8b-routed-32k", "llama3-70b-share-routed-128k",
+        "mixed-append-routed-ragged"]
+
+
+def _sample(sess):
+    wl = sess.wl
+    B, Hkv = wl.batch, wl.num_kv_heads
+    pairs = [(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)]
+    if wl.ragged:
+        L = sess.seq_lens
+        pairs += [(int(np.argmax(L)), 1 % Hkv), (int(np.argmin(L)), (Hkv - 1) // 2)]
+    seen, out = set(), []
+    for p in pairs:
+        if p not in seen:
+            seen.add(p)
+            out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    wl = WORKLOADS[name]
+    print("case", name, flush=True)
+    sess = DecodeSession(wl, "cuda")
+    sess.step()
+    torch.cuda.synchronize()
+    pairs = _sample(sess)
+    states = {}
+    for b, g in pairs:
+        H.check_encode(sess, b, g)
+        st = H.oracle_state(sess, b, g)
+        states[(b, g)] = st
+        info = H.check_pair(sess, b, g, state=st, slack=H.new_token_slack(sess, b, g, st))
+        print("  end-to-end", (b, g), info, flush=True)
+    staged = {b: H.stage_oracle_sequence(sess, b) for b in sorted({b for b, _ in pairs})}
+    sess.decode()
+    torch.cuda.synchronize()
+    for b, g in pairs:
+        info = H.check_pair(sess, b, g, state=staged[b][g])
+        print("  staged", (b, g), info, flush=True)
+    if wl.planted_frac > 0:
+        # the planted pages carry a clear routing signal: routing must find them
+        for b, g in pairs:
+            N = -(-sess.seq_lens[b] // wl.page_size)
+            planted = set(synth.planted_pages(wl, b, N).tolist())
+            sel = set(sess.sel[b, g].cpu().numpy().tolist())
+            recall = len(planted & sel) / len(planted)
+            print("  planted recall", (b, g), recall, flush=True)
+            assert recall >= 0.9
