@@ -225,35 +225,34 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         Ls += f * s_ml[w][h][1];
       }
     }
-    part[h * PW + 2 + e] = Z;
+    store_shared_f32(&part[h * PW + 2 + e], Z);
     if (e == 0) {
-      part[h * PW] = M;
-      part[h * PW + 1] = Ls;
+      store_shared_f32(&part[h * PW], M);
+      store_shared_f32(&part[h * PW + 1], Ls);
     }
   }
 
   // ---- ticket: the last workgroup of the pair merges the splits
+  wait_stores_done();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(&counters[pair], 1u);
+    const uint32_t prev = take_ticket(&counters[pair]);
     s_last = (prev == static_cast<uint32_t>(num_splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const float* allp = partials + static_cast<size_t>(pair) * num_splits * G * PW;
   for (int i = threadIdx.x; i < G * RV; i += kThreads) {
     const int h = i / RV, e = i - h * RV;
     float M = kNegInf;
-    for (int sp = 0; sp < num_splits; ++sp) M = fmaxf(M, allp[(sp * G + h) * PW]);
+    for (int sp = 0; sp < num_splits; ++sp) M = fmaxf(M, load_shared_f32(&allp[(sp * G + h) * PW]));
     float Z = 0.f, Ls = 0.f;
     if (M != kNegInf) {
       for (int sp = 0; sp < num_splits; ++sp) {
         const float* r = allp + (sp * G + h) * PW;
-        const float f = fast_exp2(r[0] - M);
-        Z += f * r[2 + e];
-        Ls += f * r[1];
+        const float f = fast_exp2(load_shared_f32(&r[0]) - M);
+        Z += f * load_shared_f32(&r[2 + e]);
+        Ls += f * load_shared_f32(&r[1]);
       }
     }
     const int qh = g * G + h;
@@ -263,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
           (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
     }
   }
-  if (threadIdx.x == 0) counters[pair] = 0u;
+  if (threadIdx.x == 0) reset_ticket(&counters[pair]);
 }
 
 template <class S, int G, int KW, int RV>

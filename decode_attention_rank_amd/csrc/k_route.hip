@@ -66,7 +66,7 @@ __device__ void select_pages(float* scores, int N, int k, int k_max, int max_pag
       hist[tid] = 0;  // kThreads == 256 bins
       __syncthreads();
       for (int j = tid; j < N; j += kThreads) {
-        const uint32_t key = order_key(scores[j]);
+        const uint32_t key = order_key(load_shared_f32(&scores[j]));
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -107,7 +107,7 @@ __device__ void select_pages(float* scores, int N, int k, int k_max, int max_pag
   for (int j0 = 0; j0 < N; j0 += kThreads) {
     const int j = j0 + tid;
     const bool in = j < N;
-    const uint32_t key = in ? order_key(scores[j]) : 0u;
+    const uint32_t key = in ? order_key(load_shared_f32(&scores[j])) : 0u;
     const bool gt = in && (take_all || key > prefix);
     const bool eq = in && !take_all && k > 0 && key == prefix;
     int eq_total = 0;
@@ -161,9 +161,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       const uint8_t* vb = v_lat + (phys * Hkv + g) * slab_v + slot * 16;
       const uint8_t* kb = k_lat + (phys * Hkv + g) * slab_k + slot * 16;
 #pragma unroll
-      for (int c = 0; c < CV; ++c) vc[c] = load16(vb + static_cast<size_t>(c) * P * 16);
+      for (int c = 0; c < CV; ++c) vc[c] = load16_stream(vb + static_cast<size_t>(c) * P * 16);
 #pragma unroll
-      for (int c = 0; c < CK; ++c) kc[c] = load16(kb + static_cast<size_t>(c) * P * 16);
+      for (int c = 0; c < CK; ++c) kc[c] = load16_stream(kb + static_cast<size_t>(c) * P * 16);
     } else {
 #pragma unroll
       for (int c = 0; c < CV; ++c) vc[c] = make_uint4(0, 0, 0, 0);
@@ -197,20 +197,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       m = row16_max(m);
       if (P == 32) m = fmaxf(m, __shfl_xor(m, 16, kWave));
     }
-    if (slot == 0 && valid) sc[j] = m;
+    if (slot == 0 && valid) store_shared_f32(&sc[j], m);
   }
 
   // Ticket: the last workgroup of this pair selects its pages.
   __shared__ int s_last;
+  wait_stores_done();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(&counters[pair], 1u);
+    const uint32_t prev = take_ticket(&counters[pair]);
     s_last = (prev == static_cast<uint32_t>(num_splits - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const int N = (L + P - 1) >> log2P;
   int k = 0;
   if (N > 0) {
@@ -219,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     k = min(k, k_max);
   }
   select_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
-  if (threadIdx.x == 0) counters[pair] = 0u;
+  if (threadIdx.x == 0) reset_ticket(&counters[pair]);
 }
 
 template <class S, int G, int RV, int RK>

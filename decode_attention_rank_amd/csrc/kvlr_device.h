@@ -59,6 +59,38 @@ __device__ inline void store16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
+// Streaming 16-byte load: marked non-temporal, for data read once per launch.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off without cache flushes.
+//
+// The L2 of each XCD is not coherent with the others, and a release/acquire
+// fence at device scope writes back and invalidates the whole L2 of the XCD
+// that runs it. Instead, values that another workgroup will read are written
+// and read with device-scope relaxed atomics (coherent at device scope: they
+// bypass the non-coherent L2 lines), each wave waits for its stores to
+// complete, and the ticket itself is a device-scope atomic add. A workgroup
+// that draws the last ticket has therefore seen every other workgroup's
+// stores completed before their tickets.
+__device__ inline void store_shared_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_shared_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ inline uint32_t take_ticket(uint32_t* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void reset_ticket(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 __device__ inline void static_for(F&& f) {

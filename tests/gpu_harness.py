@@ -10,8 +10,8 @@ Tolerances (derived in the design notes):
   * z, o: max_i |gpu - ref| / ||ref||_2 <= 5e-3 per (sequence, head), with the
     reference evaluated on the GPU's own accepted page set;
   * lse: absolute 2e-3 (natural log units);
-  * encode: bf16 latents within one bf16 unit in the last place of the
-    oracle's correctly rounded value; f32 latents within 1e-5 of the row norm.
+  * encode: one unit in the last place of the stored type plus the float32
+    accumulation bound n * 2**-24 * sum |a_i b_i| (see check_encode).
 """
 
 from __future__ import annotations
@@ -159,29 +159,52 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def check_encode(sess, b: int, g: int) -> dict:
-    """GPU-written latents of (b, g)'s new tokens against the oracle's encode."""
+    """GPU-written latents of (b, g)'s new tokens against the oracle's encode.
+
+    The kernel accumulates in float32 and then rounds once to the storage
+    type, so an element may differ from the oracle's correctly rounded value
+    by one unit in the last place of the stored type plus the float32
+    accumulation error, bounded by gamma * sum_i |a_i b_i| with
+    gamma = n * 2**-24 for n accumulated terms. The residual latent also
+    inherits the GPU's own stored value latent, through |dv| |W_pred A_k|.
+    """
     wl = sess.wl
     L0, n = sess.lens_before[b], sess.n_new[b]
     if n == 0:
         return {}
     off = sum(sess.n_new[:b])
     f = factors_np(sess, g)
-    enc = O.encode_tokens(f64(sess.k_new[off:off + n, g]), f64(sess.v_new[off:off + n, g]),
-                          f["A_v"], f["A_k"], f["W_pred"], key_mode=wl.key_mode, storage=wl.storage)
+    Kn = f64(sess.k_new[off:off + n, g])
+    Vn = f64(sess.v_new[off:off + n, g])
+    enc = O.encode_tokens(Kn, Vn, f["A_v"], f["A_k"], f["W_pred"], key_mode=wl.key_mode,
+                          storage=wl.storage)
     got = {k: f64(v[g]) for k, v in sess.read_rows(b, L0 + n, L0).items()}
+    d, rv = wl.head_dim, wl.rank_v
+    u = 2.0 ** -24
+    if wl.storage == "bf16":
+        def unit(x, y):
+            return bf16_ulp(np.maximum(np.abs(x), np.abs(y)))
+    else:
+        def unit(x, y):
+            return np.maximum(np.abs(x), np.abs(y)) * 2.0 ** -23
     info = {}
-    for name in ("v", "k_lat"):
-        ref, gv = enc[name], got[name]
-        if wl.storage == "bf16":
-            diff = np.abs(gv - ref) / bf16_ulp(ref)
-            info[name + "_max_ulp"] = float(diff.max())
-            info[name + "_frac_off"] = float((diff > 0).mean())
-            assert diff.max() <= 1.0 + 1e-9, f"{name}: {diff.max()} ulp"
-        else:
-            scale = np.linalg.norm(ref, axis=-1, keepdims=True) + 1e-30
-            err = float((np.abs(gv - ref) / scale).max())
-            info[name + "_rel"] = err
-            assert err <= 1e-5, f"{name}: rel {err}"
-    if wl.routed:
+    # value latent: d products per element
+    tol_v = unit(enc["v"], got["v"]) + d * u * (np.abs(Vn) @ np.abs(f["A_v"]))
+    dv = np.abs(got["v"] - enc["v"])
+    assert np.all(dv <= tol_v), f"v off by {(dv / tol_v).max():.2f} x tolerance"
+    info["v_frac_off"] = float((dv > 0).mean())
+    if wl.key_mode == "exact":
+        M = f["W_pred"] @ f["A_k"]
+        absM = np.abs(M)
+        terms = np.abs(Kn) @ np.abs(f["A_k"]) + np.abs(got["v"]) @ absM
+        m_err = d * u * (np.abs(f["W_pred"]) @ np.abs(f["A_k"])) + 2.0 ** -16 * absM
+        tol_c = (unit(enc["k_lat"], got["k_lat"]) + (d + 2 * rv) * u * terms
+                 + dv @ absM + np.abs(got["v"]) @ m_err)
+    else:
+        tol_c = unit(enc["k_lat"], got["k_lat"]) + d * u * (np.abs(Kn) @ np.abs(f["A_k"]))
+    dc = np.abs(got["k_lat"] - enc["k_lat"])
+    assert np.all(dc <= tol_c), f"k_lat off by {(dc / tol_c).max():.2f} x tolerance"
+    info["k_lat_frac_off"] = float((dc > 0).mean())
+    if wl.key_mode == "exact":
         assert np.array_equal(got["k_exact"], enc["k_exact"]), "original keys not copied exactly"
     return info
