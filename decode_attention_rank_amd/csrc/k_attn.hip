@@ -22,6 +22,10 @@
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
 
+#ifndef KVLR_ATTN_PREFETCH
+#define KVLR_ATTN_PREFETCH 0
+#endif
+
 namespace kvlr {
 namespace {
 
@@ -34,120 +38,97 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <class S, int G, int KW, int RV>
+template <class S, int G, int KW, int RV, bool ROWPAGE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(
     const uint8_t* __restrict__ keys, const uint8_t* __restrict__ v_lat,
-    const float* __restrict__ qsrc, int q_stride, const int32_t* __restrict__ seq_lens,
+    const float* __restrict__ qsrc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ sel,
-    float* __restrict__ partials, uint32_t* __restrict__ counters, float* __restrict__ z_out,
+    const int32_t* __restrict__ sel_counts, float* __restrict__ partials, uint32_t* __restrict__ counters, float* __restrict__ z_out,
     float* __restrict__ lse_out, int Hq, int Hkv, int P, int log2P, int max_pages, int k_max,
-    float scale_log2e, int rows_per_split, int num_splits) {
+    float scale_log2e, int rows_per_chunk, int max_splits, int batch) {
   constexpr int CH = S::CH;
-  constexpr int CKW = KW / CH;   // key chunks per token
-  constexpr int CV = RV / CH;    // value-latent chunks per token
+  constexpr int CKW = KW / CH;     // key chunks per token
+  constexpr int CV = RV / CH;      // value-latent chunks per token
   constexpr int TPL = kWave / CV;  // token stride between a lane's P.V tokens
-  constexpr int PW = RV + 2;     // partial record: m, l, z[RV]
+  constexpr int PW = RV + 2;       // partial record: m, l, z[RV]
 
+  extern __shared__ int s_base[];
   __shared__ float s_p[kWaves][kWave][G];
   __shared__ float s_ml[kWaves][G][2];
   __shared__ float s_z[kWaves][G][RV];
   __shared__ int s_last;
 
-  const int pair = blockIdx.y;
-  const int b = pair / Hkv;
-  const int g = pair - b * Hkv;
-  const int L = seq_lens[b];
-  const int N = (L + P - 1) >> log2P;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int ipr_log2 = 6 - log2P;  // items (pages) per row = 64 / P
-  const int n_items = sel ? k_max : N;
-  const int nrows = (n_items + (1 << ipr_log2) - 1) >> ipr_log2;
-  const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
-  const int32_t* __restrict__ sl = sel ? sel + static_cast<size_t>(pair) * k_max : nullptr;
-  const float* __restrict__ qg = qsrc + static_cast<size_t>(b * Hq + g * G) * q_stride;
   const size_t slab_k = static_cast<size_t>(CKW) * P * 16;
   const size_t slab_v = static_cast<size_t>(CV) * P * 16;
-
-  float m[G], lsum[G], z[G][CH];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    lsum[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < CH; ++e) z[h][e] = 0.f;
-  }
   const int my_c = lane % CV;
 
-  const int row0 = blockIdx.x * rows_per_split;
-  const int row1 = min(row0 + rows_per_split, nrows);
-  for (int row = row0 + wave; row < row1; row += kWaves) {
-    // ---- this lane's token: item row*IPR + lane/P, slot lane%P
-    const int item = (row << ipr_log2) + (lane >> log2P);
-    const int slot = lane & (P - 1);
-    int page = -1;
-    if (item < n_items) page = sl ? sl[item] : item;
-    const bool valid = page >= 0 && page < N && (page << log2P) + slot < L;
-    const int phys = valid ? pt[page] : 0;
+  // attended items (pages) of a (sequence, KV head) pair
+  auto items_of = [&](int b, int g) {
+    if (!sel) return (seq_lens[b] + P - 1) >> log2P;
+    return sel_counts ? min(max(sel_counts[b * Hkv + g], 0), k_max) : k_max;
+  };
+  build_chunk_prefix(batch, s_base, [&](int b) {
+    int items = 0;
+    for (int g = 0; g < Hkv; ++g) items = max(items, items_of(b, g));
+    const int rows = (items + (1 << ipr_log2) - 1) >> ipr_log2;
+    return Hkv * max(1, (rows + rows_per_chunk - 1) / rows_per_chunk);
+  });
+  const int total = s_base[batch];
 
-    // ---- scores: one lane per token, query in scalar registers
-    float s[G];
-    {
-      uint4 kc[CKW];
-      if (valid) {
-        const uint8_t* kb = keys + (static_cast<size_t>(phys) * Hkv + g) * slab_k + slot * 16;
-#pragma unroll
-        for (int c = 0; c < CKW; ++c) kc[c] = load16(kb + static_cast<size_t>(c) * P * 16);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CKW; ++c) kc[c] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = 0.f;
-      static_for<0, CKW>([&](auto cc) {
-        constexpr int C = decltype(cc)::value;
-        float x[CH];
-        S::unpack(kc[C], x);
-        fma_heads<G, CH, KW, C * CH>(qg, x, s);
-      });
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = valid ? s[h] * scale_log2e : kNegInf;
-    }
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int b = find_sequence(s_base, batch, w);
+    const int L = seq_lens[b];
+    const int N = (L + P - 1) >> log2P;
+    const int nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
+    const int local = w - s_base[b];
+    const int g = local / nsplit;
+    const int split = local - g * nsplit;
+    const int n_items = items_of(b, g);
+    const int nrows = (n_items + (1 << ipr_log2) - 1) >> ipr_log2;
+    const int pair = b * Hkv + g;
+    const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
+    const int32_t* __restrict__ sl = sel ? sel + static_cast<size_t>(pair) * k_max : nullptr;
+    const float* __restrict__ qg = qsrc + static_cast<size_t>(b * Hq + g * G) * KW;
+    const int row0 = split * rows_per_chunk;
+    const int row1 = min(row0 + rows_per_chunk, nrows);
 
-    // ---- online softmax (base 2); running max is wave-uniform
-    bool any = false;
-    float p[G];
+    float m[G], lsum[G], z[G][CH];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mx = wave_max_u(s[h]);
-      const float mn = fmaxf(m[h], mx);
-      any = any || (mn != kNegInf);
-      const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
-      p[h] = (mn == kNegInf) ? 0.f : fast_exp2(s[h] - mn);
-      lsum[h] = lsum[h] * alpha + p[h];
+      m[h] = kNegInf;
+      lsum[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < CH; ++e) z[h][e] *= alpha;
-      m[h] = mn;
+      for (int e = 0; e < CH; ++e) z[h][e] = 0.f;
     }
-    if (!any) continue;  // wave-uniform: nothing valid so far
-#pragma unroll
-    for (int h = 0; h < G; ++h) s_p[wave][lane][h] = p[h];
-    wave_lds_sync();
 
-    // ---- P . V_latent: lane owns chunk my_c of tokens lane/CV + k*TPL
-    if (P == kWave) {
-      // the row is one page: its physical page and valid length are uniform
-      const int upage = __builtin_amdgcn_readfirstlane(page);
-      const bool prow = upage >= 0 && upage < N;
-      const int nvalid = prow ? min(L - upage * kWave, kWave) : 0;
-      const size_t uphys = prow ? static_cast<size_t>(pt[upage]) : 0;
-      const uint8_t* vb = v_lat + (uphys * Hkv + g) * slab_v + static_cast<size_t>(my_c) * P * 16;
-      uint4 vc[CV];
+    // online softmax update for one row's scores; returns false if nothing valid yet
+    auto softmax_row = [&](float (&s)[G], bool valid) -> bool {
+      bool any = false;
+      float p[G];
 #pragma unroll
-      for (int k = 0; k < CV; ++k) {
-        const int tok = lane / CV + k * TPL;
-        vc[k] = (tok < nvalid) ? load16(vb + tok * 16) : make_uint4(0, 0, 0, 0);
+      for (int h = 0; h < G; ++h) {
+        const float sv = valid ? s[h] * scale_log2e : kNegInf;
+        const float mx = wave_max_u(sv);
+        const float mn = fmaxf(m[h], mx);
+        any = any || (mn != kNegInf);
+        const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
+        p[h] = (mn == kNegInf) ? 0.f : fast_exp2(sv - mn);
+        lsum[h] = lsum[h] * alpha + p[h];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) z[h][e] *= alpha;
+        m[h] = mn;
       }
+      if (any) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_p[wave][lane][h] = p[h];
+        wave_lds_sync();
+      }
+      return any;
+    };
+    auto accumulate_pv = [&](const uint4 (&vc)[CV]) {
 #pragma unroll
       for (int k = 0; k < CV; ++k) {
         const int tok = lane / CV + k * TPL;
@@ -160,121 +141,222 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
           for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, x[e], z[h][e]);
         }
       }
-    } else {
+      wave_lds_sync();
+    };
+    auto score_keys = [&](const uint4 (&kc)[CKW], float (&s)[G]) {
 #pragma unroll
-      for (int k = 0; k < CV; ++k) {
-        const int tok = lane / CV + k * TPL;
-        const int tphys = __shfl(phys, tok, kWave);
-        const int tvalid = __shfl(static_cast<int>(valid), tok, kWave);
-        uint4 vc = make_uint4(0, 0, 0, 0);
-        if (tvalid) {
-          const int tslot = tok & (P - 1);
-          vc = load16(v_lat + (static_cast<size_t>(tphys) * Hkv + g) * slab_v +
-                      static_cast<size_t>(my_c) * P * 16 + tslot * 16);
-        }
+      for (int h = 0; h < G; ++h) s[h] = 0.f;
+      static_for<0, CKW>([&](auto cc) {
+        constexpr int C = decltype(cc)::value;
         float x[CH];
-        S::unpack(vc, x);
+        S::unpack(kc[C], x);
+        fma_heads<G, CH, KW, C * CH>(qg, x, s);
+      });
+    };
+
+    if constexpr (ROWPAGE) {
+      // one page per row: page id and physical page are wave-uniform
+      auto page_of = [&](int row) -> int {
+        const int pg = sl ? sl[row] : row;
+        return (pg >= 0 && pg < N) ? pg : -1;
+      };
+      // issue one row's key and value loads (masked past the valid tokens)
+      auto issue = [&](int pg, int ph, uint4 (&kc)[CKW], uint4 (&vc)[CV]) -> int {
+        const int nvalid = (pg >= 0) ? min(L - pg * kWave, kWave) : 0;
+        const uint8_t* kb = keys + (static_cast<size_t>(ph) * Hkv + g) * slab_k + lane * 16;
+        const uint8_t* vb = v_lat + (static_cast<size_t>(ph) * Hkv + g) * slab_v + my_c * kWave * 16;
+        const bool kvalid = lane < nvalid;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pp = s_p[wave][tok][h];
+        for (int c = 0; c < CKW; ++c)
+          kc[c] = kvalid ? load16_stream(kb + c * kWave * 16) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, x[e], z[h][e]);
+        for (int k = 0; k < CV; ++k) {
+          const int tok = lane / CV + k * TPL;
+          vc[k] = (tok < nvalid) ? load16_stream(vb + tok * 16) : make_uint4(0, 0, 0, 0);
         }
+        return nvalid;
+      };
+      auto consume = [&](int nvalid, const uint4 (&kc)[CKW], const uint4 (&vc)[CV]) {
+        if (nvalid > 0) {
+          float s[G];
+          score_keys(kc, s);
+          if (softmax_row(s, lane < nvalid)) accumulate_pv(vc);
+        }
+      };
+      int r = row0 + wave;
+      int pg = (r < row1) ? page_of(r) : -1;
+      int ph = (pg >= 0) ? pt[pg] : 0;
+#if KVLR_ATTN_PREFETCH
+      // two rows in flight: the next row's loads go out before this row is used
+      uint4 kA[CKW], vA[CV], kB[CKW], vB[CV];
+      int nA = (r < row1) ? issue(pg, ph, kA, vA) : 0;
+      while (r < row1) {
+        const int r2 = r + kWaves;
+        int nB = 0;
+        if (r2 < row1) {
+          const int pg2 = page_of(r2);
+          nB = issue(pg2, (pg2 >= 0) ? pt[pg2] : 0, kB, vB);
+        }
+        consume(nA, kA, vA);
+        if (r2 >= row1) break;
+        const int r3 = r2 + kWaves;
+        if (r3 < row1) {
+          const int pg3 = page_of(r3);
+          nA = issue(pg3, (pg3 >= 0) ? pt[pg3] : 0, kA, vA);
+        }
+        consume(nB, kB, vB);
+        r = r3;
+      }
+#else
+      for (; r < row1; r += kWaves) {
+        uint4 kc[CKW], vc[CV];
+        const int nvalid = issue(pg, ph, kc, vc);
+        // next row's page, fetched while this row's data is in flight
+        const int rn = r + kWaves;
+        const int pgn = (rn < row1) ? page_of(rn) : -1;
+        const int phn = (pgn >= 0) ? pt[pgn] : 0;
+        consume(nvalid, kc, vc);
+        pg = pgn;
+        ph = phn;
+      }
+#endif
+    } else {
+      for (int row = row0 + wave; row < row1; row += kWaves) {
+        const int item = (row << ipr_log2) + (lane >> log2P);
+        const int slot = lane & (P - 1);
+        int page = -1;
+        if (item < n_items) page = sl ? sl[item] : item;
+        const bool valid = page >= 0 && page < N && (page << log2P) + slot < L;
+        const int phys = valid ? pt[page] : 0;
+        uint4 kc[CKW];
+        if (valid) {
+          const uint8_t* kb = keys + (static_cast<size_t>(phys) * Hkv + g) * slab_k + slot * 16;
+#pragma unroll
+          for (int c = 0; c < CKW; ++c) kc[c] = load16_stream(kb + static_cast<size_t>(c) * P * 16);
+        } else {
+#pragma unroll
+          for (int c = 0; c < CKW; ++c) kc[c] = make_uint4(0, 0, 0, 0);
+        }
+        uint4 vc[CV];
+#pragma unroll
+        for (int k = 0; k < CV; ++k) {
+          const int tok = lane / CV + k * TPL;
+          const int tphys = __shfl(phys, tok, kWave);
+          const int tvalid = __shfl(static_cast<int>(valid), tok, kWave);
+          vc[k] = make_uint4(0, 0, 0, 0);
+          if (tvalid) {
+            const int tslot = tok & (P - 1);
+            vc[k] = load16_stream(v_lat + (static_cast<size_t>(tphys) * Hkv + g) * slab_v +
+                                  static_cast<size_t>(my_c) * P * 16 + tslot * 16);
+          }
+        }
+        float s[G];
+        score_keys(kc, s);
+        if (softmax_row(s, valid)) accumulate_pv(vc);
       }
     }
-    wave_lds_sync();
-  }
 
-  // ---- wave reduction: lanes with the same chunk hold disjoint token sets
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int off = CV; off < kWave; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < CH; ++e) z[h][e] += __shfl_xor(z[h][e], off, kWave);
-    lsum[h] = wave_sum_u(lsum[h]);
-  }
-  if (lane < CV) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < CH; ++e) s_z[wave][h][lane * CH + e] = z[h][e];
-  }
-  if (lane == 0) {
+    // ---- wave reduction: lanes with the same chunk hold disjoint token sets
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      s_ml[wave][h][0] = m[h];
-      s_ml[wave][h][1] = lsum[h];
+#pragma unroll
+      for (int off = CV; off < kWave; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < CH; ++e) z[h][e] += __shfl_xor(z[h][e], off, kWave);
+      lsum[h] = wave_sum_u(lsum[h]);
     }
-  }
-  __syncthreads();
-
-  // ---- workgroup partial (max, sum, z) per head
-  float* part = partials + (static_cast<size_t>(pair) * num_splits + blockIdx.x) * G * PW;
-  for (int i = threadIdx.x; i < G * RV; i += kThreads) {
-    const int h = i / RV, e = i - h * RV;
-    float M = kNegInf;
+    if (lane < CV) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
-    float Z = 0.f, Ls = 0.f;
-    if (M != kNegInf) {
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = fast_exp2(s_ml[w][h][0] - M);
-        Z += f * s_z[w][h][e];
-        Ls += f * s_ml[w][h][1];
+        for (int e = 0; e < CH; ++e) s_z[wave][h][lane * CH + e] = z[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_ml[wave][h][0] = m[h];
+        s_ml[wave][h][1] = lsum[h];
       }
     }
-    store_shared_f32(&part[h * PW + 2 + e], Z);
-    if (e == 0) {
-      store_shared_f32(&part[h * PW], M);
-      store_shared_f32(&part[h * PW + 1], Ls);
-    }
-  }
+    __syncthreads();
 
-  // ---- ticket: the last workgroup of the pair merges the splits
-  wait_stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = take_ticket(&counters[pair]);
-    s_last = (prev == static_cast<uint32_t>(num_splits - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  const float* allp = partials + static_cast<size_t>(pair) * num_splits * G * PW;
-  for (int i = threadIdx.x; i < G * RV; i += kThreads) {
-    const int h = i / RV, e = i - h * RV;
-    float M = kNegInf;
-    for (int sp = 0; sp < num_splits; ++sp) M = fmaxf(M, load_shared_f32(&allp[(sp * G + h) * PW]));
-    float Z = 0.f, Ls = 0.f;
-    if (M != kNegInf) {
-      for (int sp = 0; sp < num_splits; ++sp) {
-        const float* r = allp + (sp * G + h) * PW;
-        const float f = fast_exp2(load_shared_f32(&r[0]) - M);
-        Z += f * load_shared_f32(&r[2 + e]);
-        Ls += f * load_shared_f32(&r[1]);
+    // ---- chunk partial (max, sum, z) per head
+    float* part = partials + (static_cast<size_t>(pair) * max_splits + split) * G * PW;
+    for (int i = threadIdx.x; i < G * RV; i += kThreads) {
+      const int h = i / RV, e = i - h * RV;
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_ml[ww][h][0]);
+      float Z = 0.f, Ls = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float f = fast_exp2(s_ml[ww][h][0] - M);
+          Z += f * s_z[ww][h][e];
+          Ls += f * s_ml[ww][h][1];
+        }
+      }
+      store_shared_f32(&part[h * PW + 2 + e], Z);
+      if (e == 0) {
+        store_shared_f32(&part[h * PW], M);
+        store_shared_f32(&part[h * PW + 1], Ls);
       }
     }
-    const int qh = g * G + h;
-    z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = (Ls > 0.f) ? Z / Ls : 0.f;
-    if (e == 0 && lse_out) {
-      lse_out[static_cast<size_t>(b) * Hq + qh] =
-          (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
+
+    // ---- ticket: the last chunk of the pair merges the splits
+    wait_stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = take_ticket(&counters[pair]);
+      s_last = (prev == static_cast<uint32_t>(nsplit - 1));
     }
+    __syncthreads();
+    if (s_last) {
+      const float* allp = partials + static_cast<size_t>(pair) * max_splits * G * PW;
+      for (int i = threadIdx.x; i < G * RV; i += kThreads) {
+        const int h = i / RV, e = i - h * RV;
+        float M = kNegInf;
+        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, load_shared_f32(&allp[(sp * G + h) * PW]));
+        float Z = 0.f, Ls = 0.f;
+        if (M != kNegInf) {
+          for (int sp = 0; sp < nsplit; ++sp) {
+            const float* r = allp + (sp * G + h) * PW;
+            const float f = fast_exp2(load_shared_f32(&r[0]) - M);
+            Z += f * load_shared_f32(&r[2 + e]);
+            Ls += f * load_shared_f32(&r[1]);
+          }
+        }
+        const int qh = g * G + h;
+        z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = (Ls > 0.f) ? Z / Ls : 0.f;
+        if (e == 0 && lse_out) {
+          lse_out[static_cast<size_t>(b) * Hq + qh] =
+              (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
+        }
+      }
+      if (threadIdx.x == 0) reset_ticket(&counters[pair]);
+    }
+    __syncthreads();
   }
-  if (threadIdx.x == 0) reset_ticket(&counters[pair]);
 }
 
 template <class S, int G, int KW, int RV>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   if (a.q_stride != KW) return hipErrorInvalidValue;  // queries are read with stride KW
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
-  dim3 grid(a.num_splits, a.batch * a.dm.Hkv);
-  hipLaunchKernelGGL((attn_kernel<S, G, KW, RV>), grid, dim3(kThreads), 0, s,
-                     static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
-                     a.qsrc, a.q_stride, a.seq_lens, a.page_table, a.sel, a.partials, a.counters,
-                     a.z_out, a.lse_out, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
-                     a.scale_log2e, a.rows_per_split, a.num_splits);
+  const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
+  dim3 grid(a.grid);
+  if (a.dm.P == kWave)
+    hipLaunchKernelGGL((attn_kernel<S, G, KW, RV, true>), grid, dim3(kThreads), lds, s,
+                       static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
+                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials, a.counters, a.z_out,
+                       a.lse_out, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                       a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
+  else
+    hipLaunchKernelGGL((attn_kernel<S, G, KW, RV, false>), grid, dim3(kThreads), lds, s,
+                       static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
+                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials, a.counters, a.z_out,
+                       a.lse_out, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                       a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
   return hipGetLastError();
 }
 
@@ -313,19 +395,7 @@ hipError_t by_g(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int attn_max_splits(int pairs) {
-  const int target_wgs = 1024;
-  return max(1, (target_wgs + pairs - 1) / pairs);
-}
-
-SplitPlan attn_split_plan(int max_rows, int pairs) {
-  const int groups = max(1, (max_rows + kWaves - 1) / kWaves);
-  const int splits = min(groups, attn_max_splits(pairs));
-  SplitPlan p;
-  p.rows_per_split = kWaves * ((groups + splits - 1) / splits);
-  p.num_splits = max(1, (max_rows + p.rows_per_split - 1) / p.rows_per_split);
-  return p;
-}
+int attn_rows_per_chunk(bool selected) { return selected ? 8 : 32; }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;

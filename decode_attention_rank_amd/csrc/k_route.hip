@@ -21,6 +21,11 @@
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
 
+#ifndef KVLR_ROUTE_ROLLING
+#define KVLR_ROUTE_ROLLING 1
+#endif
+
+
 namespace kvlr {
 namespace {
 
@@ -123,113 +128,233 @@ __device__ void select_pages(float* scores, int N, int k, int k_max, int max_pag
   for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
 }
 
-template <class S, int G, int RV, int RK>
+// Scores of one 64-token row: acc[h] = q_hat_h . v + q_tilde_h . c per lane,
+// the group's projected queries broadcast from VGPRs (NQ = G*W/16).
+template <class S, int G, int RV, int RK, int NQ>
+__device__ inline float row_score(const float (&qv)[NQ], const uint4 (&vc)[RV / S::CH],
+                                  const uint4 (&kc)[RK / S::CH]) {
+  constexpr int CH = S::CH, CV = RV / CH, CK = RK / CH, W = RV + RK;
+  float acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.f;
+  static_for<0, CV>([&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    float x[CH];
+    S::unpack(vc[C], x);
+    fma_heads_bcast<G, CH, W, C * CH>(qv, x, acc);
+  });
+  static_for<0, CK>([&](auto cc) {
+    constexpr int C = decltype(cc)::value;
+    float x[CH];
+    S::unpack(kc[C], x);
+    fma_heads_bcast<G, CH, W, RV + C * CH>(qv, x, acc);
+  });
+  float m = acc[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) m = fmaxf(m, acc[h]);
+  return m;
+}
+
+// ROWPAGE: page_size == 64, so a row is exactly one page; its page-table
+// entry and base address are wave-uniform, and the next row's loads are
+// issued before the current row is scored.
+template <class S, int G, int RV, int RK, bool ROWPAGE>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const uint8_t* __restrict__ v_lat, const uint8_t* __restrict__ k_lat,
     const float* __restrict__ q_proj, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, float* __restrict__ scores,
-    uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int Hq, int Hkv, int P,
-    int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_split,
-    int num_splits) {
+    uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int32_t* __restrict__ sel_counts,
+    int Hq, int Hkv, int P,
+    int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_chunk,
+    int batch) {
   constexpr int CH = S::CH;
   constexpr int CV = RV / CH;
   constexpr int CK = RK / CH;
   constexpr int W = RV + RK;
-  const int pair = blockIdx.y;
-  const int b = pair / Hkv;
-  const int g = pair - b * Hkv;
-  const int L = seq_lens[b];
-  const int nrows = (L + kWave - 1) / kWave;
+  constexpr int NQ = G * W / 16;
+  extern __shared__ int s_base[];
+  __shared__ int s_last;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
-  const float* __restrict__ qp = q_proj + static_cast<size_t>(b * Hq + g * G) * W;
-  const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
-  float* __restrict__ sc = scores + static_cast<size_t>(pair) * max_pages;
   const size_t slab_v = static_cast<size_t>(CV) * P * 16;  // bytes of one head's page
   const size_t slab_k = static_cast<size_t>(CK) * P * 16;
 
-  const int row0 = blockIdx.x * rows_per_split;
-  const int row1 = min(row0 + rows_per_split, nrows);
-  for (int row = row0 + wave; row < row1; row += kWaves) {
-    const int t = row * kWave + lane;
-    const bool valid = t < L;
-    const int j = t >> log2P;
-    const int slot = t & (P - 1);
-    uint4 vc[CV], kc[CK];
-    if (valid) {
-      const size_t phys = static_cast<size_t>(pt[j]);
-      const uint8_t* vb = v_lat + (phys * Hkv + g) * slab_v + slot * 16;
-      const uint8_t* kb = k_lat + (phys * Hkv + g) * slab_k + slot * 16;
-#pragma unroll
-      for (int c = 0; c < CV; ++c) vc[c] = load16_stream(vb + static_cast<size_t>(c) * P * 16);
-#pragma unroll
-      for (int c = 0; c < CK; ++c) kc[c] = load16_stream(kb + static_cast<size_t>(c) * P * 16);
-    } else {
-#pragma unroll
-      for (int c = 0; c < CV; ++c) vc[c] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < CK; ++c) kc[c] = make_uint4(0, 0, 0, 0);
-    }
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    // value-latent part: q_hat . v
-    static_for<0, CV>([&](auto cc) {
-      constexpr int C = decltype(cc)::value;
-      float x[CH];
-      S::unpack(vc[C], x);
-      fma_heads<G, CH, W, C * CH>(qp, x, acc);
-    });
-    // residual part: q_tilde . c
-    static_for<0, CK>([&](auto cc) {
-      constexpr int C = decltype(cc)::value;
-      float x[CH];
-      S::unpack(kc[C], x);
-      fma_heads<G, CH, W, RV + C * CH>(qp, x, acc);
-    });
-    float m = acc[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) m = fmaxf(m, acc[h]);
-    if (!valid) m = -__builtin_huge_valf();
-    if (P == kWave) {
-      m = wave_max_u(m);
-    } else {
-      m = row16_max(m);
-      if (P == 32) m = fmaxf(m, __shfl_xor(m, 16, kWave));
-    }
-    if (slot == 0 && valid) store_shared_f32(&sc[j], m);
-  }
+  build_chunk_prefix(batch, s_base, [&](int b) {
+    const int rows = (seq_lens[b] + kWave - 1) / kWave;
+    return Hkv * max(1, (rows + rows_per_chunk - 1) / rows_per_chunk);
+  });
+  const int total = s_base[batch];
 
-  // Ticket: the last workgroup of this pair selects its pages.
-  __shared__ int s_last;
-  wait_stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = take_ticket(&counters[pair]);
-    s_last = (prev == static_cast<uint32_t>(num_splits - 1));
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int b = find_sequence(s_base, batch, w);
+    const int L = seq_lens[b];
+    const int nrows = (L + kWave - 1) / kWave;
+    const int nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
+    const int local = w - s_base[b];
+    const int g = local / nsplit;
+    const int split = local - g * nsplit;
+    const int pair = b * Hkv + g;
+    const float* __restrict__ qp = q_proj + static_cast<size_t>(b * Hq + g * G) * W;
+    const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
+    float* __restrict__ sc = scores + static_cast<size_t>(pair) * max_pages;
+    float qv[NQ];
+    load_q_rows(qp, qv);
+    const int row0 = split * rows_per_chunk;
+    const int row1 = min(row0 + rows_per_chunk, nrows);
+
+    if constexpr (ROWPAGE) {
+      // one page per row: its page-table entry and base address are uniform
+      auto row_base = [&](int row, const uint8_t*& vbase, const uint8_t*& kbase) -> bool {
+        const size_t phys = static_cast<size_t>(pt[row]);
+        vbase = v_lat + (phys * Hkv + g) * slab_v + lane * 16;
+        kbase = k_lat + (phys * Hkv + g) * slab_k + lane * 16;
+        return lane < L - row * kWave;
+      };
+      auto finish_row = [&](int row, float (&acc)[G]) {
+        float m = acc[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) m = fmaxf(m, acc[h]);
+        if (lane >= L - row * kWave) m = -__builtin_huge_valf();
+        m = wave_max_u(m);
+        if (lane == 0) store_shared_f32(&sc[row], m);
+      };
+#if KVLR_ROUTE_ROLLING
+      // Rolling prefetch: as soon as a 16-byte chunk of this row has been
+      // consumed, the same chunk of the wave's next row is requested into the
+      // freed registers, so about one row per wave stays in flight at no
+      // extra register cost.
+      int r = row0 + wave;
+      uint4 vc[CV], kc[CK];
+      if (r < row1) {
+        const uint8_t *vb, *kb;
+        const bool ok = row_base(r, vb, kb);
+#pragma unroll
+        for (int c = 0; c < CV; ++c) vc[c] = ok ? load16_stream(vb + c * kWave * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CK; ++c) kc[c] = ok ? load16_stream(kb + c * kWave * 16) : make_uint4(0, 0, 0, 0);
+      }
+      for (; r < row1; r += kWaves) {
+        const int rn = r + kWaves;
+        const uint8_t *vbn = v_lat, *kbn = k_lat;
+        const bool okn = (rn < row1) ? row_base(rn, vbn, kbn) : false;
+        float acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0.f;
+        static_for<0, CV>([&](auto cc) {
+          constexpr int C = decltype(cc)::value;
+          float x[CH];
+          S::unpack(vc[C], x);
+          fma_heads_bcast<G, CH, W, C * CH>(qv, x, acc);
+          vc[C] = okn ? load16_stream(vbn + C * kWave * 16) : make_uint4(0, 0, 0, 0);
+        });
+        static_for<0, CK>([&](auto cc) {
+          constexpr int C = decltype(cc)::value;
+          float x[CH];
+          S::unpack(kc[C], x);
+          fma_heads_bcast<G, CH, W, RV + C * CH>(qv, x, acc);
+          kc[C] = okn ? load16_stream(kbn + C * kWave * 16) : make_uint4(0, 0, 0, 0);
+        });
+        finish_row(r, acc);
+      }
+#else
+      for (int r = row0 + wave; r < row1; r += kWaves) {
+        uint4 vc[CV], kc[CK];
+        const uint8_t *vb, *kb;
+        const bool ok = row_base(r, vb, kb);
+#pragma unroll
+        for (int c = 0; c < CV; ++c) vc[c] = ok ? load16_stream(vb + c * kWave * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CK; ++c) kc[c] = ok ? load16_stream(kb + c * kWave * 16) : make_uint4(0, 0, 0, 0);
+        float acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0.f;
+        static_for<0, CV>([&](auto cc) {
+          constexpr int C = decltype(cc)::value;
+          float x[CH];
+          S::unpack(vc[C], x);
+          fma_heads_bcast<G, CH, W, C * CH>(qv, x, acc);
+        });
+        static_for<0, CK>([&](auto cc) {
+          constexpr int C = decltype(cc)::value;
+          float x[CH];
+          S::unpack(kc[C], x);
+          fma_heads_bcast<G, CH, W, RV + C * CH>(qv, x, acc);
+        });
+        finish_row(r, acc);
+      }
+#endif
+    } else {
+      for (int row = row0 + wave; row < row1; row += kWaves) {
+        const int t = row * kWave + lane;
+        const bool valid = t < L;
+        const int j = t >> log2P;
+        const int slot = t & (P - 1);
+        uint4 vc[CV], kc[CK];
+        if (valid) {
+          const size_t phys = static_cast<size_t>(pt[j]);
+          const uint8_t* vbase = v_lat + (phys * Hkv + g) * slab_v + slot * 16;
+          const uint8_t* kbase = k_lat + (phys * Hkv + g) * slab_k + slot * 16;
+#pragma unroll
+          for (int c = 0; c < CV; ++c) vc[c] = load16_stream(vbase + static_cast<size_t>(c) * P * 16);
+#pragma unroll
+          for (int c = 0; c < CK; ++c) kc[c] = load16_stream(kbase + static_cast<size_t>(c) * P * 16);
+        } else {
+#pragma unroll
+          for (int c = 0; c < CV; ++c) vc[c] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < CK; ++c) kc[c] = make_uint4(0, 0, 0, 0);
+        }
+        float m = row_score<S, G, RV, RK>(qv, vc, kc);
+        if (!valid) m = -__builtin_huge_valf();
+        m = row16_max(m);
+        if (P == 32) m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        if (slot == 0 && valid) store_shared_f32(&sc[j], m);
+      }
+    }
+
+    // Ticket: the last chunk of this pair selects its pages.
+    wait_stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = take_ticket(&counters[pair]);
+      s_last = (prev == static_cast<uint32_t>(nsplit - 1));
+    }
+    __syncthreads();
+    if (s_last) {
+      const int N = (L + P - 1) >> log2P;
+      int k = 0;
+      if (N > 0) {
+        const long long want = (static_cast<long long>(N) * topk_num + topk_den - 1) / topk_den;
+        k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
+        k = min(k, k_max);
+      }
+      select_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
+      if (threadIdx.x == 0) {
+        if (sel_counts) sel_counts[pair] = k;
+        reset_ticket(&counters[pair]);
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (!s_last) return;
-  const int N = (L + P - 1) >> log2P;
-  int k = 0;
-  if (N > 0) {
-    const long long want = (static_cast<long long>(N) * topk_num + topk_den - 1) / topk_den;
-    k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
-    k = min(k, k_max);
-  }
-  select_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
-  if (threadIdx.x == 0) reset_ticket(&counters[pair]);
 }
 
 template <class S, int G, int RV, int RK>
 hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
-  dim3 grid(a.num_splits, a.batch * a.dm.Hkv);
-  hipLaunchKernelGGL((route_kernel<S, G, RV, RK>), grid, dim3(kThreads), 0, s,
-                     static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
-                     a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.dm.Hq,
-                     a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
-                     a.rows_per_split, a.num_splits);
+  const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
+  dim3 grid(a.grid);
+  if (a.dm.P == kWave)
+    hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true>), grid, dim3(kThreads), lds, s,
+                       static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
+                       a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts, a.dm.Hq,
+                       a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
+                       a.rows_per_chunk, a.batch);
+  else
+    hipLaunchKernelGGL((route_kernel<S, G, RV, RK, false>), grid, dim3(kThreads), lds, s,
+                       static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
+                       a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts, a.dm.Hq,
+                       a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
+                       a.rows_per_chunk, a.batch);
   return hipGetLastError();
 }
 
@@ -266,17 +391,10 @@ hipError_t by_g(const RouteArgs& a, hipStream_t s) {
 
 }  // namespace
 
-SplitPlan route_split_plan(int max_rows, int pairs) {
-  // About 8 workgroups per CU over the whole grid, at least one row per wave.
-  const int target_wgs = 2048;
-  const int target = max(1, (target_wgs + pairs - 1) / pairs);
-  const int groups = max(1, (max_rows + kWaves - 1) / kWaves);
-  const int splits = min(groups, target);
-  SplitPlan p;
-  p.rows_per_split = kWaves * ((groups + splits - 1) / splits);
-  p.num_splits = max(1, (max_rows + p.rows_per_split - 1) / p.rows_per_split);
-  return p;
-}
+#ifndef KVLR_ROUTE_RPC
+#define KVLR_ROUTE_RPC 64
+#endif
+int route_rows_per_chunk() { return KVLR_ROUTE_RPC; }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;

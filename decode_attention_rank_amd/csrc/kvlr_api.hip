@@ -53,6 +53,12 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxBatch = 4096;          // per-sequence work lists live in LDS
+#ifndef KVLR_ROUTE_GRID
+#define KVLR_ROUTE_GRID 2048
+#endif
+constexpr long long kPersistentGrid = KVLR_ROUTE_GRID;  // about 8 workgroups per CU
+constexpr long long kAttnGrid = 1024;        // attention holds more registers per wave
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
@@ -64,6 +70,10 @@ struct Plan {
 };
 
 int attn_rows(int n_items, int P) { return ceil_div(n_items, 64 / P); }
+int max_chunks(int rows, int rows_per_chunk) {
+  const int c = ceil_div(rows, rows_per_chunk);
+  return c > 1 ? c : 1;
+}
 
 Plan plan_for(const Dims& dm, int batch, int max_pages) {
   Plan p{};
@@ -75,7 +85,8 @@ Plan plan_for(const Dims& dm, int batch, int max_pages) {
     p.route_scores = off;
     off += round_up(pairs * static_cast<size_t>(max_pages) * sizeof(float));
   }
-  p.attn_max_splits = kvlr::attn_max_splits(static_cast<int>(pairs));
+  // partial slots per pair: enough for the smallest chunk size over every page
+  p.attn_max_splits = max_chunks(attn_rows(max_pages, dm.P), kvlr::attn_rows_per_chunk(true));
   p.attn_cnt = off;
   off += round_up(pairs * sizeof(uint32_t));
   p.attn_part = off;
@@ -180,13 +191,15 @@ kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* fa
 kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
                              const int32_t* seq_lens, const int32_t* page_table,
                              int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
-                             int32_t k_max, int32_t* sel_pages, float* page_scores,
-                             void* workspace, size_t ws_bytes, int32_t batch, void* stream) {
+                             int32_t k_max, int32_t* sel_pages, int32_t* sel_counts,
+                             float* page_scores, void* workspace, size_t ws_bytes,
+                             int32_t batch, void* stream) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
   if (!dm.exact) return KVLR_ERR_UNSUPPORTED;
   if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
   if (topk_num < 0 || topk_den < 1) return KVLR_ERR_INVALID_ARGUMENT;
   const long long bound = (static_cast<long long>(max_pages_per_seq) * topk_num + topk_den - 1) / topk_den;
@@ -197,6 +210,7 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
       !ok_ptr(page_table) || !ok_ptr(sel_pages) || !ok_ptr(workspace))
     return KVLR_ERR_INVALID_ARGUMENT;
   if (page_scores && !aligned16(page_scores)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_counts && !aligned16(sel_counts)) return KVLR_ERR_INVALID_ARGUMENT;
   const Plan plan = plan_for(dm, batch, max_pages_per_seq);
   if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -212,26 +226,29 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.topk_den = topk_den;
   a.k_max = k_max;
   a.sel = sel_pages;
+  a.sel_counts = sel_counts;
   a.scores = page_scores ? page_scores : reinterpret_cast<float*>(ws + plan.route_scores);
   a.counters = reinterpret_cast<uint32_t*>(ws + plan.route_cnt);
   a.batch = batch;
   const int max_rows = ceil_div(static_cast<long long>(max_pages_per_seq) * dm.P, 64);
-  const kvlr::SplitPlan sp = kvlr::route_split_plan(max_rows, batch * dm.Hkv);
-  a.rows_per_split = sp.rows_per_split;
-  a.num_splits = sp.num_splits;
+  a.rows_per_chunk = kvlr::route_rows_per_chunk();
+  const long long chunks = static_cast<long long>(batch) * dm.Hkv *
+                           (max_rows > 0 ? ceil_div(max_rows, a.rows_per_chunk) : 1);
+  a.grid = static_cast<int>(chunks < kPersistentGrid ? chunks : kPersistentGrid);
   return hip_status(kvlr::launch_route(a, as_stream(stream)));
 }
 
 kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
                              const float* q_proj, const int32_t* seq_lens,
                              const int32_t* page_table, int32_t max_pages_per_seq,
-                             const int32_t* sel_pages, int32_t k_max, float softmax_scale,
-                             float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
+                             const int32_t* sel_pages, const int32_t* sel_counts, int32_t k_max,
+                             float softmax_scale, float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
                              int32_t batch, void* stream) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
   if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_pages && (k_max < 1 || k_max > max_pages_per_seq)) return KVLR_ERR_INVALID_ARGUMENT;
@@ -240,6 +257,7 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
       !ok_ptr(workspace))
     return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_pages && !aligned16(sel_pages)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_counts && (!sel_pages || !aligned16(sel_counts))) return KVLR_ERR_INVALID_ARGUMENT;
   if (lse_out && !aligned16(lse_out)) return KVLR_ERR_INVALID_ARGUMENT;
   if (dm.exact && (!ok_ptr(cache->k_exact) || !ok_ptr(q))) return KVLR_ERR_INVALID_ARGUMENT;
   if (!dm.exact && (!ok_ptr(cache->k_lat) || !ok_ptr(q_proj))) return KVLR_ERR_INVALID_ARGUMENT;
@@ -256,6 +274,7 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.page_table = page_table;
   a.max_pages = max_pages_per_seq;
   a.sel = sel_pages;
+  a.sel_counts = sel_counts;
   a.k_max = sel_pages ? k_max : 0;
   a.scale_log2e = softmax_scale * 1.4426950408889634f;
   a.partials = reinterpret_cast<float*>(ws + plan.attn_part);
@@ -264,10 +283,11 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.lse_out = lse_out;
   a.batch = batch;
   const int rows = attn_rows(sel_pages ? k_max : max_pages_per_seq, dm.P);
-  const kvlr::SplitPlan sp = kvlr::attn_split_plan(rows, batch * dm.Hkv);
-  a.rows_per_split = sp.rows_per_split;
-  a.num_splits = sp.num_splits;
-  if (a.num_splits > plan.attn_max_splits) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  a.rows_per_chunk = kvlr::attn_rows_per_chunk(sel_pages != nullptr);
+  a.max_splits = max_chunks(rows, a.rows_per_chunk);
+  if (a.max_splits > plan.attn_max_splits) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  const long long chunks = static_cast<long long>(batch) * dm.Hkv * a.max_splits;
+  a.grid = static_cast<int>(chunks < kAttnGrid ? chunks : kAttnGrid);
   return hip_status(kvlr::launch_attn(a, as_stream(stream)));
 }
 

@@ -209,6 +209,43 @@ __device__ inline void fma_heads(const float* qp, const float (&x)[CH], float (&
 }
 
 // ---------------------------------------------------------------------------
+// Wave-uniform operands broadcast from VGPRs.
+//
+// A group's projected queries (G x W floats) are spread over NQ = G*W/16
+// VGPRs: lane l of register k holds q_flat[16k + (l & 15)], the same 16
+// values in each 16-lane row. v_fmac_f32 with the DPP row_newbcast:n
+// modifier reads lane n of its row for src0, so one VALU instruction does
+// acc += q_flat[16k + n] * x for every lane with no scalar loads at all.
+// The query registers are written only by global loads (never by a VALU
+// just before), so the DPP source needs no extra wait states.
+template <int N>
+__device__ inline void fmac_bcast(float& acc, float q, float x) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc)
+               : "v"(q), "v"(x), "n"(N));
+}
+
+template <int NQ>
+__device__ inline void load_q_rows(const float* qflat, float (&qv)[NQ]) {
+  const int l16 = threadIdx.x & 15;
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) qv[k] = qflat[16 * k + l16];
+}
+
+// acc[h] += q_flat[h*STRIDE + OFF + e] * x[e] for e < CH, h < G.
+template <int G, int CH, int STRIDE, int OFF, int NQ>
+__device__ inline void fma_heads_bcast(const float (&qv)[NQ], const float (&x)[CH],
+                                       float (&acc)[G]) {
+  static_for<0, G>([&](auto hh) {
+    constexpr int H = decltype(hh)::value;
+    static_for<0, CH>([&](auto ee) {
+      constexpr int F = H * STRIDE + OFF + decltype(ee)::value;
+      fmac_bcast<F % 16>(acc[H], qv[F / 16], x[decltype(ee)::value]);
+    });
+  });
+}
+
+// ---------------------------------------------------------------------------
 // DPP reductions (no LDS traffic). Steps within a 16-lane row use quad_perm
 // and mirrors; rows are combined with row_bcast, which leaves the full
 // result in lane 63.
@@ -276,6 +313,43 @@ __device__ inline float group_max(float v, int width) {
 __device__ inline uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent work lists. A kernel's work is a list of chunks, sequence by
+// sequence; chunk counts depend on device-side lengths, so each workgroup
+// builds the exclusive prefix s_base[0..batch] of per-sequence chunk counts
+// in LDS (wave 0, 64 sequences per step) and then walks the list with a
+// grid stride. count(b) must be >= 1.
+template <class CountFn>
+__device__ inline void build_chunk_prefix(int batch, int* s_base, CountFn count) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int b0 = 0; b0 < batch; b0 += kWave) {
+      const int b = b0 + lane;
+      int c = (b < batch) ? count(b) : 0;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(c, off, kWave);
+        if (lane >= off) c += t;
+      }
+      if (b < batch) s_base[b + 1] = carry + c;
+      carry += __shfl(c, kWave - 1, kWave);
+    }
+    if (lane == 0) s_base[0] = 0;
+  }
+  __syncthreads();
+}
+
+// Largest b with s_base[b] <= w (s_base strictly increasing, s_base[0] = 0).
+__device__ inline int find_sequence(const int* s_base, int batch, int w) {
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_base[mid] <= w) lo = mid; else hi = mid;
+  }
+  return lo;
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

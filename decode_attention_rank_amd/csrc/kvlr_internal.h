@@ -34,13 +34,15 @@ struct RouteArgs {
   int max_pages;
   int topk_num, topk_den, k_max;
   int32_t* sel;
+  int32_t* sel_counts;  // optional [B][Hkv]
   float* scores;        // [B][Hkv][max_pages]
   uint32_t* counters;   // [B * Hkv], zero between calls
   int batch;
-  int rows_per_split;   // 64-token rows per workgroup
-  int num_splits;
+  int rows_per_chunk;   // 64-token rows per work chunk
+  int grid;             // persistent workgroups
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+int route_rows_per_chunk();
 
 struct AttnArgs {
   Dims dm;
@@ -52,6 +54,7 @@ struct AttnArgs {
   const int32_t* page_table;
   int max_pages;
   const int32_t* sel;    // NULL = every page
+  const int32_t* sel_counts;  // optional valid entries per (sequence, KV head)
   int k_max;
   float scale_log2e;
   float* partials;       // [B*Hkv][num_splits][G][RV + 2]
@@ -59,10 +62,12 @@ struct AttnArgs {
   float* z_out;
   float* lse_out;        // may be NULL
   int batch;
-  int rows_per_split;
-  int num_splits;
+  int rows_per_chunk;    // 64-token rows per work chunk
+  int max_splits;        // chunk slots per pair in the partials buffer
+  int grid;              // persistent workgroups
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+int attn_rows_per_chunk(bool selected);
 
 struct UpprojArgs {
   Dims dm;
@@ -93,17 +98,5 @@ struct EncodeArgs {
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
-
-// Launch geometry shared by the workspace sizing and the launches. A pair's
-// rows are cut into at most max_splits(pairs) workgroups of rows_per_split
-// rows (a multiple of the 4 waves); the split count never exceeds the bound,
-// so a workspace sized by the bound fits every call.
-struct SplitPlan {
-  int rows_per_split;
-  int num_splits;
-};
-SplitPlan route_split_plan(int max_rows, int pairs);
-SplitPlan attn_split_plan(int max_rows, int pairs);
-int attn_max_splits(int pairs);
 
 }  // namespace kvlr

@@ -87,6 +87,8 @@ class DecodeSession:
         self.q_proj = torch.empty(B, Hq, self.qp_width, dtype=torch.float32, device=dev)
         self.sel = (torch.empty(B, H, self.k_max, dtype=torch.int32, device=dev)
                     if wl.routed else None)
+        self.sel_counts = (torch.empty(B, H, dtype=torch.int32, device=dev)
+                           if wl.routed else None)
         self.page_scores = (torch.empty(B, H, self.max_pages, dtype=torch.float32, device=dev)
                             if wl.routed else None)
         self.z = torch.empty(B, Hq, wl.rank_v, dtype=torch.float32, device=dev)
@@ -153,12 +155,14 @@ class DecodeSession:
     def route(self, stream=None):
         K.kvlr_route_pages(self.shape, self.kcache, self.q_proj, self.seq_lens_dev, self.page_table,
                            self.max_pages, self.wl.topk_num, self.wl.topk_den, self.k_max, self.sel,
-                           self.page_scores, self.workspace, self.ws_bytes, self.wl.batch, stream)
+                           self.sel_counts, self.page_scores, self.workspace, self.ws_bytes,
+                           self.wl.batch, stream)
 
-    def attend(self, stream=None, sel=True):
+    def attend(self, stream=None, sel=True, counts=True):
         use_sel = self.sel if (self.wl.routed and sel) else None
+        use_counts = self.sel_counts if (use_sel is not None and counts) else None
         K.kvlr_decode_attn(self.shape, self.kcache, self.q, self.q_proj, self.seq_lens_dev,
-                           self.page_table, self.max_pages, use_sel,
+                           self.page_table, self.max_pages, use_sel, use_counts,
                            self.k_max if use_sel is not None else 0, self.scale, self.z, self.lse,
                            self.workspace, self.ws_bytes, self.wl.batch, stream)
 

@@ -53,8 +53,9 @@
  *
  * Query-head h belongs to KV head h / G, G = num_q_heads / num_kv_heads.
  * Supported: head_dim in {64, 128}; rank_v, rank_k in {16, 32, 64} and
- * <= head_dim (rank 128 also for f32 at head_dim 128); page_size in
- * {16, 32, 64}; G in {1, 2, 4, 8}; max_pages_per_seq <= 65536.
+ * <= head_dim; page_size in
+ * {16, 32, 64}; G in {1, 2, 4, 8}; max_pages_per_seq <= 65536; batch <= 4096
+ * for routing and attention.
  * Other values return KVLR_ERR_UNSUPPORTED.
  */
 #ifndef KVLR_H
@@ -165,6 +166,8 @@ int32_t kvlr_qproj_width(const kvlr_shape* shape);
  *   k_max        host; must be >= min(max_pages_per_seq,
  *                ceil(max_pages_per_seq * topk_num / topk_den))
  *   sel_pages    out [batch][H_kv][k_max] logical page ids
+ *   sel_counts   optional out [batch][H_kv]: k_b, the number of valid
+ *                entries at the front of each sel_pages row
  *   page_scores  optional out [batch][H_kv][max_pages_per_seq] float32
  *                (S, then -inf past N); NULL keeps them in the workspace
  *   workspace    >= kvlr_workspace_bytes(...) bytes, zero-filled once
@@ -176,8 +179,9 @@ int32_t kvlr_qproj_width(const kvlr_shape* shape);
 kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
                              const int32_t* seq_lens, const int32_t* page_table,
                              int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
-                             int32_t k_max, int32_t* sel_pages, float* page_scores,
-                             void* workspace, size_t ws_bytes, int32_t batch, void* stream);
+                             int32_t k_max, int32_t* sel_pages, int32_t* sel_counts,
+                             float* page_scores, void* workspace, size_t ws_bytes,
+                             int32_t batch, void* stream);
 
 /*
  * Decode attention over the compressed cache. BasisKV English abstract:
@@ -189,9 +193,10 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
  *   EXACT:  s_t = scale * q_h . K_t (original keys)
  *   LATENT: s_t = scale * q_tilde_h . k_t (key latents)
  *   p = softmax(s);  z_out[b][h] = sum_t p_t v_t;  lse_out = log sum exp s
- * Attended pages: sel_pages[b][g][0 .. k_max) with -1 entries skipped, or
- * every page 0 .. N-1 when sel_pages is NULL. An empty set gives z = 0 and
- * lse = -inf.
+ * Attended pages: sel_pages[b][g][0 .. n) with -1 entries skipped, where
+ * n = sel_counts[b][g] when sel_counts is given (entries past it are not
+ * read) and n = k_max otherwise; or every page 0 .. N-1 when sel_pages is
+ * NULL. An empty set gives z = 0 and lse = -inf.
  *   q        [batch][num_q_heads][head_dim] float32 (EXACT; may be NULL in LATENT)
  *   q_proj   from kvlr_project_queries (LATENT; may be NULL in EXACT)
  *   z_out    out [batch][num_q_heads][rank_v] float32
@@ -201,7 +206,8 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
 kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
                              const float* q_proj, const int32_t* seq_lens,
                              const int32_t* page_table, int32_t max_pages_per_seq,
-                             const int32_t* sel_pages, int32_t k_max, float softmax_scale,
+                             const int32_t* sel_pages, const int32_t* sel_counts, int32_t k_max,
+                             float softmax_scale,
                              float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
                              int32_t batch, void* stream);
 

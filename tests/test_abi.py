@@ -89,9 +89,9 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     E = K.KVLR_ERR_INVALID_ARGUMENT
     # null pointers
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c), None, None, None, 512, 1, 8, 64,
-                                None, None, None, 0, 16, None) == E
+                                None, None, None, None, 0, 16, None) == E
     assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c), None, None, None, None, 512, None,
-                                0, 0.1, None, None, None, 0, 16, None) == E
+                                None, 0, 0.1, None, None, None, 0, 16, None) == E
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None, None,
                                   None, None, None, 512, 16, 16, None) == E
     assert lib.kvlr_project_queries(ctypes.byref(s), ctypes.byref(f), None, None, 16, None) == E
@@ -99,28 +99,34 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     fake = 1 << 20  # aligned non-null placeholder; never dereferenced on these paths
     c2 = K.make_cache(fake, fake, fake)
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 63,
-                                fake, None, fake, 1 << 30, 16, None) == E
+                                fake, None, None, fake, 1 << 30, 16, None) == E
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 513,
-                                fake, None, fake, 1 << 30, 16, None) == E
+                                fake, None, None, fake, 1 << 30, 16, None) == E
     # topk fraction with a zero denominator
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 0, 64,
-                                fake, None, fake, 1 << 30, 16, None) == E
+                                fake, None, None, fake, 1 << 30, 16, None) == E
     # misaligned pointer
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake + 4, fake, fake, 512, 1, 8,
-                                64, fake, None, fake, 1 << 30, 16, None) == E
+                                64, fake, None, None, fake, 1 << 30, 16, None) == E
     # workspace too small
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
-                                fake, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+                                fake, None, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
     assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, fake,
-                                64, 0.1, fake, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+                                None, 64, 0.1, fake, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    # counts without a page list
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, None,
+                                fake, 64, 0.1, fake, None, fake, 1 << 30, 16, None) == E
+    # batch above the supported maximum
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
+                                fake, None, None, fake, 1 << 40, 5000, None) == K.KVLR_ERR_UNSUPPORTED
     # non-positive or non-finite softmax scale
     for sc in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512,
-                                    fake, 64, sc, fake, None, fake, 1 << 30, 16, None) == E
+                                    fake, None, 64, sc, fake, None, fake, 1 << 30, 16, None) == E
     # routing needs the routed (exact-key) cache
     sl = _shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)
     assert lib.kvlr_route_pages(ctypes.byref(sl), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
-                                fake, None, fake, 1 << 30, 16, None) == K.KVLR_ERR_UNSUPPORTED
+                                fake, None, None, fake, 1 << 30, 16, None) == K.KVLR_ERR_UNSUPPORTED
     # negative batch / sizes
     assert lib.kvlr_upproject(ctypes.byref(s), ctypes.byref(f), fake, fake, -1, None) == E
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,

@@ -224,7 +224,7 @@ def test_binding_reports_bad_launch_arguments():
     s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=1)
     with pytest.raises(K.KvlrError):
         K.kvlr_route_pages(s.shape, s.kcache, s.q_proj, s.seq_lens_dev, s.page_table, s.max_pages,
-                           1, 8, s.k_max - 1, s.sel, None, s.workspace, s.ws_bytes, wl.batch)
+                           1, 8, s.k_max - 1, s.sel, None, None, s.workspace, s.ws_bytes, wl.batch)
     with pytest.raises(K.KvlrError):
         K.kvlr_decode_attn(s.shape, s.kcache, s.q, s.q_proj, s.seq_lens_dev, s.page_table,
-                           s.max_pages, s.sel, s.k_max, 0.1, s.z, s.lse, s.workspace, 64, wl.batch)
+                           s.max_pages, s.sel, None, s.k_max, 0.1, s.z, s.lse, s.workspace, 64, wl.batch)
