@@ -14,7 +14,6 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -26,21 +25,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from decode_attention_rank_amd.session import DecodeSession  # noqa: E402
+from decode_attention_rank_amd.traffic import source_hash  # noqa: E402
 from decode_attention_rank_amd.workloads import DEFAULT_BENCH_WORKLOAD, WORKLOADS  # noqa: E402
 
 METRIC = "decode-attn KV-tokens/s over compressed cache + % of HBM peak GB/s (1 GPU)"
 HBM_PEAK_GBPS = 8000.0
+CPU_CACHE_BYTES = 6 << 30  # host memory for oracle inputs repeated after the first pass
 ROUTE_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_route.hip")
 ATTN_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_attn.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_hash(path: str) -> str:
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str, src: str):
@@ -61,43 +57,70 @@ def cpu_baseline(sess, budget_s: float):
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from tests import gpu_harness as H
-    import oracle as O
-
     wl = sess.wl
-    order = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
-    rng = np.random.default_rng(0)
-    rng.shuffle(order)
-    spent, tokens, pairs = 0.0, 0, 0
-    for b, g in order:
-        st_rows = sess.prefix_rows(b)
-        prefix = {k: H.f64(v[g]) for k, v in st_rows.items()}
-        off = sum(sess.n_new[:b])
-        n = sess.n_new[b]
-        Kn = H.f64(sess.k_new[off:off + n, g])
-        Vn = H.f64(sess.v_new[off:off + n, g])
-        f = H.factors_np(sess, g)
-        q = H.q_group(sess, b, g)
-        t0 = time.perf_counter()
-        st = O.append_tokens(prefix, sess.lens_before[b], Kn, Vn, f["A_v"], f["A_k"], f["W_pred"],
-                             key_mode=wl.key_mode, storage=wl.storage)
-        res = O.decode_pair(q, st, f, sess.seq_lens[b], wl.page_size, key_mode=wl.key_mode,
-                            scale=sess.scale, topk=(wl.topk_num, wl.topk_den))
-        O.upproject(res["z"], f["B_v"])
-        spent += time.perf_counter() - t0
-        tokens += sess.seq_lens[b]
-        pairs += 1
-        if spent >= budget_s:
+    seqs = list(range(wl.batch))
+    np.random.default_rng(0).shuffle(seqs)
+    order = [(b, g) for b in seqs for g in range(wl.num_kv_heads)]
+    memo = {}
+    spent, tokens, pairs, passes = 0.0, 0, 0, 0
+    cache, cached_bytes = [], 0
+    while spent < budget_s:
+        passes += 1
+        items = cache if passes > 1 else (_oracle_inputs(sess, b, g, memo) for b, g in order)
+        for item in items:
+            t0 = time.perf_counter()
+            _oracle_pair(wl, sess.scale, item)
+            spent += time.perf_counter() - t0
+            tokens += item["L"]
+            pairs += 1
+            if passes == 1 and cached_bytes < CPU_CACHE_BYTES:
+                cache.append(item)
+                cached_bytes += sum(a.nbytes for a in item["prefix"].values())
+            if spent >= budget_s:
+                break
+        if not cache:
             break
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     value = tokens / wl.num_kv_heads / spent
     return {
         "value": value, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"{pairs} of {wl.batch * wl.num_kv_heads} (sequence, KV head) pairs, "
-                   f"{tokens} context tokens, {spent:.1f} s of float64 numpy on the host; "
+        "sample": (f"{pairs} (sequence, KV head) pair runs, {passes} pass(es) over the "
+                   f"{wl.batch * wl.num_kv_heads} pairs taken sequence by sequence in shuffled "
+                   f"order (later passes repeat the first {len(cache)}), {tokens} context "
+                   f"tokens, {spent:.1f} s of float64 numpy on the host; "
                    f"rate = tokens / H_kv / seconds"),
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def _oracle_inputs(sess, b, g, memo):
+    """One pair's inputs for the oracle, in float64 (not timed)."""
+    from tests import gpu_harness as H
+
+    if memo.get("b") != b:
+        memo.clear()
+        memo["b"], memo["rows"] = b, sess.prefix_rows(b)
+    st_rows = memo["rows"]
+    off = sum(sess.n_new[:b])
+    n = sess.n_new[b]
+    return {
+        "prefix": {k: H.f64(v[g]) for k, v in st_rows.items()},
+        "L_before": sess.lens_before[b], "L": sess.seq_lens[b],
+        "K": H.f64(sess.k_new[off:off + n, g]), "V": H.f64(sess.v_new[off:off + n, g]),
+        "f": H.factors_np(sess, g), "q": H.q_group(sess, b, g),
+    }
+
+
+def _oracle_pair(wl, scale, it):
+    """Append, route, attend and up-project one pair with the oracle."""
+    import oracle as O
+
+    f = it["f"]
+    st = O.append_tokens(it["prefix"], it["L_before"], it["K"], it["V"], f["A_v"], f["A_k"],
+                         f["W_pred"], key_mode=wl.key_mode, storage=wl.storage)
+    res = O.decode_pair(it["q"], st, f, it["L"], wl.page_size, key_mode=wl.key_mode, scale=scale,
+                        topk=(wl.topk_num, wl.topk_den))
+    O.upproject(res["z"], f["B_v"])
 
 
 def main():
@@ -192,6 +215,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": cfg,
         "step_algo_bytes": step_bytes,
+        "kernel_algo_bytes": {"encode_kernel": sess.append_bytes(), "attn_kernel": sess.attend_bytes(),
+                              "route_kernel": sess.route_bytes() if wl.routed else 0},
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": roof,
     }
