@@ -25,6 +25,10 @@
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
 
+#ifndef KVLR_ENCODE_WGS
+#define KVLR_ENCODE_WGS 3072  // workgroups over all KV heads (each loops over tiles)
+#endif
+
 namespace kvlr {
 namespace {
 
@@ -83,10 +87,15 @@ struct EncSmem {
   alignas(16) E ak[KSD][RK / 16][kWave][KPL];
   alignas(16) E mhi[ROUTED ? KSV : 1][RK / 16][kWave][KPL];
   alignas(16) E mlo[(ROUTED && KPL > 1) ? KSV : 1][RK / 16][kWave][KPL];
-  float mstage[ROUTED ? RV : 1][RK + 1];
-  // per-wave row-major tiles of the rounded latents (16 tokens)
-  alignas(16) E vt[kWaves][16][RV + CH];
-  alignas(16) E ct[kWaves][16][RK + CH];
+  struct Tiles {
+    // per-wave row-major tiles of the rounded latents (16 tokens)
+    alignas(16) E vt[kWaves][16][RV + CH];
+    alignas(16) E ct[kWaves][16][RK + CH];
+  };
+  union {
+    float mstage[ROUTED ? RV : 1][RK + 1];  // set-up only
+    Tiles t;
+  } u;
 };
 
 __device__ inline void wave_lds_sync() {
@@ -111,6 +120,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   constexpr int NTV = RV / 16, NTK = RK / 16;
   constexpr int CV = RV / CH, CK = RK / CH, CD = D / CH;
   __shared__ SM sm;
+  extern __shared__ int s_seq[];  // cu_new[0..batch], then lens_before[0..batch)
 
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
@@ -119,19 +129,28 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   const E* Av = reinterpret_cast<const E*>(A_v) + static_cast<size_t>(g) * D * RV;
   const E* Ak = reinterpret_cast<const E*>(A_k) + static_cast<size_t>(g) * D * RK;
 
-  // ---- stage B fragments: element (k, n) with k = ks*KSTEP + KPL*(l/16) + e, n = nt*16 + l%16
-  for (int idx = tid; idx < KSD * NTV * kWave * KPL; idx += kThreads) {
-    const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTV;
-    const int ks = idx / (KPL * kWave * NTV);
-    const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
-    sm.av[ks][nt][l][e] = Av[k * RV + n];
-  }
-  for (int idx = tid; idx < KSD * NTK * kWave * KPL; idx += kThreads) {
-    const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTK;
-    const int ks = idx / (KPL * kWave * NTK);
-    const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
-    sm.ak[ks][nt][l][e] = Ak[k * RK + n];
-  }
+  // ---- stage B fragments: element (k, n) with k = ks*KSTEP + KPL*(l/16) + e,
+  // n = nt*16 + l%16; each thread reads CH consecutive n of one row k
+  auto stage = [&](const E* src, E* dst, int R) {
+    const int rc = R / CH;  // chunks per row
+    for (int idx = tid; idx < D * rc; idx += kThreads) {
+      const int k = idx / rc, n0 = (idx - k * rc) * CH;
+      float x[CH];
+      S::unpack(load16(src + static_cast<size_t>(k) * R + n0), x);
+      const int ks = k / KSTEP, kk = k - ks * KSTEP;
+#pragma unroll
+      for (int e2 = 0; e2 < CH; ++e2) {
+        const int n = n0 + e2;
+        const int l = (kk / KPL) * 16 + (n & 15);
+        dst[((static_cast<size_t>(ks) * (R / 16) + (n >> 4)) * kWave + l) * KPL + (kk % KPL)] =
+            MM::store(x[e2]);
+      }
+    }
+  };
+  stage(Av, &sm.av[0][0][0][0], RV);
+  stage(Ak, &sm.ak[0][0][0][0], RK);
+  for (int b = tid; b <= batch; b += kThreads) s_seq[b] = cu_new[b];
+  for (int b = tid; b < batch; b += kThreads) s_seq[batch + 1 + b] = lens_before[b];
   __syncthreads();
 
   if constexpr (ROUTED) {
@@ -147,14 +166,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
         acc = MM::mma(a, MM::lds(&sm.ak[ks][nt][lane][0]), acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.mstage[mt * 16 + 4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[i];
+      for (int i = 0; i < 4; ++i) sm.u.mstage[mt * 16 + 4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[i];
     }
     __syncthreads();
     for (int idx = tid; idx < KSV * NTK * kWave * KPL; idx += kThreads) {
       const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTK;
       const int ks = idx / (KPL * kWave * NTK);
       const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
-      const float mv = (k < RV) ? -sm.mstage[k][n] : 0.f;
+      const float mv = (k < RV) ? -sm.u.mstage[k][n] : 0.f;
       const E hi = MM::store(mv);
       sm.mhi[ks][nt][l][e] = hi;
       if constexpr (KPL > 1) sm.mlo[ks][nt][l][e] = MM::store(mv - MM::value(hi));
@@ -165,58 +184,93 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   const int ntiles = (total_new + 63) / 64;
   const int r = lane & 15;        // A-operand row (token) of this lane
   const int kq = lane >> 4;       // A-operand k group of this lane
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // with 16-byte fragments (bf16) the key fragments are also the 16-byte
+  // chunks of the original key and are stored from registers
+  constexpr bool FRAG_IS_CHUNK = (KPL == CH);
+  // Loads are unconditional (no branch around them): lanes past the last
+  // token read token 0 instead, and since an output row of the products
+  // depends only on its own token row, those rows are simply never stored.
+  auto load_tile = [&](int tile, frag_t (&vf)[KSD], frag_t (&kf)[KSD]) {
+    const int i = tile * 64 + wave * 16 + r;
+    const size_t row_off = (static_cast<size_t>(i < total_new ? i : 0) * Hkv + g) * D * EB;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) vf[ks] = MM::gmem(v_new + row_off + (ks * KSTEP + KPL * kq) * EB);
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) kf[ks] = MM::gmem(k_new + row_off + (ks * KSTEP + KPL * kq) * EB);
+  };
+  // sequence of token i: largest b with cu_new[b] <= i (offsets staged in LDS);
+  // returns its page-table entry (entry 0 of sequence 0 past the last token)
+  auto locate = [&](int tile, size_t& slot_off) -> const int32_t* {
+    const int i = tile * 64 + wave * 16 + r;
+    slot_off = 0;
+    if (i >= total_new) return page_table;
+    int lo = 0, hi = batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_seq[mid] <= i) lo = mid; else hi = mid;
+    }
+    const int pos = s_seq[batch + 1 + lo] + (i - s_seq[lo]);
+    slot_off = static_cast<size_t>(pos & (P - 1)) * 16;
+    return page_table + static_cast<size_t>(lo) * max_pages + (pos >> log2P);
+  };
+  // one tile: multiply, round, store (latents via the wave's LDS tile)
+  auto process = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+                     size_t slot_off) {
     const int i = tile * 64 + wave * 16 + r;
     const bool valid = i < total_new;
-    size_t slot_off = 0, phys = 0;
-    if (valid) {
-      int lo = 0, hi = batch;  // largest b with cu_new[b] <= i
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (cu_new[mid] <= i) lo = mid; else hi = mid;
+    // original key: stored straight from the loaded fragments
+    if constexpr (ROUTED) {
+      if (valid) {
+        uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off;
+        if constexpr (FRAG_IS_CHUNK) {
+          // fragment ks of this lane is chunk ks * KSTEP / CH + kq of the key row
+#pragma unroll
+          for (int ks = 0; ks < KSD; ++ks)
+            store16(kd + static_cast<size_t>(ks * (KSTEP / CH) + kq) * P * 16,
+                    __builtin_bit_cast(uint4, kf[ks]));
+        } else {
+          const size_t row_off = (static_cast<size_t>(i) * Hkv + g) * D * EB;
+          for (int c = kq; c < CD; c += 4)
+            store16(kd + static_cast<size_t>(c) * P * 16, load16(k_new + row_off + c * 16));
+        }
       }
-      const int pos = lens_before[lo] + (i - cu_new[lo]);
-      phys = static_cast<size_t>(page_table[static_cast<size_t>(lo) * max_pages + (pos >> log2P)]);
-      slot_off = static_cast<size_t>(pos & (P - 1)) * 16;
     }
-    const size_t row_off = (static_cast<size_t>(valid ? i : 0) * Hkv + g) * D * EB;
-
     // ---- v = V A_v
     f32x4 vacc[NTV];
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) vacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const frag_t a = valid ? MM::gmem(v_new + row_off + (ks * KSTEP + KPL * kq) * EB) : MM::zero();
+    for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < NTV; ++nt) vacc[nt] = MM::mma(a, MM::lds(&sm.av[ks][nt][lane][0]), vacc[nt]);
-    }
+      for (int nt = 0; nt < NTV; ++nt) vacc[nt] = MM::mma(vf[ks], MM::lds(&sm.av[ks][nt][lane][0]), vacc[nt]);
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.vt[wave][4 * kq + j][nt * 16 + r] = MM::store(vacc[nt][j]);
-    wave_lds_sync();
-    if (valid) {
-      uint8_t* dst = v_lat + (phys * Hkv + g) * CV * P * 16 + slot_off;
-      for (int c = kq; c < CV; c += 4)
-        store16(dst + static_cast<size_t>(c) * P * 16, *reinterpret_cast<const uint4*>(&sm.vt[wave][r][c * CH]));
-    }
+      for (int j = 0; j < 4; ++j) sm.u.t.vt[wave][4 * kq + j][nt * 16 + r] = MM::store(vacc[nt][j]);
 
     // ---- residual latent (routed) or key latent (dense)
     f32x4 cacc[NTK];
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt) cacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const frag_t a = valid ? MM::gmem(k_new + row_off + (ks * KSTEP + KPL * kq) * EB) : MM::zero();
+    for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < NTK; ++nt) cacc[nt] = MM::mma(a, MM::lds(&sm.ak[ks][nt][lane][0]), cacc[nt]);
+      for (int nt = 0; nt < NTK; ++nt) cacc[nt] = MM::mma(kf[ks], MM::lds(&sm.ak[ks][nt][lane][0]), cacc[nt]);
+    wave_lds_sync();
+    if (valid) {
+      uint8_t* dst = v_lat + (phys * Hkv + g) * CV * P * 16 + slot_off;
+#pragma unroll
+      for (int c0 = 0; c0 < CV; c0 += 4) {
+        const int c = c0 + kq;
+        if (c < CV)
+          store16(dst + static_cast<size_t>(c) * P * 16, *reinterpret_cast<const uint4*>(&sm.u.t.vt[wave][r][c * CH]));
+      }
     }
     if constexpr (ROUTED) {
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks) {
         const int k = ks * KSTEP + KPL * kq;
-        const frag_t a = (k < RV) ? MM::lds(&sm.vt[wave][r][k]) : MM::zero();
+        const frag_t a = (k < RV) ? MM::lds(&sm.u.t.vt[wave][r][k]) : MM::zero();
 #pragma unroll
         for (int nt = 0; nt < NTK; ++nt) {
           cacc[nt] = MM::mma(a, MM::lds(&sm.mhi[ks][nt][lane][0]), cacc[nt]);
@@ -227,19 +281,26 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.ct[wave][4 * kq + j][nt * 16 + r] = MM::store(cacc[nt][j]);
+      for (int j = 0; j < 4; ++j) sm.u.t.ct[wave][4 * kq + j][nt * 16 + r] = MM::store(cacc[nt][j]);
     wave_lds_sync();
     if (valid) {
       uint8_t* dst = k_lat + (phys * Hkv + g) * CK * P * 16 + slot_off;
-      for (int c = kq; c < CK; c += 4)
-        store16(dst + static_cast<size_t>(c) * P * 16, *reinterpret_cast<const uint4*>(&sm.ct[wave][r][c * CH]));
-      if constexpr (ROUTED) {
-        uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off;
-        for (int c = kq; c < CD; c += 4)
-          store16(kd + static_cast<size_t>(c) * P * 16, load16(k_new + row_off + c * 16));
+#pragma unroll
+      for (int c0 = 0; c0 < CK; c0 += 4) {
+        const int c = c0 + kq;
+        if (c < CK)
+          store16(dst + static_cast<size_t>(c) * P * 16, *reinterpret_cast<const uint4*>(&sm.u.t.ct[wave][r][c * CH]));
       }
     }
     wave_lds_sync();
+  };
+
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    frag_t vf[KSD], kf[KSD];
+    load_tile(tile, vf, kf);
+    size_t slot = 0;
+    const int phys = *locate(tile, slot);
+    process(tile, vf, kf, static_cast<size_t>(phys), slot);
   }
 }
 
@@ -247,10 +308,11 @@ template <class S, int D, int RV, int RK, bool ROUTED>
 hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   const int ntiles = (a.total_new + 63) / 64;
-  int per_head = (2048 + a.dm.Hkv - 1) / a.dm.Hkv;
+  int per_head = (KVLR_ENCODE_WGS + a.dm.Hkv - 1) / a.dm.Hkv;
   if (per_head > ntiles) per_head = ntiles;
   dim3 grid(per_head, a.dm.Hkv);
-  hipLaunchKernelGGL((encode_kernel<S, D, RV, RK, ROUTED>), grid, dim3(kThreads), 0, s,
+  const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
+  hipLaunchKernelGGL((encode_kernel<S, D, RV, RK, ROUTED>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(a.A_v), static_cast<const uint8_t*>(a.A_k),
                      static_cast<const uint8_t*>(a.W_pred), static_cast<const uint8_t*>(a.k_new),
                      static_cast<const uint8_t*>(a.v_new), a.cu_new, a.lens_before, a.page_table,

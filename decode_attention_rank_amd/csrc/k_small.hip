@@ -17,81 +17,94 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// One workgroup per (sequence, KV head): the G query heads share the factor rows.
-template <class S>
-__global__ __launch_bounds__(256) void qproj_kernel(const uint8_t* __restrict__ W_pred,
-                                                    const uint8_t* __restrict__ B_k,
-                                                    const float* __restrict__ q,
-                                                    float* __restrict__ q_proj, int Hq, int Hkv,
-                                                    int G, int D, int RV, int RK, int exact) {
-  extern __shared__ float s_q[];  // [G][D]
-  constexpr int CH = S::CH;
-  const int pair = blockIdx.x;
-  const int b = pair / Hkv;
-  const int g = pair - b * Hkv;
-  const float* qg = q + static_cast<size_t>(b * Hq + g * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) s_q[i] = qg[i];
-  __syncthreads();
-  const int RVe = exact ? RV : 0;
-  const int Wd = RVe + RK;
-  for (int i = threadIdx.x; i < G * Wd; i += blockDim.x) {
-    const int h = i / Wd, o = i - h * Wd;
-    const uint8_t* row = (o < RVe)
-        ? W_pred + (static_cast<size_t>(g) * RV + o) * D * S::ELEM_BYTES
-        : B_k + (static_cast<size_t>(g) * RK + (o - RVe)) * D * S::ELEM_BYTES;
-    const float* qh = s_q + h * D;
-    float acc = 0.f;
-    for (int c = 0; c < D / CH; ++c) {
-      float x[CH];
-      S::unpack(load16(row + c * 16), x);
+// One 16 x 16 output tile of  out[r, n] = sum_k a[r, k] w(k, n)  on the float32
+// matrix cores (v_mfma_f32_16x16x4_f32), one wave per tile. Rows r are the
+// (sequence, query head) rows of one KV group: r = b * G + (h - g * G).
+// Lane l feeds A[l % 16][k] and B[k][l % 16] with k taken from the contiguous
+// quarter (l / 16) * K/4 .. + K/4 of the reduction, so every operand of the
+// tile is loaded before the first multiply and the loads overlap.
+// W_NMAJOR: w(k, n) = W[n][k] (rows of W are outputs), else W[k][n].
+template <class S, int K, bool W_NMAJOR>
+__device__ inline void small_gemm_tile(const float* __restrict__ a_src, int a_row_stride,
+                                       const uint8_t* __restrict__ W, int w_ld, int rows,
+                                       int row_tile, int n0, int G, int Hq, int g,
+                                       float* __restrict__ out, int out_stride, int out_off) {
+  constexpr int KQ = K / 4;  // reduction elements per lane quarter
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const int kq = lane >> 4;
+  const int ra = row_tile * 16 + j;
+  const bool va = ra < rows;
+  const int ba = va ? ra / G : 0;
+  const int ha = va ? g * G + (ra - ba * G) : 0;
+  float av[KQ], bv[KQ];
+  const float* ar = a_src + static_cast<size_t>(ba * Hq + ha) * a_row_stride + kq * KQ;
 #pragma unroll
-      for (int e = 0; e < CH; ++e) acc = fmaf(qh[c * CH + e], x[e], acc);
+  for (int i = 0; i < KQ; i += 4) {
+    const float4 t = va ? *reinterpret_cast<const float4*>(ar + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    av[i] = t.x;
+    av[i + 1] = t.y;
+    av[i + 2] = t.z;
+    av[i + 3] = t.w;
+  }
+  if constexpr (W_NMAJOR) {
+    constexpr int CH = S::CH;
+    const uint8_t* wr = W + (static_cast<size_t>(n0 + j) * w_ld + kq * KQ) * S::ELEM_BYTES;
+#pragma unroll
+    for (int c = 0; c < KQ / CH; ++c) {
+      float x[CH];
+      S::unpack(load16(wr + c * 16), x);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) bv[c * CH + e] = x[e];
     }
-    q_proj[(static_cast<size_t>(b) * Hq + g * G + h) * Wd + o] = acc;
+  } else {
+#pragma unroll
+    for (int i = 0; i < KQ; ++i)
+      bv[i] = S::load1(W, static_cast<long>(kq * KQ + i) * w_ld + n0 + j);
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[i], acc, 0, 0, 0);
+  // result layout: lane holds rows 4 * (l / 16) + i of column l % 16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row_tile * 16 + 4 * kq + i;
+    if (r >= rows) continue;
+    const int bb = r / G;
+    const int hh = g * G + (r - bb * G);
+    out[static_cast<size_t>(bb * Hq + hh) * out_stride + out_off + n0 + j] = acc[i];
   }
 }
 
-// One wave per 16 (sequence, head) rows of one KV group, all d columns.
+// q_proj rows: [q W_pred^T (exact mode only), q B_k^T]. Grid: (row tiles,
+// output-column tiles, KV heads).
+template <class S, int D>
+__global__ __launch_bounds__(64) void qproj_kernel(const uint8_t* __restrict__ W_pred,
+                                                   const uint8_t* __restrict__ B_k,
+                                                   const float* __restrict__ q,
+                                                   float* __restrict__ q_proj, int B, int Hq,
+                                                   int Hkv, int G, int RV, int RK, int exact) {
+  const int g = blockIdx.z;
+  const int RVe = exact ? RV : 0;
+  const int Wd = RVe + RK;
+  const int n0 = blockIdx.y * 16;
+  const bool pred = n0 < RVe;
+  const uint8_t* W = pred ? W_pred + static_cast<size_t>(g) * RV * D * S::ELEM_BYTES
+                          : B_k + static_cast<size_t>(g) * RK * D * S::ELEM_BYTES;
+  const int wn0 = pred ? n0 : n0 - RVe;
+  small_gemm_tile<S, D, true>(q, D, W, D, B * G, blockIdx.x, wn0, G, Hq, g, q_proj, Wd,
+                              pred ? 0 : RVe);
+}
+
+// o = z B_v per KV group. Grid: (row tiles, D / 16, KV heads).
 template <class S, int RV, int D>
 __global__ __launch_bounds__(64) void upproject_kernel(const float* __restrict__ z,
                                                        const uint8_t* __restrict__ B_v,
                                                        float* __restrict__ o, int B, int Hq,
                                                        int Hkv, int G) {
-  constexpr int NT = D / 16;
-  const int g = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int rows = B * G;
-  // A operand row of this lane: l % 16; k offset: l / 16
-  const int ra = blockIdx.x * 16 + (lane & 15);
-  const bool va = ra < rows;
-  const int ba = va ? ra / G : 0;
-  const int ha = va ? g * G + (ra - ba * G) : 0;
-  const float* zr = z + (static_cast<size_t>(ba) * Hq + ha) * RV;
-  const int kq = lane >> 4;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const size_t bbase = static_cast<size_t>(g) * RV * D;
-#pragma unroll 4
-  for (int k0 = 0; k0 < RV; k0 += 4) {
-    const float a = va ? zr[k0 + kq] : 0.f;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float bv = S::load1(B_v, bbase + static_cast<size_t>(k0 + kq) * D + n * 16 + (lane & 15));
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[n], 0, 0, 0);
-    }
-  }
-  // D layout: lane holds rows 4*(l/16)+i, column l%16 of each 16x16 tile
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = blockIdx.x * 16 + 4 * (lane >> 4) + i;
-    if (r >= rows) continue;
-    const int bb = r / G;
-    const int hh = g * G + (r - bb * G);
-    float* orow = o + (static_cast<size_t>(bb) * Hq + hh) * D;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) orow[n * 16 + (lane & 15)] = acc[n][i];
-  }
+  const int g = blockIdx.z;
+  small_gemm_tile<S, RV, false>(z, RV, B_v + static_cast<size_t>(g) * RV * D * S::ELEM_BYTES, D,
+                                B * G, blockIdx.x, blockIdx.y * 16, G, Hq, g, o, D, 0);
 }
 
 __global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
@@ -105,7 +118,7 @@ __global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __r
 
 template <class S, int RV>
 hipError_t up_by_d(const UpprojArgs& a, hipStream_t s) {
-  dim3 grid((a.batch * a.dm.G + 15) / 16, a.dm.Hkv);
+  dim3 grid((a.batch * a.dm.G + 15) / 16, a.dm.D / 16, a.dm.Hkv);
   switch (a.dm.D) {
     case 64:
       hipLaunchKernelGGL((upproject_kernel<S, RV, 64>), grid, dim3(64), 0, s, a.z,
@@ -117,6 +130,26 @@ hipError_t up_by_d(const UpprojArgs& a, hipStream_t s) {
                          static_cast<const uint8_t*>(a.B_v), a.o, a.batch, a.dm.Hq, a.dm.Hkv,
                          a.dm.G);
       return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class S, int D>
+hipError_t qproj_t(const QprojArgs& a, hipStream_t s) {
+  const int width = (a.dm.exact ? a.dm.RV : 0) + a.dm.RK;
+  dim3 grid((a.batch * a.dm.G + 15) / 16, width / 16, a.dm.Hkv);
+  hipLaunchKernelGGL((qproj_kernel<S, D>), grid, dim3(64), 0, s,
+                     static_cast<const uint8_t*>(a.W_pred), static_cast<const uint8_t*>(a.B_k),
+                     a.q, a.q_proj, a.batch, a.dm.Hq, a.dm.Hkv, a.dm.G, a.dm.RV, a.dm.RK,
+                     a.dm.exact);
+  return hipGetLastError();
+}
+
+template <class S>
+hipError_t qproj_by_d(const QprojArgs& a, hipStream_t s) {
+  switch (a.dm.D) {
+    case 64: return qproj_t<S, 64>(a, s);
+    case 128: return qproj_t<S, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -135,19 +168,8 @@ hipError_t up_by_rv(const UpprojArgs& a, hipStream_t s) {
 
 hipError_t launch_qproj(const QprojArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  const size_t lds = static_cast<size_t>(a.dm.G) * a.dm.D * sizeof(float);
-  dim3 grid(a.batch * a.dm.Hkv);
-  if (a.dm.dtype == 0)
-    hipLaunchKernelGGL((qproj_kernel<BF16>), grid, dim3(256), lds, s,
-                       static_cast<const uint8_t*>(a.W_pred), static_cast<const uint8_t*>(a.B_k),
-                       a.q, a.q_proj, a.dm.Hq, a.dm.Hkv, a.dm.G, a.dm.D, a.dm.RV, a.dm.RK,
-                       a.dm.exact);
-  else
-    hipLaunchKernelGGL((qproj_kernel<F32>), grid, dim3(256), lds, s,
-                       static_cast<const uint8_t*>(a.W_pred), static_cast<const uint8_t*>(a.B_k),
-                       a.q, a.q_proj, a.dm.Hq, a.dm.Hkv, a.dm.G, a.dm.D, a.dm.RV, a.dm.RK,
-                       a.dm.exact);
-  return hipGetLastError();
+  if (a.dm.dtype == 0) return qproj_by_d<BF16>(a, s);
+  return qproj_by_d<F32>(a, s);
 }
 
 hipError_t launch_upproject(const UpprojArgs& a, hipStream_t s) {

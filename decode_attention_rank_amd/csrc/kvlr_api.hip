@@ -53,7 +53,7 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxBatch = 4096;          // per-sequence work lists live in LDS
+constexpr int kMaxBatch = 4096;          // per-sequence offsets and work lists live in LDS
 #ifndef KVLR_ROUTE_GRID
 #define KVLR_ROUTE_GRID 2048
 #endif
@@ -145,6 +145,7 @@ kvlr_status kvlr_append_encode(const kvlr_shape* shape, const kvlr_factors* fact
   if (!factors || !cache || batch < 0 || total_new < 0) return KVLR_ERR_INVALID_ARGUMENT;
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
   if (batch == 0 || total_new == 0) return KVLR_OK;
+  if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
   if (!ok_ptr(factors->A_v) || !ok_ptr(factors->A_k) || !ok_ptr(cache->v_lat) ||
       !ok_ptr(cache->k_lat) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(cu_new) ||
       !ok_ptr(seq_lens_before) || !ok_ptr(page_table))

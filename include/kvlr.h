@@ -54,7 +54,7 @@
  * Query-head h belongs to KV head h / G, G = num_q_heads / num_kv_heads.
  * Supported: head_dim in {64, 128}; rank_v, rank_k in {16, 32, 64} and
  * <= head_dim; page_size in {16, 32, 64}; G in {1, 2, 4, 8};
- * max_pages_per_seq <= 65536; batch <= 4096 for routing and attention.
+ * max_pages_per_seq <= 65536; batch <= 4096.
  * Other values return KVLR_ERR_UNSUPPORTED.
  */
 #ifndef KVLR_H

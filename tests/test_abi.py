@@ -119,6 +119,8 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     # batch above the supported maximum
     assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
                                 fake, None, None, fake, 1 << 40, 5000, None) == K.KVLR_ERR_UNSUPPORTED
+    assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
+                                  fake, fake, fake, 512, 5000, 16, None) == K.KVLR_ERR_UNSUPPORTED
     # non-positive or non-finite softmax scale
     for sc in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512,
