@@ -7,23 +7,31 @@
 // space, z = sum_t p_t v_t, and B_v is applied once per head afterwards.
 // In the dense low-rank mode the keys are latents too: s_t = scale q B_k^T . k_t.
 //
-// Work split: grid (split, pair). A workgroup of 4 waves takes a range of
-// 64-token rows of the pair's page list (selected pages, or all pages). Per row:
+// Work split: a persistent grid walks a device-built list of chunks; a chunk
+// is a run of up to rows_per_chunk 64-token rows of one (sequence, KV head)
+// pair's page list (selected pages, or all pages), and the 4 waves of a
+// workgroup take every fourth row of it. Per row:
 //   scores  - one lane per token; the token's key row is read as 16-byte
 //             chunks (contiguous across the row's tokens), the wave-uniform
 //             query is read with scalar loads; G heads share each load;
 //   softmax - online (running max and sum per head, base-2 exponent);
 //   P.V     - lanes regroup as (latent chunk c, tokens l/CV + k*64/CV), the
 //             probabilities are exchanged through LDS, each lane accumulates
-//             G x CH latent outputs;
-// then waves and workgroups merge their (max, sum, z) partials; the last
-// workgroup of a pair (atomic ticket) merges the splits into z and lse.
+//             G x CH latent outputs.
+// With one page per row (page_size 64) every key and value register is
+// re-requested with the wave's next row as soon as it has been used, so each
+// wave keeps a row in flight.
+// Waves and workgroups then merge their (max, sum, z) partials; the last
+// workgroup of a pair (atomic ticket) merges the chunks into z and lse.
 
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
 
-#ifndef KVLR_ATTN_PREFETCH
-#define KVLR_ATTN_PREFETCH 0
+#ifndef KVLR_ATTN_ROWS_SELECTED
+#define KVLR_ATTN_ROWS_SELECTED 16
+#endif
+#ifndef KVLR_ATTN_ROWS_DENSE
+#define KVLR_ATTN_ROWS_DENSE 128
 #endif
 
 namespace kvlr {
@@ -155,71 +163,86 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     };
 
     if constexpr (ROWPAGE) {
-      // one page per row: page id and physical page are wave-uniform
+      // One page per row: page id and physical page are wave-uniform. Each
+      // key or value register is re-requested with the next row's data as
+      // soon as this row has used it, so a wave always has a row in flight.
+      // The loads carry no branch (the compiler can then count them in
+      // flight): past the last row every lane reads one shared address, and
+      // slots past the sequence end are read but never used (scores are
+      // masked, value chunks are zeroed when used).
       auto page_of = [&](int row) -> int {
+        if (row >= row1) return -1;
         const int pg = sl ? sl[row] : row;
         return (pg >= 0 && pg < N) ? pg : -1;
       };
-      // issue one row's key and value loads (masked past the valid tokens)
-      auto issue = [&](int pg, int ph, uint4 (&kc)[CKW], uint4 (&vc)[CV]) -> int {
-        const int nvalid = (pg >= 0) ? min(L - pg * kWave, kWave) : 0;
-        const uint8_t* kb = keys + (static_cast<size_t>(ph) * Hkv + g) * slab_k + lane * 16;
-        const uint8_t* vb = v_lat + (static_cast<size_t>(ph) * Hkv + g) * slab_v + my_c * kWave * 16;
-        const bool kvalid = lane < nvalid;
+      struct RowRef {
+        const uint8_t* kb;
+        const uint8_t* vb;
+        int kstride, vstride, nvalid;
+      };
+      auto row_ref = [&](int pg) -> RowRef {
+        RowRef rr;
+        if (pg >= 0) {
+          const size_t ph = static_cast<size_t>(pt[pg]);
+          rr.kb = keys + (ph * Hkv + g) * slab_k + lane * 16;
+          rr.vb = v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * 16;
+          rr.kstride = kWave * 16;
+          rr.vstride = 16;
+          rr.nvalid = min(L - pg * kWave, kWave);
+        } else {
+          rr.kb = keys;
+          rr.vb = v_lat;
+          rr.kstride = 0;
+          rr.vstride = 0;
+          rr.nvalid = 0;
+        }
+        return rr;
+      };
+      int r = row0 + wave;
+      uint4 kc[CKW], vc[CV];
+      RowRef cur = row_ref(page_of(r));
 #pragma unroll
-        for (int c = 0; c < CKW; ++c)
-          kc[c] = kvalid ? load16_stream(kb + c * kWave * 16) : make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < CKW; ++c) kc[c] = load16_stream(cur.kb + c * cur.kstride);
+#pragma unroll
+      for (int k = 0; k < CV; ++k) vc[k] = load16_stream(cur.vb + (lane / CV + k * TPL) * cur.vstride);
+      RowRef nxt = row_ref(page_of(r + kWaves));
+      int pg2 = page_of(r + 2 * kWaves);
+      for (; r < row1; r += kWaves) {
+        // table lookups run ahead: physical page two rows on, page id three rows on
+        const RowRef nn = row_ref(pg2);
+        const int pg3 = page_of(r + 3 * kWaves);
+        float s[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[h] = 0.f;
+        static_for<0, CKW>([&](auto cc) {
+          constexpr int C = decltype(cc)::value;
+          float x[CH];
+          S::unpack(kc[C], x);
+          fma_heads<G, CH, KW, C * CH>(qg, x, s);
+          kc[C] = load16_stream(nxt.kb + C * nxt.kstride);
+        });
+        const bool use = (cur.nvalid > 0) && softmax_row(s, lane < cur.nvalid);
 #pragma unroll
         for (int k = 0; k < CV; ++k) {
           const int tok = lane / CV + k * TPL;
-          vc[k] = (tok < nvalid) ? load16_stream(vb + tok * 16) : make_uint4(0, 0, 0, 0);
+          if (use) {
+            float x[CH];
+            S::unpack(vc[k], x);
+            const bool tv = tok < cur.nvalid;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float pp = s_p[wave][tok][h];
+#pragma unroll
+              for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, tv ? x[e] : 0.f, z[h][e]);
+            }
+          }
+          vc[k] = load16_stream(nxt.vb + tok * nxt.vstride);
         }
-        return nvalid;
-      };
-      auto consume = [&](int nvalid, const uint4 (&kc)[CKW], const uint4 (&vc)[CV]) {
-        if (nvalid > 0) {
-          float s[G];
-          score_keys(kc, s);
-          if (softmax_row(s, lane < nvalid)) accumulate_pv(vc);
-        }
-      };
-      int r = row0 + wave;
-      int pg = (r < row1) ? page_of(r) : -1;
-      int ph = (pg >= 0) ? pt[pg] : 0;
-#if KVLR_ATTN_PREFETCH
-      // two rows in flight: the next row's loads go out before this row is used
-      uint4 kA[CKW], vA[CV], kB[CKW], vB[CV];
-      int nA = (r < row1) ? issue(pg, ph, kA, vA) : 0;
-      while (r < row1) {
-        const int r2 = r + kWaves;
-        int nB = 0;
-        if (r2 < row1) {
-          const int pg2 = page_of(r2);
-          nB = issue(pg2, (pg2 >= 0) ? pt[pg2] : 0, kB, vB);
-        }
-        consume(nA, kA, vA);
-        if (r2 >= row1) break;
-        const int r3 = r2 + kWaves;
-        if (r3 < row1) {
-          const int pg3 = page_of(r3);
-          nA = issue(pg3, (pg3 >= 0) ? pt[pg3] : 0, kA, vA);
-        }
-        consume(nB, kB, vB);
-        r = r3;
+        if (use) wave_lds_sync();
+        cur = nxt;
+        nxt = nn;
+        pg2 = pg3;
       }
-#else
-      for (; r < row1; r += kWaves) {
-        uint4 kc[CKW], vc[CV];
-        const int nvalid = issue(pg, ph, kc, vc);
-        // next row's page, fetched while this row's data is in flight
-        const int rn = r + kWaves;
-        const int pgn = (rn < row1) ? page_of(rn) : -1;
-        const int phn = (pgn >= 0) ? pt[pgn] : 0;
-        consume(nvalid, kc, vc);
-        pg = pgn;
-        ph = phn;
-      }
-#endif
     } else {
       for (int row = row0 + wave; row < row1; row += kWaves) {
         const int item = (row << ipr_log2) + (lane >> log2P);
@@ -395,7 +418,9 @@ hipError_t by_g(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int attn_rows_per_chunk(bool selected) { return selected ? 8 : 32; }
+int attn_rows_per_chunk(bool selected) {
+  return selected ? KVLR_ATTN_ROWS_SELECTED : KVLR_ATTN_ROWS_DENSE;
+}
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
