@@ -128,6 +128,130 @@ __device__ void select_pages(float* scores, int N, int k, int k_max, int max_pag
   for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
 }
 
+// Exclusive prefix sum of v over the workgroup in thread order; also returns
+// the total. One LDS slot per wave; contains two barriers.
+__device__ inline int block_excl_sum(int v, int* total, int* lds4) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) lds4[wave] = incl;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = lds4[w];
+    before += (w < wave) ? c : 0;
+    sum += c;
+  }
+  __syncthreads();
+  *total = sum;
+  return before + incl - v;
+}
+
+constexpr int kSelectLds = 4096;  // largest page count selected from LDS
+
+// select_pages for N <= kSelectLds: the order keys are read once into LDS;
+// the radix passes run on LDS, and the ascending compaction gives thread t
+// the contiguous pages t*per .. t*per+per-1 (two block-wide scans place them).
+__device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max_pages,
+                                 int32_t* sel) {
+  __shared__ uint32_t s_keys[kSelectLds];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_kk;
+  __shared__ int lds4[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+#pragma unroll 8
+  for (int j = tid; j < N; j += kThreads) s_keys[j] = order_key(load_shared_f32(&scores[j]));
+  __syncthreads();
+
+  const bool take_all = (k >= N);
+  uint32_t prefix = 0, pmask = 0;
+  int kk = k;
+  if (!take_all && k > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;  // kThreads == 256 bins
+      __syncthreads();
+      for (int j = tid; j < N; j += kThreads) {
+        const uint32_t key = s_keys[j];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t local = h0 + h1 + h2 + h3;
+        uint32_t suf = local;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const uint32_t o = __shfl_down(suf, off, kWave);
+          if (lane + off < kWave) suf += o;
+        }
+        const uint64_t hit = __ballot(suf >= static_cast<uint32_t>(kk));
+        const int top = 63 - __clzll(hit);
+        if (lane == top) {
+          // the bin (4*lane + d) holding the kk-th largest key, scanning d = 3 .. 0
+          const uint32_t a3 = suf - local, a2 = a3 + h3, a1 = a2 + h2, a0 = a1 + h1;
+          const uint32_t need = static_cast<uint32_t>(kk);
+          const int d = (a3 + h3 >= need) ? 3 : (a2 + h2 >= need) ? 2 : (a1 + h1 >= need) ? 1 : 0;
+          const uint32_t above = (d == 3) ? a3 : (d == 2) ? a2 : (d == 1) ? a1 : a0;
+          s_digit = static_cast<uint32_t>(4 * lane + d);
+          s_kk = kk - static_cast<int>(above);
+        }
+      }
+      __syncthreads();
+      prefix |= s_digit << shift;
+      pmask |= 255u << shift;
+      kk = s_kk;
+      __syncthreads();
+    }
+  }
+  // prefix = key of the k-th largest score; the kk lowest-index pages with
+  // exactly that key are taken, with every page above it
+  const int per = (N + kThreads - 1) / kThreads;
+  const int jb = min(tid * per, N), je = min(jb + per, N);
+  const bool use_eq = !take_all && k > 0;
+  int n_gt = 0, n_eq = 0;
+  for (int j = jb; j < je; ++j) {
+    const uint32_t key = s_keys[j];
+    n_gt += (take_all || key > prefix) ? 1 : 0;
+    n_eq += (use_eq && key == prefix) ? 1 : 0;
+  }
+  int tot = 0;
+  const int eq_before = block_excl_sum(n_eq, &tot, lds4);
+  const int eq_take = min(max(kk - eq_before, 0), n_eq);
+  int pos = block_excl_sum(n_gt + eq_take, &tot, lds4);
+  int eq_rank = eq_before;
+  for (int j = jb; j < je; ++j) {
+    const uint32_t key = s_keys[j];
+    const bool gt = take_all || key > prefix;
+    const bool eq = use_eq && key == prefix;
+    const bool take = gt || (eq && eq_rank < kk);
+    eq_rank += eq ? 1 : 0;
+    if (take) {
+      if (pos < k_max) sel[pos] = j;
+      ++pos;
+    }
+  }
+  for (int i = k + tid; i < k_max; i += kThreads) sel[i] = -1;
+  for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
+}
+
+__device__ inline void select_top_pages(float* scores, int N, int k, int k_max, int max_pages,
+                                        int32_t* sel) {
+  if (N <= kSelectLds)
+    select_pages_lds(scores, N, k, k_max, max_pages, sel);
+  else
+    select_pages(scores, N, k, k_max, max_pages, sel);
+}
+
 // Scores of one 64-token row: acc[h] = q_hat_h . v + q_tilde_h . c per lane,
 // the group's projected queries broadcast from VGPRs (NQ = G*W/16).
 template <class S, int G, int RV, int RK, int NQ>
@@ -328,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
         k = min(k, k_max);
       }
-      select_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
+      select_top_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
       if (threadIdx.x == 0) {
         if (sel_counts) sel_counts[pair] = k;
         reset_ticket(&counters[pair]);

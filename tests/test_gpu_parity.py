@@ -228,3 +228,32 @@ def test_binding_reports_bad_launch_arguments():
     with pytest.raises(K.KvlrError):
         K.kvlr_decode_attn(s.shape, s.kcache, s.q, s.q_proj, s.seq_lens_dev, s.page_table,
                            s.max_pages, s.sel, None, s.k_max, 0.1, s.z, s.lse, s.workspace, 64, wl.batch)
+
+
+def test_long_sequence_selects_from_global_scores():
+    # more than 4096 pages in one sequence: the selection reads its scores from
+    # global memory instead of staging them
+    wl = make_wl(G=1, d=64, rv=16, rk=16, P=16, storage="bf16", routed=True, B=2, Hkv=1,
+                 topk=(1, 16))
+    _say("case long sequence", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=[70001, 300], append_per_seq=3)
+    out = run_and_check(sess, pairs=[(0, 0), (1, 0)])
+    assert -(-70001 // 16) > 4096
+    assert all(o.get("tie_band", 0) < 50 for o in out)
+
+
+def test_exact_ties_go_to_the_lowest_pages():
+    # zero queries make every page score exactly 0: the k lowest page indices win
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True, topk=(3, 8))
+    _say("case exact ties")
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=5)
+    sess.q.zero_()
+    sess.step()
+    torch.cuda.synchronize()
+    for b, L in enumerate(LENS):
+        N = -(-L // 64)
+        k = O.pages_to_keep(N, 3, 8)
+        for g in range(wl.num_kv_heads):
+            sel = sess.sel[b, g].cpu().numpy()
+            assert (sel[:k] == np.arange(k)).all() and (sel[k:] == -1).all()
+            assert int(sess.sel_counts[b, g]) == k
