@@ -24,6 +24,9 @@
 #ifndef KVLR_ROUTE_ROLLING
 #define KVLR_ROUTE_ROLLING 1
 #endif
+#ifndef KVLR_ROUTE_MFMA
+#define KVLR_ROUTE_MFMA 1
+#endif
 
 
 namespace kvlr {
@@ -31,6 +34,26 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 8 floats as bfloat16: hi = RNE(x), lo = RNE(x - hi); hi + lo carries about
+// 16 significant bits of x, so a product with a bf16 latent through the two
+// halves is exact to about 2^-18 relative.
+__device__ inline void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = f32_to_bf16_rne(x[2 * i]), h1 = f32_to_bf16_rne(x[2 * i + 1]);
+    const uint32_t l0 = f32_to_bf16_rne(x[2 * i] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(x[2 * i + 1] - __uint_as_float(h1 << 16));
+    h[i] = h0 | (h1 << 16);
+    l[i] = l0 | (l1 << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
 
 // Exclusive prefix count of `flag` over the workgroup in thread order; also
 // returns the total. Uses one LDS slot per wave; contains two barriers.
@@ -321,12 +344,101 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ qp = q_proj + static_cast<size_t>(b * Hq + g * G) * W;
     const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
     float* __restrict__ sc = scores + static_cast<size_t>(pair) * max_pages;
-    float qv[NQ];
-    load_q_rows(qp, qv);
+    // the vector-ALU paths keep the projected queries spread over the lanes
+    constexpr bool kMfma = ROWPAGE && S::CH == 8 && KVLR_ROUTE_MFMA;
+    float qv[kMfma ? 1 : NQ];
+    if constexpr (!kMfma) load_q_rows(qp, qv);
     const int row0 = split * rows_per_chunk;
     const int row1 = min(row0 + rows_per_chunk, nrows);
 
-    if constexpr (ROWPAGE) {
+    if constexpr (kMfma) {
+      // Matrix-core scoring (bf16 storage, one page per row). A 64-token row
+      // is four 16-token tiles; per tile, scores[token][head] = sum over the
+      // concatenated [v | c] latent (K, in steps of 32) of latent x query,
+      // as v_mfma_f32_16x16x32_bf16 with tokens as rows (lane l: token l%16,
+      // 8 latent elements from k-group l/16: one 16-byte chunk of the page)
+      // and heads as columns (the projected queries split into bf16 high and
+      // low halves, two products per step). Heads past the group and tokens
+      // past the sequence end are masked before the page max.
+      // k-steps: ceil(CV/4) over the value latent, then ceil(CK/4) over the
+      // residual, so each step reads one slab (a uniform base address)
+      constexpr int KSV = (CV + 3) / 4, KSK = (CK + 3) / 4, KS = KSV + KSK;
+      const int kq = lane >> 4, col = lane & 15;
+      bf16x8 qhi[KS], qlo[KS];
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const bool on_v = st < KSV;
+        const int ci = 4 * (on_v ? st : st - KSV) + kq;  // chunk within the slab
+        const bool have = col < G && ci < (on_v ? CV : CK);
+        const float* src = qp + col * W + (on_v ? 0 : RV) + ci * 8;
+        float x[8];
+        if (have) {
+          const float4 a = *reinterpret_cast<const float4*>(src);
+          const float4 c = *reinterpret_cast<const float4*>(src + 4);
+          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+          x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        split_bf16x8(x, qhi[st], qlo[st]);
+      }
+      // Past the slab's last chunk a lane re-reads chunk 0 (its query half is
+      // zero); past the last row every lane reads one shared address.
+      struct RowRef {
+        const uint8_t* vb;
+        const uint8_t* kb;
+        int on;  // 1 for a real row
+      };
+      auto row_ref = [&](int row) -> RowRef {
+        if (row >= row1) return RowRef{v_lat, k_lat, 0};
+        const size_t phys = static_cast<size_t>(pt[row]);
+        return RowRef{v_lat + (phys * Hkv + g) * slab_v, k_lat + (phys * Hkv + g) * slab_k, 1};
+      };
+      auto a_addr = [&](const RowRef& rr, int j, int st) -> const uint8_t* {
+        const bool on_v = st < KSV;
+        int ci = 4 * (on_v ? st : st - KSV) + kq;
+        if (ci >= (on_v ? CV : CK)) ci = 0;
+        const uint32_t off = static_cast<uint32_t>(rr.on) *
+                             static_cast<uint32_t>((j * 16 + col) * 16 + ci * (kWave * 16));
+        return (on_v ? rr.vb : rr.kb) + off;
+      };
+      int r = row0 + wave;
+      uint4 A[4][KS];
+      RowRef cur = row_ref(r);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int st = 0; st < KS; ++st) A[j][st] = load16_stream(a_addr(cur, j, st));
+      RowRef nxt = row_ref(r + kWaves);
+      for (; r < row1; r += kWaves) {
+        const RowRef nn = row_ref(r + 2 * kWaves);  // page-table entry two rows ahead
+        f32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < KS; ++st) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, A[j][st]);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[st], acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[st], acc[j], 0, 0, 0);
+            A[j][st] = load16_stream(a_addr(nxt, j, st));
+          }
+        }
+        const int nvalid = L - r * kWave;
+        float m = -__builtin_huge_valf();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const bool ok = col < G && (j * 16 + 4 * kq + v) < nvalid;
+            m = ok ? fmaxf(m, acc[j][v]) : m;
+          }
+        m = wave_max_u(m);
+        if (lane == 0) store_shared_f32(&sc[r], m);
+        nxt = nn;
+      }
+    } else if constexpr (ROWPAGE) {
       // one page per row: its page-table entry and base address are uniform
       auto row_base = [&](int row, const uint8_t*& vbase, const uint8_t*& kbase) -> bool {
         const size_t phys = static_cast<size_t>(pt[row]);
