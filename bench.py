@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_BENCH_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="up-projection inside the attention launch instead of its own")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -149,27 +151,28 @@ def main():
     log(f"[bench] staged in {time.time() - t0:.1f}s; KV tokens/step {sess.kv_tokens()}")
 
     stream = torch.cuda.current_stream()
-    dominant = "route" if wl.routed else "attn"
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
+    attend = sess.attend_upproject if args.fused else sess.attend
+
     def step(i=None):
-        sess.append()
-        sess.project_queries()
+        sess.prepare()
         if wl.routed:
             if i is not None:
                 ev[i][0].record(stream)
             sess.route()
             if i is not None:
                 ev[i][1].record(stream)
-            sess.attend()
+            attend()
         else:
             if i is not None:
                 ev[i][0].record(stream)
-            sess.attend()
+            attend()
             if i is not None:
                 ev[i][1].record(stream)
-        sess.upproject()
+        if not args.fused:
+            sess.upproject()
 
     for _ in range(args.warmup):
         step()

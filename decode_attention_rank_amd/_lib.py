@@ -29,7 +29,8 @@ KVLR_KEYS_EXACT = 1
 
 EXPORTED = (
     "kvlr_append_encode", "kvlr_project_queries", "kvlr_qproj_width", "kvlr_route_pages",
-    "kvlr_decode_attn", "kvlr_upproject", "kvlr_workspace_bytes", "kvlr_workspace_init",
+    "kvlr_decode_attn", "kvlr_decode_attn_upproject", "kvlr_upproject", "kvlr_workspace_bytes",
+    "kvlr_workspace_init",
     "kvlr_status_string", "kvlr_version",
 )
 
@@ -67,6 +68,9 @@ _SIG = {
                           _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_decode_attn": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I,
                           _P, _P, _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
+    "kvlr_decode_attn_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
+                                    ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _I,
+                                    ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I, _I], ctypes.c_size_t),
     "kvlr_workspace_init": ([_P, ctypes.c_size_t, _P], _I),
@@ -176,6 +180,16 @@ def kvlr_decode_attn(shape, cache, q, q_proj, seq_lens, page_table, max_pages_pe
         _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_counts), k_max,
         float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(workspace), ws_bytes, batch,
         _stream(stream)))
+
+
+def kvlr_decode_attn_upproject(shape, factors, cache, q, q_proj, seq_lens, page_table,
+                               max_pages_per_seq, sel_pages, sel_counts, k_max, softmax_scale,
+                               z_out, lse_out, o_out, workspace, ws_bytes, batch, stream=None):
+    _check("kvlr_decode_attn_upproject", lib().kvlr_decode_attn_upproject(
+        ctypes.byref(shape), ctypes.byref(factors), ctypes.byref(cache), _ptr(q), _ptr(q_proj),
+        _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_counts),
+        k_max, float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(o_out), _ptr(workspace),
+        ws_bytes, batch, _stream(stream)))
 
 
 def kvlr_upproject(shape, factors, z, o_out, batch, stream=None):

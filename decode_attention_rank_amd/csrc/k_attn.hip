@@ -51,8 +51,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const uint8_t* __restrict__ keys, const uint8_t* __restrict__ v_lat,
     const float* __restrict__ qsrc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_counts, float* __restrict__ partials, uint32_t* __restrict__ counters, float* __restrict__ z_out,
-    float* __restrict__ lse_out, int Hq, int Hkv, int P, int log2P, int max_pages, int k_max,
+    const int32_t* __restrict__ sel_counts, float* __restrict__ partials,
+    uint32_t* __restrict__ counters, float* __restrict__ z_out, float* __restrict__ lse_out,
+    const uint8_t* __restrict__ B_v, float* __restrict__ o_out, int Dh, int Hq, int Hkv, int P,
+    int log2P, int max_pages, int k_max,
     float scale_log2e, int rows_per_chunk, int max_splits, int batch) {
   constexpr int CH = S::CH;
   constexpr int CKW = KW / CH;     // key chunks per token
@@ -350,10 +352,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
           }
         }
         const int qh = g * G + h;
-        z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = (Ls > 0.f) ? Z / Ls : 0.f;
+        const float zv = (Ls > 0.f) ? Z / Ls : 0.f;
+        z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = zv;
+        s_z[0][h][e] = zv;
         if (e == 0 && lse_out) {
           lse_out[static_cast<size_t>(b) * Hq + qh] =
               (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
+        }
+      }
+      if (o_out) {
+        // value compression tied to the output projection: o_h = z_h B_v, once per head
+        __syncthreads();
+        const uint8_t* Bg = B_v + static_cast<size_t>(g) * RV * Dh * S::ELEM_BYTES;
+        for (int i = threadIdx.x; i < G * Dh; i += kThreads) {
+          const int h = i / Dh, d = i - h * Dh;
+          float acc = 0.f;
+#pragma unroll 8
+          for (int e = 0; e < RV; ++e) acc = fmaf(s_z[0][h][e], S::load1(Bg, static_cast<long>(e) * Dh + d), acc);
+          o_out[(static_cast<size_t>(b) * Hq + g * G + h) * Dh + d] = acc;
         }
       }
       if (threadIdx.x == 0) reset_ticket(&counters[pair]);
@@ -371,14 +387,16 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   if (a.dm.P == kWave)
     hipLaunchKernelGGL((attn_kernel<S, G, KW, RV, true>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
-                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials, a.counters, a.z_out,
-                       a.lse_out, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials,
+                       a.counters, a.z_out, a.lse_out, static_cast<const uint8_t*>(a.B_v), a.o_out,
+                       a.dm.D, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
                        a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
   else
     hipLaunchKernelGGL((attn_kernel<S, G, KW, RV, false>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
-                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials, a.counters, a.z_out,
-                       a.lse_out, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials,
+                       a.counters, a.z_out, a.lse_out, static_cast<const uint8_t*>(a.B_v), a.o_out,
+                       a.dm.D, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
                        a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
   return hipGetLastError();
 }

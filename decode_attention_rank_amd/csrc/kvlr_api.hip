@@ -239,12 +239,13 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   return hip_status(kvlr::launch_route(a, as_stream(stream)));
 }
 
-kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
-                             const float* q_proj, const int32_t* seq_lens,
-                             const int32_t* page_table, int32_t max_pages_per_seq,
-                             const int32_t* sel_pages, const int32_t* sel_counts, int32_t k_max,
-                             float softmax_scale, float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
-                             int32_t batch, void* stream) {
+static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors* factors,
+                                    const kvlr_cache* cache, const float* q, const float* q_proj,
+                                    const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t max_pages_per_seq, const int32_t* sel_pages,
+                                    const int32_t* sel_counts, int32_t k_max, float softmax_scale,
+                                    float* z_out, float* lse_out, float* o_out, void* workspace,
+                                    size_t ws_bytes, int32_t batch, void* stream) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
@@ -261,6 +262,7 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
   if (sel_counts && (!sel_pages || !aligned16(sel_counts))) return KVLR_ERR_INVALID_ARGUMENT;
   if (lse_out && !aligned16(lse_out)) return KVLR_ERR_INVALID_ARGUMENT;
   if (dm.exact && (!ok_ptr(cache->k_exact) || !ok_ptr(q))) return KVLR_ERR_INVALID_ARGUMENT;
+  if (o_out && (!factors || !ok_ptr(factors->B_v) || !aligned16(o_out))) return KVLR_ERR_INVALID_ARGUMENT;
   if (!dm.exact && (!ok_ptr(cache->k_lat) || !ok_ptr(q_proj))) return KVLR_ERR_INVALID_ARGUMENT;
   const Plan plan = plan_for(dm, batch, max_pages_per_seq);
   if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
@@ -282,6 +284,8 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.counters = reinterpret_cast<uint32_t*>(ws + plan.attn_cnt);
   a.z_out = z_out;
   a.lse_out = lse_out;
+  a.B_v = o_out ? factors->B_v : nullptr;
+  a.o_out = o_out;
   a.batch = batch;
   const int rows = attn_rows(sel_pages ? k_max : max_pages_per_seq, dm.P);
   a.rows_per_chunk = kvlr::attn_rows_per_chunk(sel_pages != nullptr);
@@ -290,6 +294,31 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
   const long long chunks = static_cast<long long>(batch) * dm.Hkv * a.max_splits;
   a.grid = static_cast<int>(chunks < kAttnGrid ? chunks : kAttnGrid);
   return hip_status(kvlr::launch_attn(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
+                             const float* q_proj, const int32_t* seq_lens,
+                             const int32_t* page_table, int32_t max_pages_per_seq,
+                             const int32_t* sel_pages, const int32_t* sel_counts, int32_t k_max,
+                             float softmax_scale, float* z_out, float* lse_out, void* workspace,
+                             size_t ws_bytes, int32_t batch, void* stream) {
+  return decode_attn_impl(shape, nullptr, cache, q, q_proj, seq_lens, page_table, max_pages_per_seq,
+                          sel_pages, sel_counts, k_max, softmax_scale, z_out, lse_out, nullptr,
+                          workspace, ws_bytes, batch, stream);
+}
+
+kvlr_status kvlr_decode_attn_upproject(const kvlr_shape* shape, const kvlr_factors* factors,
+                                       const kvlr_cache* cache, const float* q,
+                                       const float* q_proj, const int32_t* seq_lens,
+                                       const int32_t* page_table, int32_t max_pages_per_seq,
+                                       const int32_t* sel_pages, const int32_t* sel_counts,
+                                       int32_t k_max, float softmax_scale, float* z_out,
+                                       float* lse_out, float* o_out, void* workspace,
+                                       size_t ws_bytes, int32_t batch, void* stream) {
+  if (!o_out) return KVLR_ERR_INVALID_ARGUMENT;
+  return decode_attn_impl(shape, factors, cache, q, q_proj, seq_lens, page_table,
+                          max_pages_per_seq, sel_pages, sel_counts, k_max, softmax_scale, z_out,
+                          lse_out, o_out, workspace, ws_bytes, batch, stream);
 }
 
 kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors, const float* z,

@@ -61,6 +61,8 @@ struct AttnArgs {
   uint32_t* counters;    // [B * Hkv]
   float* z_out;
   float* lse_out;        // may be NULL
+  const void* B_v;       // with o_out: up-project z in the final merge
+  float* o_out;          // may be NULL
   int batch;
   int rows_per_chunk;    // 64-token rows per work chunk
   int max_splits;        // chunk slots per pair in the partials buffer

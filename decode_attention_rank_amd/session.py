@@ -169,16 +169,39 @@ class DecodeSession:
     def upproject(self, stream=None):
         K.kvlr_upproject(self.shape, self.kfactors, self.z, self.o, self.wl.batch, stream)
 
-    def decode(self, stream=None):
+    def prepare(self, stream=None):
+        """Append-encode and query projection of one step (one stream: a second
+        stream joined by events costs more than the projection it would hide)."""
+        self.append(stream)
         self.project_queries(stream)
+
+    def attend_upproject(self, stream=None):
+        """Attention with the up-projection applied in the same launch."""
+        use_sel = self.sel if self.wl.routed else None
+        use_counts = self.sel_counts if use_sel is not None else None
+        K.kvlr_decode_attn_upproject(self.shape, self.kfactors, self.kcache, self.q, self.q_proj,
+                                     self.seq_lens_dev, self.page_table, self.max_pages, use_sel,
+                                     use_counts, self.k_max if use_sel is not None else 0,
+                                     self.scale, self.z, self.lse, self.o, self.workspace,
+                                     self.ws_bytes, self.wl.batch, stream)
+
+    def finish(self, stream=None, fused=False):
+        """Routing (routed caches), attention and up-projection."""
         if self.wl.routed:
             self.route(stream)
-        self.attend(stream)
-        self.upproject(stream)
+        if fused:
+            self.attend_upproject(stream)
+        else:
+            self.attend(stream)
+            self.upproject(stream)
+
+    def decode(self, stream=None):
+        self.project_queries(stream)
+        self.finish(stream)
 
     def step(self, stream=None):
-        self.append(stream)
-        self.decode(stream)
+        self.prepare(stream)
+        self.finish(stream)
 
     # ------------------------------------------------------------------ metrics
     def kv_tokens(self) -> int:

@@ -211,6 +211,26 @@ kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, c
                              int32_t batch, void* stream);
 
 /*
+ * kvlr_decode_attn followed by the up-projection, in one launch. BasisKV
+ * English abstract and method details (key innovation): the value latent is
+ * tied to the output projection, so o_h = z_h . B_v[g] is applied once per
+ * query head, here by the workgroup that merges the head group's partials.
+ * Arguments as for kvlr_decode_attn, plus:
+ *   factors  B_v is read ([H_kv][rank_v][head_dim], storage type)
+ *   o_out    out [batch][num_q_heads][head_dim] float32 (required)
+ * z_out and lse_out are written as by kvlr_decode_attn. o equals what
+ * kvlr_upproject gives for the same z up to float32 summation order.
+ */
+kvlr_status kvlr_decode_attn_upproject(const kvlr_shape* shape, const kvlr_factors* factors,
+                                       const kvlr_cache* cache, const float* q,
+                                       const float* q_proj, const int32_t* seq_lens,
+                                       const int32_t* page_table, int32_t max_pages_per_seq,
+                                       const int32_t* sel_pages, const int32_t* sel_counts,
+                                       int32_t k_max, float softmax_scale, float* z_out,
+                                       float* lse_out, float* o_out, void* workspace,
+                                       size_t ws_bytes, int32_t batch, void* stream);
+
+/*
  * Up-projection, once per query head. BasisKV English abstract and method
  * details: value compression is tied to the output projection, so the
  * decoder B_v is applied to the attention-weighted latent z.

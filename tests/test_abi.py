@@ -121,6 +121,13 @@ def test_bad_arguments_are_rejected_before_launch(lib):
                                 fake, None, None, fake, 1 << 40, 5000, None) == K.KVLR_ERR_UNSUPPORTED
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
                                   fake, fake, fake, 512, 5000, 16, None) == K.KVLR_ERR_UNSUPPORTED
+    # the fused up-projection needs its output and the factors
+    assert lib.kvlr_decode_attn_upproject(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
+                                          fake, fake, 512, fake, None, 64, 0.1, fake, None, None, fake,
+                                          1 << 30, 16, None) == E
+    assert lib.kvlr_decode_attn_upproject(ctypes.byref(s), None, ctypes.byref(c2), fake, fake, fake,
+                                          fake, 512, fake, None, 64, 0.1, fake, None, fake, fake,
+                                          1 << 30, 16, None) == E
     # non-positive or non-finite softmax scale
     for sc in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512,

@@ -257,3 +257,19 @@ def test_exact_ties_go_to_the_lowest_pages():
             sel = sess.sel[b, g].cpu().numpy()
             assert (sel[:k] == np.arange(k)).all() and (sel[k:] == -1).all()
             assert int(sess.sel_counts[b, g]) == k
+
+
+@pytest.mark.parametrize("routed", [True, False])
+def test_fused_upprojection_matches_separate_calls(routed):
+    wl = make_wl(G=8, d=128, rv=32, rk=32 if routed else 16, P=64, storage="bf16", routed=routed)
+    _say("case fused up-projection", routed)
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=3)
+    s.prepare()
+    s.finish(fused=False)
+    torch.cuda.synchronize()
+    z1, l1, o1 = s.z.clone(), s.lse.clone(), s.o.clone()
+    s.o.fill_(float("nan"))
+    s.finish(fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s.z, z1) and torch.equal(s.lse, l1)
+    assert H.rel_err(H.f64(s.o), H.f64(o1)) < 1e-6
