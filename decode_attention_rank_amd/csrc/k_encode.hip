@@ -129,58 +129,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   const E* Av = reinterpret_cast<const E*>(A_v) + static_cast<size_t>(g) * D * RV;
   const E* Ak = reinterpret_cast<const E*>(A_k) + static_cast<size_t>(g) * D * RK;
 
-  // ---- stage B fragments: element (k, n) with k = ks*KSTEP + KPL*(l/16) + e,
-  // n = nt*16 + l%16; each thread reads CH consecutive n of one row k
-  auto stage = [&](const E* src, E* dst, int R) {
-    const int rc = R / CH;  // chunks per row
-    for (int idx = tid; idx < D * rc; idx += kThreads) {
-      const int k = idx / rc, n0 = (idx - k * rc) * CH;
-      float x[CH];
-      S::unpack(load16(src + static_cast<size_t>(k) * R + n0), x);
-      const int ks = k / KSTEP, kk = k - ks * KSTEP;
-#pragma unroll
-      for (int e2 = 0; e2 < CH; ++e2) {
-        const int n = n0 + e2;
-        const int l = (kk / KPL) * 16 + (n & 15);
-        dst[((static_cast<size_t>(ks) * (R / 16) + (n >> 4)) * kWave + l) * KPL + (kk % KPL)] =
-            MM::store(x[e2]);
-      }
-    }
-  };
-  stage(Av, &sm.av[0][0][0][0], RV);
-  stage(Ak, &sm.ak[0][0][0][0], RK);
-  for (int b = tid; b <= batch; b += kThreads) s_seq[b] = cu_new[b];
-  for (int b = tid; b < batch; b += kThreads) s_seq[batch + 1 + b] = lens_before[b];
-  __syncthreads();
-
-  if constexpr (ROUTED) {
-    // M = W_pred A_k  [RV x RK], one 16x16 tile per wave at a time
-    const uint8_t* Wg = W_pred + static_cast<size_t>(g) * RV * D * EB;
-    for (int ti = wave; ti < NTV * NTK; ti += kWaves) {
-      const int mt = ti / NTK, nt = ti - mt * NTK;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int row = mt * 16 + (lane & 15);
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) {
-        const frag_t a = MM::gmem(Wg + (static_cast<size_t>(row) * D + ks * KSTEP + KPL * (lane >> 4)) * EB);
-        acc = MM::mma(a, MM::lds(&sm.ak[ks][nt][lane][0]), acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.u.mstage[mt * 16 + 4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[i];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < KSV * NTK * kWave * KPL; idx += kThreads) {
-      const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTK;
-      const int ks = idx / (KPL * kWave * NTK);
-      const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
-      const float mv = (k < RV) ? -sm.u.mstage[k][n] : 0.f;
-      const E hi = MM::store(mv);
-      sm.mhi[ks][nt][l][e] = hi;
-      if constexpr (KPL > 1) sm.mlo[ks][nt][l][e] = MM::store(mv - MM::value(hi));
-    }
-    __syncthreads();
-  }
-
   const int ntiles = (total_new + 63) / 64;
   const int r = lane & 15;        // A-operand row (token) of this lane
   const int kq = lane >> 4;       // A-operand k group of this lane
@@ -198,6 +146,62 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) kf[ks] = MM::gmem(k_new + row_off + (ks * KSTEP + KPL * kq) * EB);
   };
+  // this workgroup's first tile, and the W_pred rows of M = W_pred A_k, are
+  // requested before the set-up below
+  frag_t vf[KSD], kf[KSD];
+  load_tile(blockIdx.x, vf, kf);
+  constexpr int MT = ROUTED ? (NTV * NTK + kWaves - 1) / kWaves : 0;  // M tiles per wave
+  frag_t wa[MT > 0 ? MT : 1][KSD];
+  if constexpr (ROUTED) {
+    const uint8_t* Wg = W_pred + static_cast<size_t>(g) * RV * D * EB;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int ti = wave + m * kWaves;
+      const int mt = (ti < NTV * NTK ? ti : 0) / NTK;
+      const int row = mt * 16 + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+        wa[m][ks] = MM::gmem(Wg + (static_cast<size_t>(row) * D + ks * KSTEP + KPL * (lane >> 4)) * EB);
+    }
+  }
+
+  // ---- stage B fragments: element (k, n) with k = ks*KSTEP + KPL*(l/16) + e,
+  // n = nt*16 + l%16; each thread reads CH consecutive n of one row k
+  auto stage = [&](const E* src, E* dst, auto rr) {
+    constexpr int R = decltype(rr)::value;
+    constexpr int RC = R / CH;                    // chunks per row
+    constexpr int NCHK = D * RC;                  // chunks of the factor
+    constexpr int IT = (NCHK + kThreads - 1) / kThreads;
+    uint4 buf[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {             // every load in flight first
+      const int idx = tid + it * kThreads;
+      const int k = idx / RC, n0 = (idx - k * RC) * CH;
+      buf[it] = (idx < NCHK) ? load16(src + static_cast<size_t>(k) * R + n0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + it * kThreads;
+      if (idx >= NCHK) continue;
+      const int k = idx / RC, n0 = (idx - k * RC) * CH;
+      float x[CH];
+      S::unpack(buf[it], x);
+      const int ks = k / KSTEP, kk = k - ks * KSTEP;
+#pragma unroll
+      for (int e2 = 0; e2 < CH; ++e2) {
+        const int n = n0 + e2;
+        const int l = (kk / KPL) * 16 + (n & 15);
+        dst[((static_cast<size_t>(ks) * (R / 16) + (n >> 4)) * kWave + l) * KPL + (kk % KPL)] =
+            MM::store(x[e2]);
+      }
+    }
+  };
+  stage(Av, &sm.av[0][0][0][0], std::integral_constant<int, RV>{});
+  stage(Ak, &sm.ak[0][0][0][0], std::integral_constant<int, RK>{});
+  for (int b = tid; b <= batch; b += kThreads) s_seq[b] = cu_new[b];
+  for (int b = tid; b < batch; b += kThreads) s_seq[batch + 1 + b] = lens_before[b];
+  __syncthreads();
+
   // sequence of token i: largest b with cu_new[b] <= i (offsets staged in LDS);
   // returns its page-table entry (entry 0 of sequence 0 past the last token)
   auto locate = [&](int tile, size_t& slot_off) -> const int32_t* {
@@ -213,6 +217,36 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     slot_off = static_cast<size_t>(pos & (P - 1)) * 16;
     return page_table + static_cast<size_t>(lo) * max_pages + (pos >> log2P);
   };
+  // the first tile's page-table entry is requested before M is formed
+  size_t slot0 = 0;
+  const int phys0 = *locate(blockIdx.x, slot0);
+
+  if constexpr (ROUTED) {
+    // M = W_pred A_k  [RV x RK], 16x16 tiles spread over the waves
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int ti = wave + m * kWaves;
+      if (ti >= NTV * NTK) continue;
+      const int mt = ti / NTK, nt = ti - mt * NTK;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) acc = MM::mma(wa[m][ks], MM::lds(&sm.ak[ks][nt][lane][0]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.u.mstage[mt * 16 + 4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[i];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < KSV * NTK * kWave * KPL; idx += kThreads) {
+      const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTK;
+      const int ks = idx / (KPL * kWave * NTK);
+      const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
+      const float mv = (k < RV) ? -sm.u.mstage[k][n] : 0.f;
+      const E hi = MM::store(mv);
+      sm.mhi[ks][nt][l][e] = hi;
+      if constexpr (KPL > 1) sm.mlo[ks][nt][l][e] = MM::store(mv - MM::value(hi));
+    }
+    __syncthreads();
+  }
+
   // one tile: multiply, round, store (latents via the wave's LDS tile)
   auto process = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
                      size_t slot_off) {
@@ -296,10 +330,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   };
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    frag_t vf[KSD], kf[KSD];
-    load_tile(tile, vf, kf);
-    size_t slot = 0;
-    const int phys = *locate(tile, slot);
+    size_t slot = slot0;
+    int phys = phys0;
+    if (tile != static_cast<int>(blockIdx.x)) {
+      load_tile(tile, vf, kf);
+      phys = *locate(tile, slot);
+    }
     process(tile, vf, kf, static_cast<size_t>(phys), slot);
   }
 }
