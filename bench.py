@@ -154,7 +154,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
-    attend = sess.attend_upproject if args.fused else sess.attend
+    attend = sess.attend_upproject if args.fused and wl.value_basis != "identity" else sess.attend
 
     def step(i=None):
         sess.prepare()
@@ -171,8 +171,8 @@ def main():
             attend()
             if i is not None:
                 ev[i][1].record(stream)
-        if not args.fused:
-            sess.upproject()
+        if not args.fused and wl.value_basis != "identity":
+            sess.upproject()  # the uncompressed reference stores values as they are: o = z
 
     for _ in range(args.warmup):
         step()

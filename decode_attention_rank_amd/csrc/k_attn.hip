@@ -419,6 +419,7 @@ hipError_t by_rv(const AttnArgs& a, hipStream_t s) {
     case 16: return by_kw<S, G, 16>(a, s);
     case 32: return by_kw<S, G, 32>(a, s);
     case 64: return by_kw<S, G, 64>(a, s);
+    case 128: return by_kw<S, G, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

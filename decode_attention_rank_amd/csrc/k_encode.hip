@@ -379,6 +379,10 @@ hipError_t by_rv(const EncodeArgs& a, hipStream_t s) {
     case 16: return by_rk<S, D, 16>(a, s);
     case 32: return by_rk<S, D, 32>(a, s);
     case 64: return by_rk<S, D, 64>(a, s);
+    case 128:
+      // full-width values: bf16 storage only (the f32 tiles would not fit in LDS)
+      if constexpr (D == 128 && S::CH == 8) return by_rk<S, D, 128>(a, s);
+      break;
   }
   return hipErrorInvalidValue;
 }

@@ -160,6 +160,7 @@ hipError_t up_by_rv(const UpprojArgs& a, hipStream_t s) {
     case 16: return up_by_d<S, 16>(a, s);
     case 32: return up_by_d<S, 32>(a, s);
     case 64: return up_by_d<S, 64>(a, s);
+    case 128: return up_by_d<S, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

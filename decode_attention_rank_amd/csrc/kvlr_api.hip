@@ -38,7 +38,10 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
   const int G = s->num_q_heads / s->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVLR_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return KVLR_ERR_UNSUPPORTED;
-  if (!one_of(s->rank_v, 16, 32, 64) || !one_of(s->rank_k, 16, 32, 64)) return KVLR_ERR_UNSUPPORTED;
+  // rank_v may be the full head_dim 128 (values stored uncompressed); rank_k <= 64
+  if (!(one_of(s->rank_v, 16, 32, 64) || s->rank_v == 128) || !one_of(s->rank_k, 16, 32, 64))
+    return KVLR_ERR_UNSUPPORTED;
+  if (s->rank_v == 128 && s->dtype != KVLR_DTYPE_BF16) return KVLR_ERR_UNSUPPORTED;
   if (!one_of(s->page_size, 16, 32, 64)) return KVLR_ERR_UNSUPPORTED;
   dm->Hq = s->num_q_heads;
   dm->Hkv = s->num_kv_heads;
@@ -199,6 +202,7 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
   if (!dm.exact) return KVLR_ERR_UNSUPPORTED;
+  if (dm.RV > 64) return KVLR_ERR_UNSUPPORTED;  // routing reads compressed value latents
   if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
   if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;

@@ -48,7 +48,7 @@ class DecodeSession:
         self.shape = K.make_shape(
             num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
             page_size=wl.page_size, rank_v=wl.rank_v, rank_k=wl.rank_k, dtype=kvlr_dtype(wl),
-            key_mode=K.KVLR_KEYS_EXACT if wl.routed else K.KVLR_KEYS_LATENT,
+            key_mode=K.KVLR_KEYS_EXACT if wl.exact else K.KVLR_KEYS_LATENT,
             num_phys_pages=num_phys)
         dev = self.device
         H, P = wl.num_kv_heads, wl.page_size
@@ -63,7 +63,7 @@ class DecodeSession:
         self.v_lat = layout.alloc_pages(num_phys, H, wl.rank_v, P, dt, dev, tail_fill)
         self.k_lat = layout.alloc_pages(num_phys, H, wl.rank_k, P, dt, dev, tail_fill)
         self.k_exact = (layout.alloc_pages(num_phys, H, wl.head_dim, P, dt, dev, tail_fill)
-                        if wl.routed else None)
+                        if wl.exact else None)
         self.kcache = K.make_cache(self.v_lat, self.k_lat, self.k_exact)
 
         # lengths and page table on the device
@@ -121,7 +121,7 @@ class DecodeSession:
         pages = self.page_table_cpu[b]
         layout.pack_sequence(self.v_lat, pages, rows["v"], tail_fill)
         layout.pack_sequence(self.k_lat, pages, rows["k_lat"], tail_fill)
-        if self.wl.routed:
+        if self.wl.exact:
             layout.pack_sequence(self.k_exact, pages, rows["k_exact"], tail_fill)
 
     def read_rows(self, b: int, L: int | None = None, start: int = 0) -> dict:
@@ -129,7 +129,7 @@ class DecodeSession:
         pages = self.page_table_cpu[b]
         out = {"v": layout.unpack_sequence(self.v_lat, pages, L, start),
                "k_lat": layout.unpack_sequence(self.k_lat, pages, L, start)}
-        if self.wl.routed:
+        if self.wl.exact:
             out["k_exact"] = layout.unpack_sequence(self.k_exact, pages, L, start)
         return out
 
@@ -173,7 +173,8 @@ class DecodeSession:
         """Append-encode and query projection of one step (one stream: a second
         stream joined by events costs more than the projection it would hide)."""
         self.append(stream)
-        self.project_queries(stream)
+        if self.needs_qproj:
+            self.project_queries(stream)
 
     def attend_upproject(self, stream=None):
         """Attention with the up-projection applied in the same launch."""
@@ -195,8 +196,15 @@ class DecodeSession:
             self.attend(stream)
             self.upproject(stream)
 
+    @property
+    def needs_qproj(self) -> bool:
+        """Projected queries feed routing and latent-key scoring; exact keys
+        attended without routing use the queries as they are."""
+        return self.wl.routed or not self.wl.exact
+
     def decode(self, stream=None):
-        self.project_queries(stream)
+        if self.needs_qproj:
+            self.project_queries(stream)
         self.finish(stream)
 
     def step(self, stream=None):
@@ -217,7 +225,8 @@ class DecodeSession:
         wl = self.wl
         eb = torch.empty(0, dtype=self.dtype).element_size()
         if not wl.routed:
-            return sum(self.seq_lens) * wl.num_kv_heads * (wl.rank_k + wl.rank_v) * eb
+            key = wl.head_dim if wl.exact else wl.rank_k
+            return sum(self.seq_lens) * wl.num_kv_heads * (key + wl.rank_v) * eb
         tot = 0
         P = wl.page_size
         for L in self.seq_lens:
@@ -230,5 +239,5 @@ class DecodeSession:
         wl = self.wl
         eb = torch.empty(0, dtype=self.dtype).element_size()
         read = self.total_new * wl.num_kv_heads * 2 * wl.head_dim * eb
-        write = self.total_new * wl.num_kv_heads * (wl.rank_v + wl.rank_k + (wl.head_dim if wl.routed else 0)) * eb
+        write = self.total_new * wl.num_kv_heads * (wl.rank_v + wl.rank_k + (wl.head_dim if wl.exact else 0)) * eb
         return read + write

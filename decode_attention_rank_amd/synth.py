@@ -6,7 +6,9 @@ path and the CPU oracle consume what it produces.
 
 Recipe (per KV head g; all draws seeded by (workload seed, role, sequence)):
   * Two orthonormal bases Q_v[g], Q_k[g] of R^d (QR of a seeded Gaussian,
-    float64 on the host, signs fixed so the R diagonal is positive).
+    float64 on the host, signs fixed so the R diagonal is positive). With
+    value_basis "identity" Q_v is the identity, so full-rank value factors
+    store the values themselves (the uncompressed reference).
   * Signal coefficients per token: C ~ N(0,1) of width signal_rank for V;
     key coefficients kc = [C[:, :shared_rank], E] with E ~ N(0,1), so the
     first shared_rank key coordinates are carried by the value (the part a
@@ -74,6 +76,8 @@ def bases(wl: Workload):
         sign = torch.sign(torch.diagonal(r, dim1=-2, dim2=-1))
         sign[sign == 0] = 1.0
         out.append(q * sign.unsqueeze(-2))
+    if wl.value_basis == "identity":
+        out[0] = torch.eye(d, dtype=torch.float64).expand(wl.num_kv_heads, d, d).clone()
     return out[0], out[1]
 
 
@@ -83,7 +87,7 @@ def make_factors(wl: Workload, device="cpu"):
     Qv, Qk = bases(wl)
     H, d, rv, rk, ns = wl.num_kv_heads, wl.head_dim, wl.rank_v, wl.rank_k, wl.shared_rank
     A_v = Qv[:, :, :rv]
-    if wl.routed:
+    if wl.exact:
         if ns > rv or ns + rk > d:
             raise ValueError("shared_rank must fit in rank_v and shared_rank + rank_k in head_dim")
         W = torch.zeros(H, rv, d, dtype=torch.float64)
@@ -191,7 +195,7 @@ def synth_latent_cache(wl: Workload, b: int, n: int, device="cpu", *, q=None, Qk
     dt = storage_dtype(wl)
     v = torch.empty(H, n, rv, dtype=dt, device=device)
     kl = torch.empty(H, n, rk, dtype=dt, device=device)
-    ke = torch.empty(H, n, d, dtype=dt, device=device) if wl.routed else None
+    ke = torch.empty(H, n, d, dtype=dt, device=device) if wl.exact else None
     for g in range(H):
         C, kc = _coefficients(wl, b, g, 0, n, device, Qk, q)
         gen = _gen(device, wl.seed, "noise", b, g)
@@ -200,16 +204,16 @@ def synth_latent_cache(wl: Workload, b: int, n: int, device="cpu", *, q=None, Qk
         vv[:, :m] += C[:, :m]
         v[g] = vv.to(dt)
         kk = s * torch.randn(n, rk, generator=gen, device=device)
-        src = kc[:, ns:] if wl.routed else kc
+        src = kc[:, ns:] if wl.exact else kc
         m = min(src.shape[1], rk)
         kk[:, :m] += src[:, :m]
         kl[g] = kk.to(dt)
-        if wl.routed:
+        if wl.exact:
             basis = Qk[g, :, :rs].to(torch.float32).to(device)
             K = kc @ basis.T.contiguous() + s * torch.randn(n, d, generator=gen, device=device)
             ke[g] = K.to(dt)
     out = {"v": v, "k_lat": kl}
-    if wl.routed:
+    if wl.exact:
         out["k_exact"] = ke
     return out
 

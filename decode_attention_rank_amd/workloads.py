@@ -32,6 +32,8 @@ class Workload:
     planted_boost: float = 0.0  # shift, in coefficient standard deviations
     append_per_seq: int = 1     # tokens each sequence appends in one step
     ragged: bool = False        # lognormal per-sequence contexts
+    route: bool = True          # exact keys: route (True) or attend every page (False)
+    value_basis: str = "random"  # "identity": the value latent is the value itself
     ctx_min: int = 0
     ctx_max: int = 0
     seed: int = 0
@@ -41,8 +43,13 @@ class Workload:
         return self.num_q_heads // self.num_kv_heads
 
     @property
-    def routed(self) -> bool:
+    def exact(self) -> bool:
+        """Original keys are kept (and attention scores them exactly)."""
         return self.key_mode == "exact"
+
+    @property
+    def routed(self) -> bool:
+        return self.exact and self.route
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -82,6 +89,13 @@ WORKLOADS = {
         key_mode="exact", context=0, topk_num=1, topk_den=8,
         signal_rank=48, shared_rank=32, noise_std=0.05, append_per_seq=4096,
         ragged=True, ctx_min=4096, ctx_max=131072, seed=4),
+    # Uncompressed reference at the 8B shapes: original keys and full-width
+    # values (identity value factors), every page attended.
+    "llama3-8b-uncompressed-32k": Workload(
+        name="llama3-8b-uncompressed-32k", batch=16, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, page_size=64, rank_v=128, rank_k=16, storage="bf16",
+        key_mode="exact", context=32768, route=False, value_basis="identity",
+        signal_rank=48, shared_rank=16, noise_std=0.05, seed=5),
 }
 
 DEFAULT_BENCH_WORKLOAD = "llama3-8b-routed-32k"

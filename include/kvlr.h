@@ -53,8 +53,10 @@
  *
  * Query-head h belongs to KV head h / G, G = num_q_heads / num_kv_heads.
  * Supported: head_dim in {64, 128}; rank_v, rank_k in {16, 32, 64} and
- * <= head_dim; page_size in {16, 32, 64}; G in {1, 2, 4, 8};
- * max_pages_per_seq <= 65536; batch <= 4096.
+ * <= head_dim, and rank_v = 128 with bf16 storage (values kept at full
+ * width: the uncompressed reference, attended without routing);
+ * page_size in {16, 32, 64};
+ * G in {1, 2, 4, 8}; max_pages_per_seq <= 65536; batch <= 4096.
  * Other values return KVLR_ERR_UNSUPPORTED.
  */
 #ifndef KVLR_H
@@ -174,6 +176,7 @@ int32_t kvlr_qproj_width(const kvlr_shape* shape);
  *                leaves it ready for the next one. Calls sharing one
  *                workspace must not overlap.
  * Scores are unscaled; NaN inputs give an unspecified selection.
+ * rank_v above 64 returns KVLR_ERR_UNSUPPORTED.
  */
 kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
                              const int32_t* seq_lens, const int32_t* page_table,

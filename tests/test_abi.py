@@ -68,6 +68,7 @@ def test_qproj_width_and_workspace_size(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), K.KVLR_ERR_UNSUPPORTED),
     (dict(rank_v=48), K.KVLR_ERR_UNSUPPORTED),
+    (dict(rank_v=128, dtype=K.KVLR_DTYPE_F32), K.KVLR_ERR_UNSUPPORTED),    # full width: bf16 only
     (dict(page_size=128), K.KVLR_ERR_UNSUPPORTED),
     (dict(num_q_heads=48, num_kv_heads=3), K.KVLR_ERR_UNSUPPORTED),   # G = 16
     (dict(num_q_heads=30), K.KVLR_ERR_INVALID_ARGUMENT),              # not a multiple
@@ -132,6 +133,10 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     for sc in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512,
                                     fake, None, 64, sc, fake, None, fake, 1 << 30, 16, None) == E
+    # routing reads compressed value latents
+    assert lib.kvlr_route_pages(ctypes.byref(_shape(rank_v=128)), ctypes.byref(c2), fake, fake, fake,
+                                512, 1, 8, 64, fake, None, None, fake, 1 << 30, 16,
+                                None) == K.KVLR_ERR_UNSUPPORTED
     # routing needs the routed (exact-key) cache
     sl = _shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)
     assert lib.kvlr_route_pages(ctypes.byref(sl), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,

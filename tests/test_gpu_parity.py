@@ -27,15 +27,19 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def make_wl(*, G, d, rv, rk, P, storage, routed, B=4, Hkv=2, topk=(1, 8), seed=11, planted=0.0):
+def make_wl(*, G, d, rv, rk, P, storage, routed, B=4, Hkv=2, topk=(1, 8), seed=11, planted=0.0,
+            exact=None, value_basis="random"):
+    exact = routed if exact is None else exact
     rs = min(48, d // 2)
-    ns = min(rv, rs // 2, d - rk) if routed else 0
+    ns = min(rv, rs // 2, d - rk) if exact else 0
+    mode = ("routed" if routed else "exact-all") if exact else "latent"
     return Workload(
-        name=f"t-G{G}-d{d}-rv{rv}-rk{rk}-P{P}-{storage}-{'exact' if routed else 'latent'}",
+        name=f"t-G{G}-d{d}-rv{rv}-rk{rk}-P{P}-{storage}-{mode}",
         batch=B, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, page_size=P, rank_v=rv,
-        rank_k=rk, storage=storage, key_mode="exact" if routed else "latent", context=0,
+        rank_k=rk, storage=storage, key_mode="exact" if exact else "latent", context=0,
         topk_num=topk[0], topk_den=topk[1], signal_rank=rs, shared_rank=ns, noise_std=0.05,
-        planted_frac=planted, planted_boost=4.0 if planted else 0.0, seed=seed)
+        planted_frac=planted, planted_boost=4.0 if planted else 0.0, seed=seed,
+        route=routed, value_basis=value_basis)
 
 
 def run_and_check(sess, pairs=None, stage=True):
@@ -273,3 +277,27 @@ def test_fused_upprojection_matches_separate_calls(routed):
     torch.cuda.synchronize()
     assert torch.equal(s.z, z1) and torch.equal(s.lse, l1)
     assert H.rel_err(H.f64(s.o), H.f64(o1)) < 1e-6
+
+
+UNCOMPRESSED = [
+    dict(G=4, d=128, rv=128, rk=16, P=64),
+    dict(G=8, d=128, rv=128, rk=32, P=32),
+    dict(G=2, d=64, rv=64, rk=16, P=16),
+]
+
+
+@pytest.mark.parametrize("cfg", UNCOMPRESSED, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_uncompressed_reference(cfg):
+    # original keys, values at full width (identity factors), every page attended:
+    # plain paged attention, checked against the oracle like the compressed paths
+    wl = make_wl(routed=False, exact=True, value_basis="identity", storage="bf16", **cfg)
+    _say("case", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    run_and_check(sess)
+    # the stored value latents are the values themselves
+    b = 1
+    rows = sess.read_rows(b)
+    off = sum(sess.n_new[:b])
+    n = sess.n_new[b]
+    assert torch.equal(rows["v"][:, sess.lens_before[b]:].cpu(),
+                       sess.v_new[off:off + n].transpose(0, 1).cpu())

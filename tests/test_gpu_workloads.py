@@ -18,7 +18,7 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 FULL = ["llama3-8b-dense-32k", "llama3-8b-routed-32k", "llama3-70b-share-routed-128k",
-        "mixed-append-routed-ragged"]
+        "mixed-append-routed-ragged", "llama3-8b-uncompressed-32k"]
 
 
 def _sample(sess):
