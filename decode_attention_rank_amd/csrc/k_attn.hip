@@ -27,6 +27,9 @@
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
 
+#ifndef KVLR_ATTN_MFMA
+#define KVLR_ATTN_MFMA 1
+#endif
 #ifndef KVLR_ATTN_ROWS_SELECTED
 #define KVLR_ATTN_ROWS_SELECTED 16
 #endif
@@ -47,7 +50,7 @@ __device__ inline void wave_lds_sync() {
 }
 
 template <class S, int G, int KW, int RV, bool ROWPAGE>
-__global__ __launch_bounds__(kThreads) void attn_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(
     const uint8_t* __restrict__ keys, const uint8_t* __restrict__ v_lat,
     const float* __restrict__ qsrc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ sel,
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const float* __restrict__ qg = qsrc + static_cast<size_t>(b * Hq + g * G) * KW;
     const int row0 = split * rows_per_chunk;
     const int row1 = min(row0 + rows_per_chunk, nrows);
+    constexpr bool kMfma = ROWPAGE && S::CH == 8 && KVLR_ATTN_MFMA;
 
     float m[G], lsum[G], z[G][CH];
 #pragma unroll
@@ -164,7 +168,172 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
       });
     };
 
-    if constexpr (ROWPAGE) {
+    if constexpr (kMfma) {
+      // Matrix-core scores (bf16 storage, one page per row): a 64-token row is
+      // four 16-token tiles, scores[token][head] from v_mfma_f32_16x16x32_bf16
+      // with tokens as rows (lane l: token l%16, one 16-byte key chunk from
+      // k-group l/16) and heads as columns (the queries split into bf16 high
+      // and low halves, two products per step; exact to about 2^-18 relative).
+      // Lane l then holds head l%16's scores of tokens 16j + 4(l/16) + v. The
+      // row max per head comes from two cross-lane steps; the running max and
+      // rescale stay wave-uniform per head, each lane keeps a partial sum of
+      // its own probabilities, and P.V runs as in the vector path.
+      constexpr int KS = (CKW + 3) / 4;  // k-steps of 32 key elements
+      const int kq = lane >> 4, col = lane & 15;
+      // the query halves, one 16-byte fragment per (k-step, half, lane), live
+      // in the wave's LDS slice and are read once per k-step of a row
+      __shared__ uint4 s_qf[kWaves][KS][2][kWave];
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const int ci = 4 * st + kq;
+        float x[8];
+        if (col < G && ci < CKW) {
+          const float* src = qg + col * KW + ci * 8;
+          const float4 a0 = *reinterpret_cast<const float4*>(src);
+          const float4 a1 = *reinterpret_cast<const float4*>(src + 4);
+          x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+          x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        bf16x8 hi, lo;
+        split_bf16x8(x, hi, lo);
+        s_qf[wave][st][0][lane] = __builtin_bit_cast(uint4, hi);
+        s_qf[wave][st][1][lane] = __builtin_bit_cast(uint4, lo);
+      }
+      wave_lds_sync();
+      auto page_of = [&](int row) -> int {
+        if (row >= row1) return -1;
+        const int pg = sl ? sl[row] : row;
+        return (pg >= 0 && pg < N) ? pg : -1;
+      };
+      // past the last row every lane reads one shared address (on = 0);
+      // past the last key chunk a lane re-reads chunk 0 (its query half is zero)
+      struct RowRef {
+        const uint8_t* kb;
+        const uint8_t* vb;
+        int on, nvalid;
+      };
+      auto row_ref = [&](int pg) -> RowRef {
+        if (pg < 0) return RowRef{keys, v_lat, 0, 0};
+        const size_t ph = static_cast<size_t>(pt[pg]);
+        return RowRef{keys + (ph * Hkv + g) * slab_k,
+                      v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * 16, 1,
+                      min(L - pg * kWave, kWave)};
+      };
+      auto a_addr = [&](const RowRef& rr, int j, int st) -> const uint8_t* {
+        int ci = 4 * st + kq;
+        if (ci >= CKW) ci = 0;
+        return rr.kb + static_cast<uint32_t>(rr.on) *
+                           static_cast<uint32_t>((j * 16 + col) * 16 + ci * (kWave * 16));
+      };
+      auto v_addr = [&](const RowRef& rr, int k) -> const uint8_t* {
+        return rr.vb + static_cast<uint32_t>(rr.on) * static_cast<uint32_t>((lane / CV + k * TPL) * 16);
+      };
+      int r = row0 + wave;
+      uint4 A[4][KS], vc[CV];
+      RowRef cur = row_ref(page_of(r));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int st = 0; st < KS; ++st) A[j][st] = load16_stream(a_addr(cur, j, st));
+#pragma unroll
+      for (int k = 0; k < CV; ++k) vc[k] = load16_stream(v_addr(cur, k));
+      RowRef nxt = row_ref(page_of(r + kWaves));
+      int pg2 = page_of(r + 2 * kWaves);
+      float lcol = 0.f;  // sum of this lane's probabilities of head col
+      for (; r < row1; r += kWaves) {
+        // table lookups run ahead: physical page two rows on, page id three rows on
+        const RowRef nn = row_ref(pg2);
+        const int pg3 = page_of(r + 3 * kWaves);
+        f32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const bf16x8 qhi = __builtin_bit_cast(bf16x8, s_qf[wave][st][0][lane]);
+          const bf16x8 qlo = __builtin_bit_cast(bf16x8, s_qf[wave][st][1][lane]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, A[j][st]);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo, acc[j], 0, 0, 0);
+            A[j][st] = load16_stream(a_addr(nxt, j, st));
+          }
+        }
+        // scaled score of (token 16j + 4kq + v, head col), -inf when masked
+        auto score = [&](int j, int v) -> float {
+          const bool ok = col < G && (j * 16 + 4 * kq + v) < cur.nvalid;
+          return ok ? acc[j][v] * scale_log2e : kNegInf;
+        };
+        float rm = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) rm = fmaxf(rm, score(j, v));
+        rm = fmaxf(rm, __shfl_xor(rm, 16, kWave));
+        rm = fmaxf(rm, __shfl_xor(rm, 32, kWave));
+        bool any = false;
+        float mcol = kNegInf, acol = 1.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rm), h));
+          const float mn = fmaxf(m[h], mx);
+          const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
+          any = any || (mn != kNegInf);
+          m[h] = mn;
+#pragma unroll
+          for (int e = 0; e < CH; ++e) z[h][e] *= alpha;
+          if (col == h) {
+            mcol = mn;
+            acol = alpha;
+          }
+        }
+        lcol *= acol;
+        if (any) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float sc = score(j, v);
+              const float pv = (sc == kNegInf) ? 0.f : fast_exp2(sc - mcol);
+              lcol += pv;
+              if (col < G) s_p[wave][j * 16 + 4 * kq + v][col] = pv;
+            }
+          wave_lds_sync();
+        }
+#pragma unroll
+        for (int k = 0; k < CV; ++k) {
+          const int tok = lane / CV + k * TPL;
+          if (any) {
+            float x[CH];
+            S::unpack(vc[k], x);
+            const bool tv = tok < cur.nvalid;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float pp = s_p[wave][tok][h];
+#pragma unroll
+              for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, tv ? x[e] : 0.f, z[h][e]);
+            }
+          }
+          vc[k] = load16_stream(v_addr(nxt, k));
+        }
+        if (any) wave_lds_sync();
+        cur = nxt;
+        nxt = nn;
+        pg2 = pg3;
+      }
+      // per-head probability sums: lanes col, col+16, col+32, col+48 hold
+      // disjoint tokens; lane 0 carries each total into the reduction below
+      lcol += __shfl_xor(lcol, 16, kWave);
+      lcol += __shfl_xor(lcol, 32, kWave);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lcol), h));
+        lsum[h] = (lane == 0) ? t : 0.f;
+      }
+    } else if constexpr (ROWPAGE) {
       // One page per row: page id and physical page are wave-uniform. Each
       // key or value register is re-requested with the next row's data as
       // soon as this row has used it, so a wave always has a row in flight.

@@ -15,7 +15,6 @@
 namespace kvlr {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One 16 x 16 output tile of  out[r, n] = sum_k a[r, k] w(k, n)  on the float32
 // matrix cores (v_mfma_f32_16x16x4_f32), one wave per tile. Rows r are the

@@ -51,6 +51,26 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 8 floats as bfloat16: hi = RNE(x), lo = RNE(x - hi); hi + lo carries about
+// 16 significant bits of x, so a product with a bf16 latent through the two
+// halves is exact to about 2^-18 relative.
+__device__ inline void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = f32_to_bf16_rne(x[2 * i]), h1 = f32_to_bf16_rne(x[2 * i + 1]);
+    const uint32_t l0 = f32_to_bf16_rne(x[2 * i] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(x[2 * i + 1] - __uint_as_float(h1 << 16));
+    h[i] = h0 | (h1 << 16);
+    l[i] = l0 | (l1 << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
 __device__ inline uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
