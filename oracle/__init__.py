@@ -23,4 +23,7 @@ from .kvlr_oracle import (  # noqa: F401
     upproject,
     decode_pair,
     attend_selected,
+    output_projection,
+    fold_output_weights,
+    latent_output_projection,
 )

@@ -304,3 +304,44 @@ def decode_pair(q_group, state, factors, L: int, P: int, *, key_mode: str,
         raise ValueError(f"unknown key mode {key_mode!r}")
     z, o, lse = attend_selected(q, state, factors, L, P, sel, key_mode=key_mode, scale=scale)
     return {"sel": sel, "scores": S, "z": z, "o": o, "lse": lse}
+
+
+# ----------------------------------------------------------------------------
+# Output projection (BasisKV English abstract and method details, key
+# innovation: the value latent is tied to the output projection, so one
+# low-rank value representation narrows both the value cache and what the
+# attention output carries)
+# ----------------------------------------------------------------------------
+
+def output_projection(o, W_o):
+    """Plain attention output through the output projection.
+
+    o: [n_heads, d] per-head outputs of one sequence (o_h = z_h B_v[g(h)]).
+    W_o: [hidden, n_heads * d], rows are output features (the usual
+    "out x in" layout). Returns [hidden] = W_o . concat_h(o_h).
+    """
+    o = np.asarray(o, np.float64).reshape(-1)
+    return np.asarray(W_o, np.float64) @ o
+
+
+def fold_output_weights(B_v_heads, W_o):
+    """F = W_o . blockdiag(B_v^T): the output projection seen from the latents.
+
+    B_v_heads: [n_heads, r_v, d], the up-projection of each query head's KV
+    head. W_o: [hidden, n_heads * d]. Returns F [hidden, n_heads * r_v] with
+    F[:, h r_v + e] = sum_j W_o[:, h d + j] B_v[h][e, j], so that
+    F . concat_h(z_h) = W_o . concat_h(z_h B_v[h]) for every z.
+    """
+    B = np.asarray(B_v_heads, np.float64)
+    W = np.asarray(W_o, np.float64)
+    n_heads, r_v, d = B.shape
+    cols = []
+    for h in range(n_heads):
+        W_h = W[:, h * d:(h + 1) * d]          # [hidden, d]
+        cols.append(W_h @ B[h].T)             # [hidden, r_v]
+    return np.concatenate(cols, axis=1)
+
+
+def latent_output_projection(z, F):
+    """[hidden] = F . concat_h(z_h) for one sequence (z: [n_heads, r_v])."""
+    return np.asarray(F, np.float64) @ np.asarray(z, np.float64).reshape(-1)

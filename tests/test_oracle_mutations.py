@@ -99,3 +99,14 @@ def test_wrong_k_rounding_is_caught(monkeypatch):
         return 0 if N <= 0 else min(N, max(1, (N * num) // den))
     _patch(monkeypatch, "pages_to_keep", wrong)
     _fails(pins.test_pages_to_keep, 9, 1, 8, 2)
+
+
+def test_untransposed_fold_is_caught(monkeypatch):
+    # folding with B_v instead of its transpose (it runs when r_v = d)
+    def bad(B_v_heads, W_o):
+        B = np.asarray(B_v_heads, np.float64)
+        W = np.asarray(W_o, np.float64)
+        n, _, d = B.shape
+        return np.concatenate([W[:, h * d:(h + 1) * d] @ B[h] for h in range(n)], axis=1)
+    _patch(monkeypatch, "fold_output_weights", bad)
+    _fails(pins.test_fold_equals_library_linear_of_upprojected_outputs, 16)

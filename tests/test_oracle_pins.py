@@ -385,3 +385,49 @@ def test_golden_worked_example():
         np.testing.assert_allclose(np.exp(res["lse"]), exp[key]["lse_exp"], rtol=1e-12)
     res = O.decode_pair(q, routed, f, L, P, key_mode="exact", scale=scale, topk=(1, 3))
     np.testing.assert_allclose(np.exp(res["scores"]), exp["routed_k1"]["scores_exp"], rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Output projection and its fold onto the value latents
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r_v", [8, 16])
+def test_fold_equals_library_linear_of_upprojected_outputs(r_v):
+    rng = np.random.default_rng(21)
+    n_heads, d, hidden = 6, 16, 40
+    B_v = rng.standard_normal((n_heads, r_v, d))
+    W_o = rng.standard_normal((hidden, n_heads * d))
+    z = rng.standard_normal((n_heads, r_v))
+    # library path: o_h = z_h B_v[h] by torch matmul, then nn.functional.linear
+    zt = torch.from_numpy(z).unsqueeze(1)                       # [H, 1, r_v]
+    o = torch.bmm(zt, torch.from_numpy(B_v).contiguous()).reshape(1, -1)
+    ref = torch.nn.functional.linear(o, torch.from_numpy(W_o)).reshape(-1).numpy()
+    F = O.fold_output_weights(B_v, W_o)
+    assert F.shape == (hidden, n_heads * r_v)
+    np.testing.assert_allclose(O.latent_output_projection(z, F), ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.output_projection(o.numpy().reshape(n_heads, d), W_o), ref,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_fold_with_identity_upprojection_is_the_output_weight():
+    rng = np.random.default_rng(22)
+    n_heads, d, hidden = 3, 8, 12
+    B_v = np.stack([np.eye(d)] * n_heads)
+    W_o = rng.standard_normal((hidden, n_heads * d))
+    np.testing.assert_array_equal(O.fold_output_weights(B_v, W_o), W_o)
+
+
+def test_fold_column_is_one_latent_direction():
+    # a unit latent e_(h, e) is carried by column h*r_v + e of F, which is the
+    # output weight applied to row e of that head's up-projection
+    rng = np.random.default_rng(23)
+    n_heads, d, r_v, hidden = 4, 8, 4, 10
+    B_v = rng.standard_normal((n_heads, r_v, d))
+    W_o = rng.standard_normal((hidden, n_heads * d))
+    F = O.fold_output_weights(B_v, W_o)
+    for h in range(n_heads):
+        for e in range(r_v):
+            col = np.zeros(hidden)
+            for n in range(hidden):
+                col[n] = sum(W_o[n, h * d + j] * B_v[h, e, j] for j in range(d))
+            np.testing.assert_allclose(F[:, h * r_v + e], col, rtol=1e-12, atol=1e-12)
