@@ -123,6 +123,29 @@ def _oracle_pair(wl, scale, it):
     O.upproject(res["z"], f["B_v"])
 
 
+def time_output_projection(sess, reps: int = 50):
+    """The folded output projection F . z (F = W_o blockdiag(B_v^T)), timed on
+    its own after the steps: it reads F ([hidden][H_q r_v] bf16) once."""
+    sess.prepare_output_projection()
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        sess.output_projection()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        sess.output_projection()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    wl = sess.wl
+    f_bytes = sess.F.numel() * sess.F.element_size()
+    w_bytes = sess.W_o.numel() * sess.W_o.element_size()
+    gbps = f_bytes / (us * 1e-6) / 1e9
+    return {"kernel": "oproj_kernel", "hidden": sess.hidden, "avg_launch_us": round(us, 2),
+            "folded_weight_bytes": f_bytes, "unfolded_weight_bytes": w_bytes,
+            "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +246,8 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": roof,
     }
+    if wl.storage == "bf16":
+        out["output_projection"] = time_output_projection(sess)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(sess, args.cpu_budget)

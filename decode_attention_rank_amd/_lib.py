@@ -30,7 +30,7 @@ KVLR_KEYS_EXACT = 1
 EXPORTED = (
     "kvlr_append_encode", "kvlr_project_queries", "kvlr_qproj_width", "kvlr_route_pages",
     "kvlr_decode_attn", "kvlr_decode_attn_upproject", "kvlr_upproject", "kvlr_workspace_bytes",
-    "kvlr_workspace_init",
+    "kvlr_workspace_init", "kvlr_fold_output_weights", "kvlr_output_projection",
     "kvlr_status_string", "kvlr_version",
 )
 
@@ -73,6 +73,9 @@ _SIG = {
                                     ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I, _I], ctypes.c_size_t),
+    "kvlr_fold_output_weights": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _I,
+                                  _P, _P], _I),
+    "kvlr_output_projection": ([ctypes.POINTER(kvlr_shape), _P, _P, _I, _P, _I, _P], _I),
     "kvlr_workspace_init": ([_P, ctypes.c_size_t, _P], _I),
     "kvlr_status_string": ([_I], ctypes.c_char_p),
     "kvlr_version": ([], _I),
@@ -195,3 +198,13 @@ def kvlr_decode_attn_upproject(shape, factors, cache, q, q_proj, seq_lens, page_
 def kvlr_upproject(shape, factors, z, o_out, batch, stream=None):
     _check("kvlr_upproject", lib().kvlr_upproject(
         ctypes.byref(shape), ctypes.byref(factors), _ptr(z), _ptr(o_out), batch, _stream(stream)))
+
+
+def kvlr_fold_output_weights(shape, factors, W_o, hidden, F_out, stream=None):
+    _check("kvlr_fold_output_weights", lib().kvlr_fold_output_weights(
+        ctypes.byref(shape), ctypes.byref(factors), _ptr(W_o), hidden, _ptr(F_out), _stream(stream)))
+
+
+def kvlr_output_projection(shape, F, z, hidden, out, batch, stream=None):
+    _check("kvlr_output_projection", lib().kvlr_output_projection(
+        ctypes.byref(shape), _ptr(F), _ptr(z), hidden, _ptr(out), batch, _stream(stream)))

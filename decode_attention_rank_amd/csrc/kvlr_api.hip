@@ -342,4 +342,40 @@ kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors,
   return hip_status(kvlr::launch_upproject(a, as_stream(stream)));
 }
 
+kvlr_status kvlr_fold_output_weights(const kvlr_shape* shape, const kvlr_factors* factors,
+                                     const void* W_o, int32_t hidden, void* F_out, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (dm.dtype != KVLR_DTYPE_BF16) return KVLR_ERR_UNSUPPORTED;
+  if (!factors || hidden < 16 || hidden % 16 != 0 || hidden > (1 << 20)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(factors->B_v) || !ok_ptr(W_o) || !ok_ptr(F_out)) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::FoldArgs a{};
+  a.dm = dm;
+  a.W_o = W_o;
+  a.B_v = factors->B_v;
+  a.F = F_out;
+  a.hidden = hidden;
+  return hip_status(kvlr::launch_fold(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_output_projection(const kvlr_shape* shape, const void* F, const float* z,
+                                   int32_t hidden, float* out, int32_t batch, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (dm.dtype != KVLR_DTYPE_BF16) return KVLR_ERR_UNSUPPORTED;
+  if (batch < 0 || hidden < 16 || hidden % 16 != 0 || hidden > (1 << 20)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return KVLR_OK;
+  if (!ok_ptr(F) || !ok_ptr(z) || !ok_ptr(out)) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::OprojArgs a{};
+  a.dm = dm;
+  a.F = F;
+  a.z = z;
+  a.out = out;
+  a.hidden = hidden;
+  a.batch = batch;
+  return hip_status(kvlr::launch_oproj(a, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -80,6 +80,25 @@ struct UpprojArgs {
 };
 hipError_t launch_upproject(const UpprojArgs& a, hipStream_t s);
 
+struct FoldArgs {
+  Dims dm;
+  const void* W_o;  // [hidden][Hq * D] bf16
+  const void* B_v;  // [Hkv][RV][D] bf16
+  void* F;          // [hidden][Hq * RV] bf16
+  int hidden;
+};
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+
+struct OprojArgs {
+  Dims dm;
+  const void* F;    // [hidden][Hq * RV] bf16
+  const float* z;   // [B][Hq][RV]
+  float* out;       // [B][hidden]
+  int hidden;
+  int batch;
+};
+hipError_t launch_oproj(const OprojArgs& a, hipStream_t s);
+
 struct EncodeArgs {
   Dims dm;
   const void* A_v;

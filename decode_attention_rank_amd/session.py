@@ -211,6 +211,21 @@ class DecodeSession:
         self.prepare(stream)
         self.finish(stream)
 
+    # ------------------------------------------------------------ output side
+    def prepare_output_projection(self):
+        """Draws W_o and folds it onto the value latents (F = W_o blockdiag(B_v^T))."""
+        wl = self.wl
+        self.hidden = synth.output_width(wl)
+        self.W_o = synth.make_output_weight(wl, self.device)
+        self.F = torch.empty(self.hidden, wl.num_q_heads * wl.rank_v, dtype=self.dtype,
+                             device=self.device)
+        self.out = torch.empty(wl.batch, self.hidden, dtype=torch.float32, device=self.device)
+        K.kvlr_fold_output_weights(self.shape, self.kfactors, self.W_o, self.hidden, self.F)
+
+    def output_projection(self, stream=None):
+        K.kvlr_output_projection(self.shape, self.F, self.z, self.hidden, self.out, self.wl.batch,
+                                 stream)
+
     # ------------------------------------------------------------------ metrics
     def kv_tokens(self) -> int:
         return sum(self.seq_lens)

@@ -26,6 +26,8 @@ Recipe (per KV head g; all draws seeded by (workload seed, role, sequence)):
     Q_k[:, shared_rank:shared_rank + rank_k], B_k = A_k^T. Dense:
     A_k = Q_k[:, :rank_k], B_k = A_k^T. Rounded to the storage type.
   * Queries q ~ N(0, 1/d) per coordinate, float32.
+  * Output projection W_o [hidden][H_q d] ~ N(0, 1/(H_q d)), in the storage
+    type (hidden = H_q d unless the workload names its share's width).
   * Planted pages (routing signal): a seeded fraction of each sequence's
     pages get their key coefficients (and the shared value coefficients)
     shifted by boost * u, u the unit vector of Q_k[:, :rs]^T q_bar, q_bar the
@@ -45,7 +47,7 @@ import torch
 from .workloads import Workload
 
 _ROLE = {"bases": 1, "q": 2, "coef": 3, "noise": 4, "lens": 5, "planted": 6,
-         "pages": 7, "raw": 8}
+         "pages": 7, "raw": 8, "oproj": 9}
 
 TORCH_STORAGE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -111,6 +113,20 @@ def make_queries(wl: Workload, device="cpu") -> torch.Tensor:
     g = _gen("cpu", wl.seed, "q")
     q = torch.randn(wl.batch, wl.num_q_heads, wl.head_dim, generator=g, dtype=torch.float64)
     return (q / math.sqrt(wl.head_dim)).to(torch.float32).to(device)
+
+
+def output_width(wl: Workload) -> int:
+    """Output features of the attention layer (the head share's row count of W_o)."""
+    return wl.hidden if wl.hidden else wl.num_q_heads * wl.head_dim
+
+
+def make_output_weight(wl: Workload, device="cpu") -> torch.Tensor:
+    """Output projection W_o [hidden][H_q * d] in the storage type, entries
+    N(0, 1 / (H_q d)) (seeded)."""
+    g = _gen("cpu", wl.seed, "oproj")
+    n_in = wl.num_q_heads * wl.head_dim
+    W = torch.randn(output_width(wl), n_in, generator=g, dtype=torch.float64) / math.sqrt(n_in)
+    return W.to(storage_dtype(wl)).to(device)
 
 
 def make_seq_lens(wl: Workload) -> list[int]:

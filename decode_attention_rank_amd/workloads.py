@@ -34,6 +34,7 @@ class Workload:
     ragged: bool = False        # lognormal per-sequence contexts
     route: bool = True          # exact keys: route (True) or attend every page (False)
     value_basis: str = "random"  # "identity": the value latent is the value itself
+    hidden: int = 0             # output features of W_o (0: num_q_heads * head_dim)
     ctx_min: int = 0
     ctx_max: int = 0
     seed: int = 0
@@ -80,7 +81,7 @@ WORKLOADS = {
         head_dim=128, page_size=64, rank_v=32, rank_k=32, storage="bf16",
         key_mode="exact", context=131072, topk_num=1, topk_den=16,
         signal_rank=48, shared_rank=32, noise_std=0.05,
-        planted_frac=0.05, planted_boost=4.0, seed=3),
+        planted_frac=0.05, planted_boost=4.0, hidden=8192, seed=3),
     # Mixed: every sequence appends a 4096-token chunk (encoded on append),
     # then one routed decode over ragged lognormal contexts.
     "mixed-append-routed-ragged": Workload(

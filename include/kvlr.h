@@ -257,6 +257,33 @@ const char* kvlr_status_string(kvlr_status status);
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
 int32_t kvlr_version(void);
 
+/*
+ * Output projection seen from the value latents. BasisKV English abstract and
+ * method details (key innovation): value compression is tied to the output
+ * projection, so the same low-rank value representation narrows both the
+ * value cache and what the attention output carries. With o_h = z_h . B_v,
+ *   W_o . concat_h(o_h) = F . concat_h(z_h),  F = W_o . blockdiag_h(B_v^T).
+ * bf16 storage only (other types return KVLR_ERR_UNSUPPORTED).
+ *
+ * kvlr_fold_output_weights forms F once (a weight preparation):
+ *   W_o    [hidden][num_q_heads * head_dim] bf16, rows are output features
+ *   F_out  out [hidden][num_q_heads * rank_v] bf16 (RNE of float32 sums of
+ *          exact bf16 products)
+ *   hidden host; a positive multiple of 16, at most 2^20
+ */
+kvlr_status kvlr_fold_output_weights(const kvlr_shape* shape, const kvlr_factors* factors,
+                                     const void* W_o, int32_t hidden, void* F_out, void* stream);
+
+/*
+ * kvlr_output_projection applies F to a batch of latent outputs:
+ *   out[b] = F . z[b],  z [batch][num_q_heads][rank_v] float32 (read as one
+ *   row of num_q_heads * rank_v), out [batch][hidden] float32.
+ * z enters as bf16 high and low halves (about 16 significant bits), sums are
+ * float32.
+ */
+kvlr_status kvlr_output_projection(const kvlr_shape* shape, const void* F, const float* z,
+                                   int32_t hidden, float* out, int32_t batch, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -164,3 +164,20 @@ def test_python_binding_raises(lib):
     with pytest.raises(K.KvlrError) as ei:
         K.kvlr_upproject(_shape(head_dim=96), K.make_factors(), None, None, 1)
     assert ei.value.status == K.KVLR_ERR_UNSUPPORTED
+
+
+def test_output_projection_arguments(lib):
+    s = _shape()
+    f = K.make_factors()
+    fake = 1 << 20
+    E = K.KVLR_ERR_INVALID_ARGUMENT
+    assert lib.kvlr_fold_output_weights(ctypes.byref(s), ctypes.byref(f), fake, 4096, fake, None) == E
+    f2 = K.make_factors(B_v=fake)
+    assert lib.kvlr_fold_output_weights(ctypes.byref(s), ctypes.byref(f2), fake, 4090, fake, None) == E
+    assert lib.kvlr_fold_output_weights(ctypes.byref(s), ctypes.byref(f2), None, 4096, fake, None) == E
+    assert lib.kvlr_output_projection(ctypes.byref(s), fake, fake, 4096, fake, -1, None) == E
+    assert lib.kvlr_output_projection(ctypes.byref(s), fake, fake, 0, fake, 4, None) == E
+    assert lib.kvlr_output_projection(ctypes.byref(s), fake, fake, 4096, fake, 0, None) == 0
+    sf = _shape(dtype=K.KVLR_DTYPE_F32)
+    assert lib.kvlr_output_projection(ctypes.byref(sf), fake, fake, 4096, fake, 4, None) == \
+        K.KVLR_ERR_UNSUPPORTED

@@ -301,3 +301,45 @@ def test_uncompressed_reference(cfg):
     n = sess.n_new[b]
     assert torch.equal(rows["v"][:, sess.lens_before[b]:].cpu(),
                        sess.v_new[off:off + n].transpose(0, 1).cpu())
+
+
+@pytest.mark.parametrize("cfg", [dict(G=4, d=128, rv=64, rk=32, P=64, B=5),
+                                 dict(G=8, d=128, rv=32, rk=32, P=64, B=3),
+                                 dict(G=2, d=64, rv=16, rk=16, P=16, B=20, hidden=208)],
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_output_projection_fold(cfg):
+    # F = W_o blockdiag(B_v^T) formed on the GPU, then applied to the step's z;
+    # checked against the oracle's plain output projection of its own outputs
+    # (hidden 208 = 13 output tiles: an odd count for the 32-column tiles)
+    cfg = dict(cfg)
+    hidden = cfg.pop("hidden", 0)
+    wl = make_wl(routed=True, storage="bf16", **cfg).scaled(hidden=hidden)
+    _say("case output projection", wl.name)
+    lens = [777, 1, 640, 2049, 65] * 4
+    s = DecodeSession(wl, "cuda", seq_lens=lens[:wl.batch], append_per_seq=3)
+    s.step()
+    s.prepare_output_projection()
+    s.output_projection()
+    torch.cuda.synchronize()
+    G, Hq = wl.group, wl.num_q_heads
+    Bv = np.stack([H.f64(s.factors["B_v"][h // G]) for h in range(Hq)])
+    Wo = H.f64(s.W_o)
+    F_ref = O.fold_output_weights(Bv, Wo)
+    # F: one bf16 rounding of a float32 sum of exact products, so within one
+    # bf16 unit of the exact value plus the float32 accumulation bound
+    acc_bound = wl.head_dim * 2.0 ** -24 * O.fold_output_weights(np.abs(Bv), np.abs(Wo))
+    Fg = H.f64(s.F)
+    assert np.all(np.abs(Fg - F_ref) <= H.bf16_ulp(np.abs(F_ref)) + acc_bound)
+    for b in range(wl.batch):
+        z = []
+        for g in range(wl.num_kv_heads):
+            st = H.oracle_state(s, b, g)
+            f = H.factors_np(s, g)
+            pages = [int(j) for j in s.sel[b, g].cpu().numpy() if j >= 0]
+            zz, _, _ = O.attend_selected(H.q_group(s, b, g), st, f, s.seq_lens[b], wl.page_size,
+                                         pages, key_mode=wl.key_mode, scale=s.scale)
+            z.append(zz)
+        z = np.concatenate(z)  # [Hq, r_v]
+        o = np.stack([O.upproject(z[h], Bv[h]) for h in range(Hq)])
+        ref = O.output_projection(o, Wo)
+        assert H.rel_err(H.f64(s.out[b]), ref) <= H.OUT_TOL
