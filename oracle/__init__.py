@@ -26,4 +26,5 @@ from .kvlr_oracle import (  # noqa: F401
     output_projection,
     fold_output_weights,
     latent_output_projection,
+    fit_factors,
 )

@@ -345,3 +345,51 @@ def fold_output_weights(B_v_heads, W_o):
 def latent_output_projection(z, F):
     """[hidden] = F . concat_h(z_h) for one sequence (z: [n_heads, r_v])."""
     return np.asarray(F, np.float64) @ np.asarray(z, np.float64).reshape(-1)
+
+
+# ----------------------------------------------------------------------------
+# Factor fitting from sample keys and values of one KV head (BasisKV English
+# abstract: low-rank K/V projections; the value latent predicts part of the
+# key, a key-specific residual holds the rest; method details, key design).
+# The pages do not give the fitting procedure; this is the plainest staged
+# reading: principal directions of the values, least-squares prediction of
+# the keys from the value latents, principal directions of what is left.
+# ----------------------------------------------------------------------------
+
+def _top_eigvecs(C, r):
+    """Eigenvectors of the symmetric C for its r largest eigenvalues, largest
+    first; each column's entry of largest magnitude made positive."""
+    w, U = np.linalg.eigh(np.asarray(C, np.float64))
+    order = np.argsort(w)[::-1][:r]
+    w, U = w[order], U[:, order]
+    for i in range(r):
+        j = np.argmax(np.abs(U[:, i]))
+        if U[j, i] < 0:
+            U[:, i] = -U[:, i]
+    return w, U
+
+
+def fit_factors(K, V, r_v: int, r_k: int, *, key_mode: str):
+    """Factors of one KV head from n sample keys and values ([n, d] each).
+
+    A_v: top-r_v eigenvectors of V^T V; B_v = A_v^T.
+    exact (routed) keys: W_pred = argmin_W |K - v W|^2 with v = V A_v, i.e.
+      (v^T v)^-1 v^T K; A_k: top-r_k eigenvectors of R^T R, R = K - v W_pred.
+    latent keys: A_k: top-r_k eigenvectors of K^T K; no W_pred.
+    B_k = A_k^T. Returns dict of float64 arrays and the eigenvalues.
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    lam_v, A_v = _top_eigvecs(V.T @ V, r_v)
+    out = {"A_v": A_v, "B_v": A_v.T.copy(), "lam_v": lam_v}
+    if key_mode == "exact":
+        v = V @ A_v
+        W = np.linalg.solve(v.T @ v, v.T @ K)
+        R = K - v @ W
+        lam_k, A_k = _top_eigvecs(R.T @ R, r_k)
+        out["W_pred"] = W
+    else:
+        lam_k, A_k = _top_eigvecs(K.T @ K, r_k)
+        out["W_pred"] = None
+    out.update(A_k=A_k, B_k=A_k.T.copy(), lam_k=lam_k)
+    return out

@@ -110,3 +110,24 @@ def test_untransposed_fold_is_caught(monkeypatch):
         return np.concatenate([W[:, h * d:(h + 1) * d] @ B[h] for h in range(n)], axis=1)
     _patch(monkeypatch, "fold_output_weights", bad)
     _fails(pins.test_fold_equals_library_linear_of_upprojected_outputs, 16)
+
+
+def test_fit_residual_taken_from_the_keys_is_caught(monkeypatch):
+    # principal directions of K instead of the prediction's residual
+    good = K.fit_factors
+
+    def bad(Kx, Vx, r_v, r_k, *, key_mode):
+        out = good(Kx, Vx, r_v, r_k, key_mode=key_mode)
+        lam, A = K._top_eigvecs(np.asarray(Kx, np.float64).T @ np.asarray(Kx, np.float64), r_k)
+        out.update(A_k=A, B_k=A.T.copy(), lam_k=lam)
+        return out
+    _patch(monkeypatch, "fit_factors", bad)
+    _fails(pins.test_fit_residual_basis_is_the_residual_principal_subspace)
+
+
+def test_fit_smallest_directions_is_caught(monkeypatch):
+    def bad_top(C, r):
+        w, U = np.linalg.eigh(np.asarray(C, np.float64))
+        return w[:r], U[:, :r]
+    monkeypatch.setattr(K, "_top_eigvecs", bad_top)
+    _fails(pins.test_fit_value_basis_is_the_top_right_singular_subspace)

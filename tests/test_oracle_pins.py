@@ -431,3 +431,78 @@ def test_fold_column_is_one_latent_direction():
             for n in range(hidden):
                 col[n] = sum(W_o[n, h * d + j] * B_v[h, e, j] for j in range(d))
             np.testing.assert_allclose(F[:, h * r_v + e], col, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Factor fitting
+# ----------------------------------------------------------------------------
+
+def _fit_data(rng, n=600, d=16, rs=6, ns=3, noise=0.01):
+    """Values of rank rs (distinct scales) plus noise; keys share ns of the
+    value coefficients and carry rs - ns of their own."""
+    Qv, Qk = _orth(rng, d), _orth(rng, d)
+    scale = 1.0 + 0.7 * np.arange(rs)[::-1]
+    C = rng.standard_normal((n, rs)) * scale
+    E = rng.standard_normal((n, rs - ns)) * (1.0 + 0.5 * np.arange(rs - ns)[::-1])
+    V = C @ Qv[:, :rs].T + noise * rng.standard_normal((n, d))
+    K = np.concatenate([C[:, :ns], E], axis=1) @ Qk[:, :rs].T + noise * rng.standard_normal((n, d))
+    return K, V
+
+
+def test_fit_value_basis_is_the_top_right_singular_subspace():
+    rng = np.random.default_rng(31)
+    K, V = _fit_data(rng)
+    f = O.fit_factors(K, V, 6, 4, key_mode="exact")
+    _, _, Vt = np.linalg.svd(V, full_matrices=False)   # library routine
+    P_ref = Vt[:6].T @ Vt[:6]
+    np.testing.assert_allclose(f["A_v"] @ f["A_v"].T, P_ref, atol=1e-9)
+    np.testing.assert_allclose(f["A_v"].T @ f["A_v"], np.eye(6), atol=1e-12)
+    np.testing.assert_allclose(f["B_v"], f["A_v"].T)
+
+
+def test_fit_prediction_is_least_squares():
+    rng = np.random.default_rng(32)
+    K, V = _fit_data(rng)
+    f = O.fit_factors(K, V, 6, 4, key_mode="exact")
+    v = V @ f["A_v"]
+    W_ls, *_ = np.linalg.lstsq(v, K, rcond=None)         # library routine
+    np.testing.assert_allclose(f["W_pred"], W_ls, atol=1e-9)
+
+
+def test_fit_residual_basis_is_the_residual_principal_subspace():
+    rng = np.random.default_rng(33)
+    K, V = _fit_data(rng)
+    f = O.fit_factors(K, V, 6, 3, key_mode="exact")
+    R = K - (V @ f["A_v"]) @ f["W_pred"]
+    _, _, Vt = np.linalg.svd(R, full_matrices=False)
+    np.testing.assert_allclose(f["A_k"] @ f["A_k"].T, Vt[:3].T @ Vt[:3], atol=1e-9)
+    # the residual of the prediction is orthogonal to the value latents
+    np.testing.assert_allclose((V @ f["A_v"]).T @ R, 0, atol=1e-8)
+
+
+def test_fit_recovers_an_exact_structure():
+    # noise-free: values of rank r_v; keys = shared part through a known map plus
+    # a part of rank r_k orthogonal to it -> prediction and residual are exact
+    rng = np.random.default_rng(34)
+    n, d, rv, rk = 400, 12, 4, 3
+    Q = _orth(rng, d)
+    C = rng.standard_normal((n, rv)) * np.array([4.0, 3.0, 2.0, 1.0])
+    V = C @ Q[:, :rv].T
+    M = rng.standard_normal((rv, d))
+    E = rng.standard_normal((n, rk)) * np.array([3.0, 2.0, 1.0])
+    K = C @ M + E @ Q[:, rv:rv + rk].T
+    f = O.fit_factors(K, V, rv, rk, key_mode="exact")
+    v = V @ f["A_v"]
+    R = K - v @ f["W_pred"]
+    # what the latents predict plus the rank-r_k residual reconstruct K exactly
+    np.testing.assert_allclose(v @ f["W_pred"] + (R @ f["A_k"]) @ f["B_k"], K, atol=1e-9)
+    np.testing.assert_allclose(f["A_v"] @ f["A_v"].T @ V.T, V.T, atol=1e-9)
+
+
+def test_fit_latent_mode_uses_key_principal_directions():
+    rng = np.random.default_rng(35)
+    K, V = _fit_data(rng)
+    f = O.fit_factors(K, V, 6, 5, key_mode="latent")
+    assert f["W_pred"] is None
+    _, _, Vt = np.linalg.svd(K, full_matrices=False)
+    np.testing.assert_allclose(f["A_k"] @ f["A_k"].T, Vt[:5].T @ Vt[:5], atol=1e-9)
