@@ -146,6 +146,50 @@ def time_output_projection(sess, reps: int = 50):
             "achieved_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def time_factor_fit(reps: int = 10):
+    """The factor fit on its calibration workload: the GPU moments call
+    (moments_mfma_kernel plus the fixed-order float64 sum of its per-run
+    partials) timed with HIP events, and the whole synchronous
+    kvlr_fit_factors call (moments, copy to host, float64 eigen-solves,
+    factor writes) by wall clock."""
+    from decode_attention_rank_amd import synth
+    from decode_attention_rank_amd.fit import FactorFit
+    from decode_attention_rank_amd.workloads import DEFAULT_FIT_WORKLOAD, FIT_WORKLOADS
+
+    wl = FIT_WORKLOADS[DEFAULT_FIT_WORKLOAD]
+    n = synth.fit_sample_count(wl)
+    H, d = wl.num_kv_heads, wl.head_dim
+    k, v = synth.make_fit_samples(wl, n, device="cuda")
+    fit = FactorFit(wl, n)
+    moments = torch.empty(H, 3, d, d, dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+    fit.fit(k, v)
+    for _ in range(3):
+        fit.moments(k, v, n, moments, 0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fit.moments(k, v, n, moments, 0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    t0 = time.perf_counter()
+    for _ in range(3):
+        fit.fit(k, v)
+    fit_ms = (time.perf_counter() - t0) * 1e3 / 3
+    algo = 2 * n * H * d * k.element_size() + H * 3 * d * d * 8
+    flops = 2.0 * n * H * 3 * d * d
+    gbps = algo / (us * 1e-6) / 1e9
+    del k, v
+    return {"workload": wl.name, "samples_per_kv_head": n, "num_kv_heads": H, "head_dim": d,
+            "rank_v": wl.rank_v, "rank_k": wl.rank_k, "storage": wl.storage,
+            "kernel": "moments_mfma_kernel", "moments_call_us": round(us, 2),
+            "algo_bytes_per_call": algo, "achieved_gbps": round(gbps, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "fit_factors_call_ms": round(fit_ms, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +198,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_BENCH_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fit", action="store_true", help="skip the factor-fit measurement")
     ap.add_argument("--fused", action="store_true",
                     help="up-projection inside the attention launch instead of its own")
     args = ap.parse_args()
@@ -248,6 +293,9 @@ def main():
     }
     if wl.storage == "bf16":
         out["output_projection"] = time_output_projection(sess)
+    if not args.no_fit:
+        log("[bench] timing the factor fit")
+        out["factor_fit"] = time_factor_fit()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(sess, args.cpu_budget)

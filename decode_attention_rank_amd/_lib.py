@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 LIB_PATH = os.environ.get("KVLR_LIBRARY") or os.path.join(
@@ -21,6 +22,7 @@ KVLR_ERR_INVALID_ARGUMENT = 1
 KVLR_ERR_UNSUPPORTED = 2
 KVLR_ERR_WORKSPACE_TOO_SMALL = 3
 KVLR_ERR_HIP = 4
+KVLR_ERR_NUMERICAL = 5
 
 KVLR_DTYPE_BF16 = 0
 KVLR_DTYPE_F32 = 1
@@ -31,7 +33,8 @@ EXPORTED = (
     "kvlr_append_encode", "kvlr_project_queries", "kvlr_qproj_width", "kvlr_route_pages",
     "kvlr_decode_attn", "kvlr_decode_attn_upproject", "kvlr_upproject", "kvlr_workspace_bytes",
     "kvlr_workspace_init", "kvlr_fold_output_weights", "kvlr_output_projection",
-    "kvlr_status_string", "kvlr_version",
+    "kvlr_status_string", "kvlr_version", "kvlr_fit_workspace_bytes", "kvlr_fit_moments",
+    "kvlr_fit_solve", "kvlr_fit_factors",
 )
 
 
@@ -52,6 +55,10 @@ class kvlr_cache(ctypes.Structure):
 
 
 class kvlr_factors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("A_v", "B_v", "A_k", "B_k", "W_pred")]
+
+
+class kvlr_factor_buffers(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("A_v", "B_v", "A_k", "B_k", "W_pred")]
 
 
@@ -79,6 +86,11 @@ _SIG = {
     "kvlr_workspace_init": ([_P, ctypes.c_size_t, _P], _I),
     "kvlr_status_string": ([_I], ctypes.c_char_p),
     "kvlr_version": ([], _I),
+    "kvlr_fit_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I], ctypes.c_size_t),
+    "kvlr_fit_moments": ([ctypes.POINTER(kvlr_shape), _P, _P, _I, _P, _I, _P, ctypes.c_size_t, _P], _I),
+    "kvlr_fit_solve": ([ctypes.POINTER(kvlr_shape), _P, _P, _P, _P, _P, _P], _I),
+    "kvlr_fit_factors": ([ctypes.POINTER(kvlr_shape), _P, _P, _I, ctypes.POINTER(kvlr_factor_buffers),
+                          _P, _P, _P, ctypes.c_size_t, _P], _I),
 }
 
 
@@ -103,7 +115,21 @@ def _ptr(x):
         return None
     if isinstance(x, torch.Tensor):
         return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
     return int(x)
+
+
+def _host_f64(x, name):
+    """A host float64 C-contiguous array (numpy or CPU tensor), or None."""
+    if x is None:
+        return None
+    ok = (isinstance(x, np.ndarray) and x.dtype == np.float64 and x.flags["C_CONTIGUOUS"]) or (
+        isinstance(x, torch.Tensor) and x.device.type == "cpu" and x.dtype == torch.float64
+        and x.is_contiguous())
+    if not ok:
+        raise TypeError(f"{name} must be a C-contiguous host float64 array")
+    return x
 
 
 def _stream(stream):
@@ -208,3 +234,32 @@ def kvlr_fold_output_weights(shape, factors, W_o, hidden, F_out, stream=None):
 def kvlr_output_projection(shape, F, z, hidden, out, batch, stream=None):
     _check("kvlr_output_projection", lib().kvlr_output_projection(
         ctypes.byref(shape), _ptr(F), _ptr(z), hidden, _ptr(out), batch, _stream(stream)))
+
+
+def make_factor_buffers(A_v=None, B_v=None, A_k=None, B_k=None, W_pred=None) -> kvlr_factor_buffers:
+    return kvlr_factor_buffers(_ptr(A_v), _ptr(B_v), _ptr(A_k), _ptr(B_k), _ptr(W_pred))
+
+
+def kvlr_fit_workspace_bytes(shape, n) -> int:
+    return lib().kvlr_fit_workspace_bytes(ctypes.byref(shape), n)
+
+
+def kvlr_fit_moments(shape, k, v, n, moments, accumulate, workspace, ws_bytes, stream=None):
+    _check("kvlr_fit_moments", lib().kvlr_fit_moments(
+        ctypes.byref(shape), _ptr(k), _ptr(v), n, _ptr(moments), int(accumulate), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def kvlr_fit_solve(shape, moments, A_v, A_k, W_pred=None, lam_v=None, lam_k=None):
+    """Host call: every array is a host float64 array (numpy or CPU tensor)."""
+    args = [_host_f64(x, nm) for x, nm in ((moments, "moments"), (A_v, "A_v"), (A_k, "A_k"),
+                                          (W_pred, "W_pred"), (lam_v, "lam_v"), (lam_k, "lam_k"))]
+    _check("kvlr_fit_solve", lib().kvlr_fit_solve(ctypes.byref(shape), *[_ptr(x) for x in args]))
+
+
+def kvlr_fit_factors(shape, k, v, n, out, lam_v, lam_k, workspace, ws_bytes, stream=None):
+    lam_v = _host_f64(lam_v, "lam_v")
+    lam_k = _host_f64(lam_k, "lam_k")
+    _check("kvlr_fit_factors", lib().kvlr_fit_factors(
+        ctypes.byref(shape), _ptr(k), _ptr(v), n, ctypes.byref(out), _ptr(lam_v), _ptr(lam_k),
+        _ptr(workspace), ws_bytes, _stream(stream)))

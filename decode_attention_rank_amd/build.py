@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvlr.so")
 
-SOURCES = ["kvlr_api.hip", "k_route.hip", "k_attn.hip", "k_encode.hip", "k_small.hip", "k_oproj.hip"]
+SOURCES = ["kvlr_api.hip", "k_route.hip", "k_attn.hip", "k_encode.hip", "k_small.hip", "k_oproj.hip",
+           "k_fit.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

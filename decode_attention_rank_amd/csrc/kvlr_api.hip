@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "kvlr.h"
 #include "kvlr_internal.h"
 
@@ -113,6 +115,7 @@ const char* kvlr_status_string(kvlr_status st) {
     case KVLR_ERR_UNSUPPORTED: return "unsupported shape";
     case KVLR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case KVLR_ERR_HIP: return g_hip_msg;
+    case KVLR_ERR_NUMERICAL: return "the fit's linear algebra failed (rank-deficient samples)";
   }
   return "unknown status";
 }
@@ -376,6 +379,127 @@ kvlr_status kvlr_output_projection(const kvlr_shape* shape, const void* F, const
   a.hidden = hidden;
   a.batch = batch;
   return hip_status(kvlr::launch_oproj(a, as_stream(stream)));
+}
+
+size_t kvlr_fit_workspace_bytes(const kvlr_shape* shape, int32_t n) {
+  Dims dm;
+  if (check_shape(shape, &dm) != KVLR_OK || n < 0) return 0;
+  const size_t per_run = static_cast<size_t>(dm.Hkv) * 3 * dm.D * dm.D;
+  const int runs = n > 0 ? kvlr::fit_runs(dm.Hkv, n).runs : 0;
+  return round_up(per_run * sizeof(double)) + round_up(runs * per_run * sizeof(float));
+}
+
+kvlr_status kvlr_fit_moments(const kvlr_shape* shape, const void* k, const void* v, int32_t n,
+                             double* moments, int32_t accumulate, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (n < 0 || (accumulate != 0 && accumulate != 1) || !ok_ptr(moments)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(workspace))) return KVLR_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < kvlr_fit_workspace_bytes(shape, n)) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  const size_t per_run = static_cast<size_t>(dm.Hkv) * 3 * dm.D * dm.D;
+  kvlr::FitArgs a{};
+  a.dm = dm;
+  a.k = k;
+  a.v = v;
+  a.n = n;
+  a.partial = n > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               round_up(per_run * sizeof(double)))
+                    : nullptr;
+  a.moments = moments;
+  a.accumulate = accumulate;
+  return hip_status(kvlr::launch_fit_moments(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_fit_solve(const kvlr_shape* shape, const double* moments, double* A_v,
+                           double* A_k, double* W_pred, double* lam_v, double* lam_k) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!moments || !A_v || !A_k || (dm.exact && !W_pred)) return KVLR_ERR_INVALID_ARGUMENT;
+  const kvlr::FitStatus fs = kvlr::fit_solve(dm, moments, A_v, A_k, W_pred, lam_v, lam_k);
+  return fs == kvlr::FitStatus::kOk ? KVLR_OK : KVLR_ERR_NUMERICAL;
+}
+
+}  // extern "C"
+
+namespace {
+
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// host image of a float64 matrix in the storage type; transposed from
+// [H][rows][cols] to [H][cols][rows] when asked
+std::vector<uint8_t> storage_image(const std::vector<double>& m, int H, int rows, int cols,
+                                   bool transpose, int dtype) {
+  const size_t elem = dtype == KVLR_DTYPE_BF16 ? 2 : 4;
+  std::vector<uint8_t> out(m.size() * elem);
+  for (int g = 0; g < H; ++g)
+    for (int i = 0; i < rows; ++i)
+      for (int j = 0; j < cols; ++j) {
+        const size_t src = (static_cast<size_t>(g) * rows + i) * cols + j;
+        const size_t dst = transpose ? (static_cast<size_t>(g) * cols + j) * rows + i : src;
+        const float f = static_cast<float>(m[src]);
+        if (elem == 2) {
+          const uint16_t b = bf16_rne(f);
+          memcpy(&out[dst * 2], &b, 2);
+        } else {
+          memcpy(&out[dst * 4], &f, 4);
+        }
+      }
+  return out;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvlr_status kvlr_fit_factors(const kvlr_shape* shape, const void* k, const void* v, int32_t n,
+                             const kvlr_factor_buffers* out, double* lam_v, double* lam_k,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (n < 1 || !out || !ok_ptr(out->A_v) || !ok_ptr(out->B_v) || !ok_ptr(out->A_k) ||
+      !ok_ptr(out->B_k) || (dm.exact && !ok_ptr(out->W_pred)) || !ok_ptr(workspace))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < kvlr_fit_workspace_bytes(shape, n)) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  double* moments = static_cast<double*>(workspace);
+  st = kvlr_fit_moments(shape, k, v, n, moments, 0, workspace, ws_bytes, stream);
+  if (st != KVLR_OK) return st;
+  const hipStream_t s = as_stream(stream);
+  const int H = dm.Hkv, D = dm.D, RV = dm.RV, RK = dm.RK;
+  std::vector<double> mom(static_cast<size_t>(H) * 3 * D * D);
+  hipError_t e = hipMemcpyAsync(mom.data(), moments, mom.size() * sizeof(double),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  std::vector<double> A_v(static_cast<size_t>(H) * D * RV), A_k(static_cast<size_t>(H) * D * RK),
+      W(dm.exact ? static_cast<size_t>(H) * RV * D : 0);
+  if (kvlr::fit_solve(dm, mom.data(), A_v.data(), A_k.data(), dm.exact ? W.data() : nullptr, lam_v,
+                      lam_k) != kvlr::FitStatus::kOk)
+    return KVLR_ERR_NUMERICAL;
+  struct Item {
+    void* dst;
+    std::vector<uint8_t> img;
+  };
+  std::vector<Item> items;
+  items.push_back({out->A_v, storage_image(A_v, H, D, RV, false, dm.dtype)});
+  items.push_back({out->B_v, storage_image(A_v, H, D, RV, true, dm.dtype)});
+  items.push_back({out->A_k, storage_image(A_k, H, D, RK, false, dm.dtype)});
+  items.push_back({out->B_k, storage_image(A_k, H, D, RK, true, dm.dtype)});
+  if (dm.exact) items.push_back({out->W_pred, storage_image(W, H, RV, D, false, dm.dtype)});
+  for (auto& it : items) {
+    e = hipMemcpyAsync(it.dst, it.img.data(), it.img.size(), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(hipStreamSynchronize(s));  // the host images must outlive the copies
 }
 
 }  // extern "C"

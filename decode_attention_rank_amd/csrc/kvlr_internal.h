@@ -120,4 +120,28 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 
+// Factor fitting: second moments of sample keys and values per KV head.
+struct FitArgs {
+  Dims dm;
+  const void* k;      // [n][Hkv][D] samples, storage type
+  const void* v;
+  int n;
+  float* partial;     // [runs][Hkv][3][D][D] per-run float32 sums
+  double* moments;    // [Hkv][3][D][D]: V^T V, K^T K, V^T K
+  int accumulate;     // add onto moments instead of overwriting
+};
+struct FitRuns {
+  int runs;   // token runs (workgroups per KV head)
+  int chunk;  // tokens per run, a multiple of 64
+};
+FitRuns fit_runs(int Hkv, int n);
+hipError_t launch_fit_moments(const FitArgs& a, hipStream_t s);
+
+enum class FitStatus { kOk, kSingular, kNoConvergence };
+// Host: factors from float64 moments. A_v [Hkv][D][RV], A_k [Hkv][D][RK],
+// W [Hkv][RV][D] (exact keys only), lam_v [Hkv][RV], lam_k [Hkv][RK] (may
+// be null).
+FitStatus fit_solve(const Dims& dm, const double* moments, double* A_v, double* A_k, double* W,
+                    double* lam_v, double* lam_k);
+
 }  // namespace kvlr

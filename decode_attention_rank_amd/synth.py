@@ -32,6 +32,12 @@ Recipe (per KV head g; all draws seeded by (workload seed, role, sequence)):
     pages get their key coefficients (and the shared value coefficients)
     shifted by boost * u, u the unit vector of Q_k[:, :rs]^T q_bar, q_bar the
     mean query of the KV group.
+  * Calibration samples for the factor fit (make_fit_samples): per KV head,
+    coefficients C ~ N(0,1) of full width d scaled by FIT_DECAY^i, so the
+    sample spectra have distinct, geometrically spaced eigenvalues;
+    V = (C * scale) Q_v^T; K = [C[:, :ns] * scale[:ns], E * FIT_KEY_SCALE *
+    scale[ns:]] Q_k^T with E ~ N(0,1) (ns = shared_rank: the key part the
+    value carries). No further noise. Rounded to the storage type.
   * Ragged contexts: L ~ round(lognormal(mu, sigma)) clipped to
     [ctx_min, ctx_max], mu = mean of the log bounds, sigma = quarter of the
     log range.
@@ -47,7 +53,10 @@ import torch
 from .workloads import Workload
 
 _ROLE = {"bases": 1, "q": 2, "coef": 3, "noise": 4, "lens": 5, "planted": 6,
-         "pages": 7, "raw": 8, "oproj": 9}
+         "pages": 7, "raw": 8, "oproj": 9, "fit": 10}
+
+FIT_DECAY = 0.97      # per-coordinate scale ratio of the calibration samples
+FIT_KEY_SCALE = 0.8   # key-only coordinates relative to the shared ones
 
 TORCH_STORAGE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -256,4 +265,34 @@ def synth_raw_tokens(wl: Workload, b: int, pos0: int, n: int, device="cpu", *, q
         bk = Qk[g, :, :rs].to(torch.float32).to(device)
         V[:, g] = (C @ bv.T.contiguous() + s * torch.randn(n, d, generator=gen, device=device)).to(dt)
         K[:, g] = (kc @ bk.T.contiguous() + s * torch.randn(n, d, generator=gen, device=device)).to(dt)
+    return K, V
+
+
+def fit_sample_count(wl: Workload) -> int:
+    """Calibration samples per KV head: every token of the workload's cache."""
+    return wl.batch * wl.context
+
+
+def make_fit_samples(wl: Workload, n: int, device="cpu"):
+    """Calibration keys and values (K, V), each [n, H_kv, d] in the storage type."""
+    Qv, Qk = bases(wl)
+    H, d, ns = wl.num_kv_heads, wl.head_dim, wl.shared_rank
+    dt = storage_dtype(wl)
+    scale = FIT_DECAY ** torch.arange(d, dtype=torch.float64)
+    kscale = scale.clone()
+    kscale[ns:] *= FIT_KEY_SCALE
+    scale = scale.to(torch.float32).to(device)
+    kscale = kscale.to(torch.float32).to(device)
+    K = torch.empty(n, H, d, dtype=dt, device=device)
+    V = torch.empty(n, H, d, dtype=dt, device=device)
+    for g in range(H):
+        gen = _gen(device, wl.seed, "fit", g)
+        C = torch.randn(n, d, generator=gen, device=device)
+        E = torch.randn(n, d - ns, generator=gen, device=device)
+        kc = torch.cat([C[:, :ns], E], dim=1) * kscale
+        bv = Qv[g].to(torch.float32).to(device)
+        bk = Qk[g].to(torch.float32).to(device)
+        V[:, g] = ((C * scale) @ bv.T.contiguous()).to(dt)
+        K[:, g] = (kc @ bk.T.contiguous()).to(dt)
+        del C, E, kc
     return K, V

@@ -100,3 +100,14 @@ WORKLOADS = {
 }
 
 DEFAULT_BENCH_WORKLOAD = "llama3-8b-routed-32k"
+
+# Factor-fit calibration cases (samples, not a decode step).
+FIT_WORKLOADS = {
+    # Factor-fit calibration at the 8B routed shapes: one sample per cached
+    # token (16 sequences x 32768), decaying sample spectra.
+    "llama3-8b-fit-512k": Workload(
+        name="llama3-8b-fit-512k", batch=16, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, page_size=64, rank_v=64, rank_k=32, storage="bf16",
+        key_mode="exact", context=32768, shared_rank=32, seed=6),
+}
+DEFAULT_FIT_WORKLOAD = "llama3-8b-fit-512k"

@@ -12,13 +12,15 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a device pointer unless marked "host".
- *     The caller owns every buffer; the library allocates nothing and keeps
- *     no mutable global state. Calls are thread-safe.
+ *     The caller owns every buffer; the library allocates no device memory
+ *     and keeps no mutable global state. Calls are thread-safe.
  *   - Each call validates its arguments on the host, then enqueues its
  *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
  *     returns without synchronising. Outputs are valid once the stream has
  *     reached the call. A non-zero status means nothing was enqueued, except
- *     KVLR_ERR_HIP, which reports a failed launch.
+ *     KVLR_ERR_HIP, which reports a failed launch. The calibration calls
+ *     kvlr_fit_solve and kvlr_fit_factors are the exceptions: they work on
+ *     the host (and the latter synchronises), as their comments say.
  *   - Device arrays must be 16-byte aligned. Integer arrays are int32.
  *   - Values that only the device holds (sequence lengths, page tables) are
  *     trusted: the caller keeps every referenced page id inside
@@ -75,6 +77,7 @@ typedef int32_t kvlr_status;
 #define KVLR_ERR_UNSUPPORTED 2
 #define KVLR_ERR_WORKSPACE_TOO_SMALL 3
 #define KVLR_ERR_HIP 4
+#define KVLR_ERR_NUMERICAL 5   /* factor fit: rank-deficient samples */
 
 #define KVLR_DTYPE_BF16 0
 #define KVLR_DTYPE_F32 1
@@ -283,6 +286,87 @@ kvlr_status kvlr_fold_output_weights(const kvlr_shape* shape, const kvlr_factors
  */
 kvlr_status kvlr_output_projection(const kvlr_shape* shape, const void* F, const float* z,
                                    int32_t hidden, float* out, int32_t batch, void* stream);
+
+/*
+ * Factor fitting from sample keys and values (calibration, not decode).
+ * BasisKV English abstract (low-rank K/V projections; the value latent
+ * predicts part of each key and a key-specific residual holds what the value
+ * cannot recover) and method details (key design: the choice of the
+ * low-rank factors). The pages leave the fit open; the library implements
+ * the staged least-squares reading, per KV head g, from n samples
+ * K, V [n][d]:
+ *   A_v    = top-r_v eigenvectors of V^T V                 B_v = A_v^T
+ *   W_pred = (v^T v)^-1 v^T K,  v = V . A_v                (exact keys only)
+ *   A_k    = top-r_k eigenvectors of R^T R, R = K - v . W_pred  (exact keys)
+ *            or of K^T K                                   (latent keys)
+ *   B_k    = A_k^T
+ * Eigenvectors come largest eigenvalue first, each scaled so that its entry
+ * of largest magnitude is positive. All of it follows from the second
+ * moments V^T V, K^T K and V^T K, which the GPU accumulates; the host solves
+ * the d x d eigenproblems in float64.
+ *
+ * Samples k, v are [n][H_kv][head_dim] in the storage type (the layout of
+ * kvlr_append_encode's new tokens); n is host, n <= 2^31 - 1. With exact
+ * keys n should well exceed rank_v + rank_k: at n <= rank_v the value latent
+ * reproduces the samples' keys exactly, the residual vanishes and A_k is
+ * arbitrary.
+ */
+typedef struct kvlr_factor_buffers {
+  void* A_v;     /* out [H_kv][head_dim][rank_v] */
+  void* B_v;     /* out [H_kv][rank_v][head_dim] */
+  void* A_k;     /* out [H_kv][head_dim][rank_k] */
+  void* B_k;     /* out [H_kv][rank_k][head_dim] */
+  void* W_pred;  /* out [H_kv][rank_v][head_dim], KVLR_KEYS_EXACT only */
+} kvlr_factor_buffers;
+
+/* Device workspace bytes for kvlr_fit_moments / kvlr_fit_factors with n
+ * samples (at most about 100 MB plus the float64 moments); 0 for a rejected
+ * shape. */
+size_t kvlr_fit_workspace_bytes(const kvlr_shape* shape, int32_t n);
+
+/*
+ * Second moments of n samples, accumulated on the GPU (stream-ordered,
+ * asynchronous like the decode calls):
+ *   moments  device [H_kv][3][head_dim][head_dim] float64: V^T V, K^T K,
+ *            V^T K per KV head. accumulate = 0 overwrites, 1 adds onto the
+ *            buffer's contents, so calibration can stream batches of samples.
+ * bf16 samples multiply exactly on the matrix cores with float32 sums over
+ * runs of at least 2048 tokens (when n allows); f32 samples use float32
+ * FMA. Runs are added in a fixed order in float64: results are
+ * deterministic. n = 0 is a no-op (or zeroes the moments).
+ */
+kvlr_status kvlr_fit_moments(const kvlr_shape* shape, const void* k, const void* v, int32_t n,
+                             double* moments, int32_t accumulate, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Host only (touches no device): the factors from float64 moments.
+ *   moments  host [H_kv][3][head_dim][head_dim] as kvlr_fit_moments writes
+ *   A_v      host out [H_kv][head_dim][rank_v] float64 (B_v = A_v^T)
+ *   A_k      host out [H_kv][head_dim][rank_k] float64 (B_k = A_k^T)
+ *   W_pred   host out [H_kv][rank_v][head_dim] float64, KVLR_KEYS_EXACT only
+ *   lam_v, lam_k  host out [H_kv][rank_v] / [H_kv][rank_k]: the eigenvalues
+ *            of the chosen eigenvectors (may be NULL)
+ * Returns KVLR_ERR_NUMERICAL when v^T v is numerically singular: a Cholesky
+ * pivot at or below 1e-6 of its largest diagonal entry, i.e. a chosen value
+ * direction with under a millionth of the leading direction's energy (below
+ * the resolution of float32-accumulated moments). Uses up to 16 host threads
+ * (one KV head each).
+ */
+kvlr_status kvlr_fit_solve(const kvlr_shape* shape, const double* moments, double* A_v,
+                           double* A_k, double* W_pred, double* lam_v, double* lam_k);
+
+/*
+ * The whole fit in one synchronous call: kvlr_fit_moments into the
+ * workspace, a copy of the moments to the host, kvlr_fit_solve, and the
+ * factors written to `out` in the storage type (RNE of the float32 value).
+ * lam_v, lam_k as in kvlr_fit_solve (host, may be NULL). Unlike the decode
+ * calls it synchronises `stream` and uses host memory (a few MB) and up to
+ * 16 host threads; it is meant for calibration, not for the decode loop.
+ */
+kvlr_status kvlr_fit_factors(const kvlr_shape* shape, const void* k, const void* v, int32_t n,
+                             const kvlr_factor_buffers* out, double* lam_v, double* lam_k,
+                             void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from decode_attention_rank_amd import _lib as K
@@ -181,3 +182,37 @@ def test_output_projection_arguments(lib):
     sf = _shape(dtype=K.KVLR_DTYPE_F32)
     assert lib.kvlr_output_projection(ctypes.byref(sf), fake, fake, 4096, fake, 4, None) == \
         K.KVLR_ERR_UNSUPPORTED
+
+
+def test_fit_arguments(lib):
+    s = _shape()
+    fake = 1 << 20
+    E = K.KVLR_ERR_INVALID_ARGUMENT
+    ws = K.kvlr_fit_workspace_bytes(s, 524288)
+    # float64 moments plus float32 per-run partials (512 workgroups over 8 heads)
+    assert ws >= 8 * 3 * 128 * 128 * (8 + 4 * 64)
+    assert K.kvlr_fit_workspace_bytes(s, 0) == 8 * 3 * 128 * 128 * 8
+    assert K.kvlr_fit_workspace_bytes(s, -1) == 0
+    assert K.kvlr_fit_workspace_bytes(_shape(head_dim=96), 100) == 0
+    assert K.kvlr_fit_workspace_bytes(s, 100) < K.kvlr_fit_workspace_bytes(s, 100000)
+    mom = lib.kvlr_fit_moments
+    assert mom(ctypes.byref(s), fake, fake, 100, fake, 2, fake, ws, None) == E       # accumulate flag
+    assert mom(ctypes.byref(s), fake, fake, -1, fake, 0, fake, ws, None) == E
+    assert mom(ctypes.byref(s), fake, fake, 100, None, 0, fake, ws, None) == E
+    assert mom(ctypes.byref(s), fake + 8, fake, 100, fake, 0, fake, ws, None) == E   # misaligned
+    assert mom(ctypes.byref(s), fake, fake, 100000, fake, 0, fake, 1024, None) == \
+        K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    out = K.make_factor_buffers(fake, fake, fake, fake, None)  # exact keys need W_pred
+    fit = lib.kvlr_fit_factors
+    assert fit(ctypes.byref(s), fake, fake, 100, ctypes.byref(out), None, None, fake, ws, None) == E
+    out = K.make_factor_buffers(fake, fake, fake, fake, fake)
+    assert fit(ctypes.byref(s), fake, fake, 0, ctypes.byref(out), None, None, fake, ws, None) == E
+    assert fit(ctypes.byref(s), fake, fake, 100000, ctypes.byref(out), None, None, fake, 64,
+               None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    assert fit(ctypes.byref(_shape(head_dim=96)), fake, fake, 100, ctypes.byref(out), None, None,
+               fake, ws, None) == K.KVLR_ERR_UNSUPPORTED
+    assert lib.kvlr_fit_solve(ctypes.byref(s), None, fake, fake, fake, None, None) == E
+    assert "linear algebra" in K.kvlr_status_string(K.KVLR_ERR_NUMERICAL)
+    with pytest.raises(TypeError):
+        K.kvlr_fit_solve(s, np.zeros((8, 3, 128, 128), np.float32), np.zeros((8, 128, 64)),
+                         np.zeros((8, 128, 32)), np.zeros((8, 64, 128)))
