@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0
 CPU_CACHE_BYTES = 6 << 30  # host memory for oracle inputs repeated after the first pass
 ROUTE_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_route.hip")
 ATTN_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_attn.hip")
+FIT_SOURCE = os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_fit.hip")
 
 
 def log(*a):
@@ -177,15 +178,19 @@ def time_factor_fit(reps: int = 10):
     for _ in range(3):
         fit.fit(k, v)
     fit_ms = (time.perf_counter() - t0) * 1e3 / 3
-    algo = 2 * n * H * d * k.element_size() + H * 3 * d * d * 8
+    kernel_algo = 2 * n * H * d * k.element_size()   # the samples, read once
+    algo = kernel_algo + H * 3 * d * d * 8             # plus the float64 moments written
     flops = 2.0 * n * H * 3 * d * d
     gbps = algo / (us * 1e-6) / 1e9
     del k, v
     return {"workload": wl.name, "samples_per_kv_head": n, "num_kv_heads": H, "head_dim": d,
             "rank_v": wl.rank_v, "rank_k": wl.rank_k, "storage": wl.storage,
-            "kernel": "moments_mfma_kernel", "moments_call_us": round(us, 2),
-            "algo_bytes_per_call": algo, "achieved_gbps": round(gbps, 1),
-            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "timed": "kvlr_fit_moments: moments_mfma_kernel + moments_sum_kernel",
+            "moments_call_us": round(us, 2), "algo_bytes_per_call": algo,
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": measured_traffic("moments_mfma_kernel", wl.name, FIT_SOURCE),
+                         "kernel": "moments_mfma_kernel", "kernel_algo_bytes": kernel_algo},
             "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "fit_factors_call_ms": round(fit_ms, 2)}
 

@@ -15,16 +15,19 @@
 // M = A_v^T C_VV A_v = v^T v:  W_pred = M^-1 P  and  R^T R = C_KK - P^T W_pred.
 //
 //  - moments_mfma_kernel (bf16 samples): a workgroup takes a run of tokens of
-//    one KV head; wave w owns the 16-dimension row block w of all three
-//    moments. Tokens are staged 64 at a time into LDS directly in matrix-core
-//    fragment order (8 tokens of one dimension per lane), so each operand is
-//    one 16-byte LDS read, and v_mfma_f32_16x16x32_bf16 forms the products
-//    (exact for bf16) with float32 sums. The next 64 tokens' loads are in
-//    flight while the current ones are multiplied.
+//    one KV head and forms the upper block triangle of Z^T Z, Z = [V K]
+//    (V^T V, K^T K, V^T K) on the matrix cores: v_mfma_f32_16x16x32_bf16,
+//    exact bf16 products, float32 sums. Tokens are staged 128 at a time into
+//    double-buffered LDS directly in fragment order (8 tokens of one
+//    dimension per lane), so an operand is one 16-byte LDS read; each wave
+//    owns a 4x4-block patch of the triangle and reuses every fragment it
+//    reads in 4 or 5 products. The next stage's loads are in flight while
+//    the current one is multiplied.
 //  - moments_valu_kernel (f32 samples): the same partial sums on the vector
 //    ALUs, one 8x8 (or 4x4) block of one moment per thread.
 //  - moments_sum_kernel adds the per-run partials in a fixed order into
-//    float64 moments (optionally onto what the buffer already holds).
+//    float64 moments (optionally onto what the buffer already holds) and
+//    mirrors the symmetric moments' lower triangle.
 //  - The host solves the small symmetric eigenproblems in float64:
 //    Householder reduction to tridiagonal form, then implicit QR steps with
 //    the Wilkinson shift (Golub and Van Loan, Matrix Computations, the
@@ -42,20 +45,91 @@
 namespace kvlr {
 namespace {
 
-constexpr int kStageTok = 64;  // tokens staged per LDS fill
+constexpr int kStageTok = 128;   // tokens staged per LDS fill (double-buffered: 128 KB)
+constexpr int kFitGrid = 256;    // workgroups over all heads: one per compute unit
 
 template <int D>
 struct MomLayout {
-  static constexpr int NB = D / 16;                    // 16-dimension blocks = waves
-  static constexpr int THREADS = NB * kWave;
+  static constexpr int NB = D / 16;                    // 16-dimension blocks per tensor
+  static constexpr int WAVES = NB;
+  static constexpr int THREADS = WAVES * kWave;
   static constexpr int KSTEPS = kStageTok / 32;        // 32-token matrix-core k-steps
   static constexpr int FRAG_DW = kWave * 4;            // one fragment: 64 lanes x 16 bytes
   static constexpr int RB_DW = KSTEPS * FRAG_DW + 4;   // +16 bytes: blocks start on rotating banks
-  static constexpr int TENSOR_DW = NB * RB_DW;
-  static constexpr int TOTAL_DW = 2 * TENSOR_DW;       // V then K
+  static constexpr int BUF_DW = 2 * NB * RB_DW;        // V blocks then K blocks
   static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per token row
-  static_assert(2 * 16 * CHUNKS == THREADS, "one staging task per thread");
+  static constexpr int TASKS = 2 * (kStageTok / 4) * CHUNKS / THREADS;  // staging tasks per thread
+  static_assert(TASKS * THREADS == 2 * (kStageTok / 4) * CHUNKS, "staging tasks divide evenly");
 };
+
+// The moments are the blocks of Z^T Z, Z = [V K] (2 NB blocks of 16
+// dimensions): V^T V, K^T K and V^T K. Only the upper triangle (block row <=
+// block column) is formed; the sum kernel mirrors the rest. A wave owns a
+// patch of 4x4 blocks (diagonal patches are triangles, two per wave), so it
+// reads 8 fragments per k-step and reuses each in 4 or 5 products.
+struct WaveJob {
+  int nf, nt;
+  int f[8];            // Z blocks whose fragments the wave reads
+  int a[20], b[20];    // tile t = fragment f[a[t]]^T times fragment f[b[t]]
+};
+
+template <int D>
+constexpr WaveJob wave_job(int w) {
+  WaveJob j{};
+  if (D == 128) {
+    const int offI[6] = {0, 0, 0, 1, 1, 2}, offJ[6] = {1, 2, 3, 2, 3, 3};
+    if (w < 6) {  // an off-diagonal 4x4 patch: 16 tiles
+      j.nf = 8;
+      for (int r = 0; r < 4; ++r) {
+        j.f[r] = 4 * offI[w] + r;
+        j.f[4 + r] = 4 * offJ[w] + r;
+      }
+      for (int r = 0; r < 4; ++r)
+        for (int c = 0; c < 4; ++c) {
+          j.a[j.nt] = r;
+          j.b[j.nt] = 4 + c;
+          ++j.nt;
+        }
+    } else {  // two diagonal patches, upper triangles: 2 x 10 tiles
+      const int p0 = 2 * (w - 6);
+      j.nf = 8;
+      for (int r = 0; r < 4; ++r) {
+        j.f[r] = 4 * p0 + r;
+        j.f[4 + r] = 4 * (p0 + 1) + r;
+      }
+      for (int h = 0; h < 2; ++h)
+        for (int r = 0; r < 4; ++r)
+          for (int c = r; c < 4; ++c) {
+            j.a[j.nt] = 4 * h + r;
+            j.b[j.nt] = 4 * h + c;
+            ++j.nt;
+          }
+    }
+  } else {  // D == 64: Z has 8 blocks, 36 upper tiles over 4 waves
+    if (w < 2) {  // half of the V^T K patch: block rows 2w, 2w+1
+      j.nf = 6;
+      j.f[0] = 2 * w;
+      j.f[1] = 2 * w + 1;
+      for (int c = 0; c < 4; ++c) j.f[2 + c] = 4 + c;
+      for (int r = 0; r < 2; ++r)
+        for (int c = 0; c < 4; ++c) {
+          j.a[j.nt] = r;
+          j.b[j.nt] = 2 + c;
+          ++j.nt;
+        }
+    } else {  // V^T V (w = 2) or K^T K (w = 3) upper triangle
+      j.nf = 4;
+      for (int r = 0; r < 4; ++r) j.f[r] = 4 * (w - 2) + r;
+      for (int r = 0; r < 4; ++r)
+        for (int c = r; c < 4; ++c) {
+          j.a[j.nt] = r;
+          j.b[j.nt] = c;
+          ++j.nt;
+        }
+    }
+  }
+  return j;
+}
 
 // bf16 half e (0..7) of a 16-byte chunk
 __device__ __forceinline__ uint32_t half_of(const uint4& x, int e) {
@@ -63,84 +137,125 @@ __device__ __forceinline__ uint32_t half_of(const uint4& x, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int D>
-__global__ __launch_bounds__(MomLayout<D>::THREADS) void moments_mfma_kernel(
-    const uint8_t* __restrict__ k, const uint8_t* __restrict__ v, float* __restrict__ partial,
-    int n, int Hkv, int chunk_tokens) {
+// The whole run for wave W of the workgroup (all waves pass the same
+// barriers; only the products differ).
+template <int D, int W>
+__device__ __forceinline__ void moments_run(const uint8_t* __restrict__ k,
+                                            const uint8_t* __restrict__ v,
+                                            float* __restrict__ partial, int n, int Hkv,
+                                            int chunk_tokens, uint32_t* lds) {
   using L = MomLayout<D>;
-  __shared__ __align__(16) uint32_t lds[L::TOTAL_DW];
+  constexpr WaveJob J = wave_job<D>(W);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;  // row block
   const int c = blockIdx.x, g = blockIdx.y;
   const int t0 = c * chunk_tokens;
   const int t1 = min(t0 + chunk_tokens, n);
   const size_t row_bytes = static_cast<size_t>(Hkv) * D * 2;
 
-  // staging task: tensor tt, 4-token group tg, 16-byte chunk ch
+  // staging task i of this thread: tensor i, 4-token group tg, 16-byte chunk ch
   const int ch = tid % L::CHUNKS;
-  const int tg = (tid / L::CHUNKS) % 16;
-  const int tt = tid / (16 * L::CHUNKS);
-  const uint8_t* src = (tt == 0 ? v : k) + static_cast<size_t>(g) * D * 2 + ch * 16;
-  // LDS slot of (token 4*tg + u, dimension 8*ch + e): block ch/2, k-step tg/8,
-  // lane (tg%8)/2 * 16 + (ch%2)*8 + e, tokens 4*(tg%2) .. +3 of the lane's 8
-  const int slot_dw = tt * L::TENSOR_DW + (ch / 2) * L::RB_DW + (tg / 8) * L::FRAG_DW +
-                      (((tg % 8) / 2) * 16 + (ch % 2) * 8) * 4 + 2 * (tg % 2);
-
-  uint4 x[4];
-  auto load_stage = [&](int base) {
+  const int tg = (tid / L::CHUNKS) % (kStageTok / 4);
+  const uint8_t* src[L::TASKS];
+  int slot[L::TASKS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = base + 4 * tg + u;
-      const int tc = min(t, t1 - 1);
-      x[u] = load16(src + static_cast<size_t>(tc) * row_bytes);
-      if (t >= t1) x[u] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < L::TASKS; ++i) {
+    const int q = tid + i * L::THREADS;
+    const int tt = q / ((kStageTok / 4) * L::CHUNKS);
+    src[i] = (tt == 0 ? v : k) + static_cast<size_t>(g) * D * 2 + ch * 16;
+    // (token 4 tg + u, dimension 8 ch + e) -> block ch/2 of tensor tt,
+    // k-step tg/8, lane ((tg%8)/2)*16 + (ch%2)*8 + e, tokens 4 (tg%2) .. +3
+    slot[i] = (tt * L::NB + ch / 2) * L::RB_DW + (tg / 8) * L::FRAG_DW +
+              (((tg % 8) / 2) * 16 + (ch % 2) * 8) * 4 + 2 * (tg % 2);
+  }
+  // The next stage's tokens are loaded while the current one is multiplied.
+  // Loads past the run's end read its last token and are zeroed, so every
+  // load is unconditional.
+  uint4 xa[L::TASKS][4];
+  auto load_stage = [&](uint4 (&x)[L::TASKS][4], int base) {
+#pragma unroll
+    for (int i = 0; i < L::TASKS; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = base + 4 * tg + u;
+        x[i][u] = load16(src[i] + static_cast<size_t>(min(t, t1 - 1)) * row_bytes);
+        if (t >= t1) x[i][u] = make_uint4(0, 0, 0, 0);
+      }
+  };
+  auto store_stage = [&](const uint4 (&x)[L::TASKS][4], uint32_t* buf) {
+#pragma unroll
+    for (int i = 0; i < L::TASKS; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint2 pk;
+        pk.x = half_of(x[i][0], e) | (half_of(x[i][1], e) << 16);
+        pk.y = half_of(x[i][2], e) | (half_of(x[i][3], e) << 16);
+        *reinterpret_cast<uint2*>(&buf[slot[i] + e * 4]) = pk;
+      }
+  };
+
+  f32x4 acc[J.nt];
+#pragma unroll
+  for (int t = 0; t < J.nt; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto multiply = [&](const uint32_t* cur) {
+#pragma unroll
+    for (int ks = 0; ks < L::KSTEPS; ++ks) {
+      bf16x8 fr[J.nf];
+#pragma unroll
+      for (int i = 0; i < J.nf; ++i)
+        fr[i] = *reinterpret_cast<const bf16x8*>(&cur[J.f[i] * L::RB_DW + ks * L::FRAG_DW + lane * 4]);
+#pragma unroll
+      for (int t = 0; t < J.nt; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[J.a[t]], fr[J.b[t]], acc[t], 0, 0, 0);
     }
   };
 
-  f32x4 acc[3][L::NB];
-#pragma unroll
-  for (int m = 0; m < 3; ++m)
-#pragma unroll
-    for (int j = 0; j < L::NB; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (t0 < t1) load_stage(t0);
-  for (int base = t0; base < t1; base += kStageTok) {
-    __syncthreads();  // the previous stage's fragments have been read
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 pk;
-      pk.x = half_of(x[0], e) | (half_of(x[1], e) << 16);
-      pk.y = half_of(x[2], e) | (half_of(x[3], e) << 16);
-      *reinterpret_cast<uint2*>(&lds[slot_dw + e * 4]) = pk;
-    }
-    __syncthreads();
-    if (base + kStageTok < t1) load_stage(base + kStageTok);
-#pragma unroll
-    for (int ks = 0; ks < L::KSTEPS; ++ks) {
-      const int off = ks * L::FRAG_DW + lane * 4;
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&lds[wv * L::RB_DW + off]);
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&lds[L::TENSOR_DW + wv * L::RB_DW + off]);
-#pragma unroll
-      for (int j = 0; j < L::NB; ++j) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&lds[j * L::RB_DW + off]);
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&lds[L::TENSOR_DW + j * L::RB_DW + off]);
-        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, acc[1][j], 0, 0, 0);
-        acc[2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bk, acc[2][j], 0, 0, 0);
-      }
-    }
+  uint32_t* buf0 = lds;
+  uint32_t* buf1 = lds + L::BUF_DW;
+  const int stages = (t1 - t0 + kStageTok - 1) / kStageTok;
+  load_stage(xa, t0);
+  store_stage(xa, buf0);
+  __syncthreads();
+  for (int s = 0; s < stages; ++s) {
+    load_stage(xa, t0 + (s + 1) * kStageTok);
+    multiply((s & 1) ? buf1 : buf0);
+    store_stage(xa, (s & 1) ? buf0 : buf1);
+    __syncthreads();  // next stage visible; this stage's buffer free for reuse
   }
   // lane holds rows 4*(lane/16) + r of column lane%16 of each 16x16 tile
   const int kq = lane >> 4, col = lane & 15;
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
+  for (int t = 0; t < J.nt; ++t) {
+    const int za = J.f[J.a[t]], zb = J.f[J.b[t]];
+    const int m = zb < L::NB ? 0 : (za >= L::NB ? 1 : 2);
+    const int row0 = (za % L::NB) * 16, col0 = (zb % L::NB) * 16;
     float* out = partial + ((static_cast<size_t>(c) * Hkv + g) * 3 + m) * D * D;
 #pragma unroll
-    for (int j = 0; j < L::NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        out[static_cast<size_t>(wv * 16 + 4 * kq + r) * D + j * 16 + col] = acc[m][j][r];
+    for (int r = 0; r < 4; ++r)
+      out[static_cast<size_t>(row0 + 4 * kq + r) * D + col0 + col] = acc[t][r];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(MomLayout<D>::THREADS) void moments_mfma_kernel(
+    const uint8_t* __restrict__ k, const uint8_t* __restrict__ v, float* __restrict__ partial,
+    int n, int Hkv, int chunk_tokens) {
+  __shared__ __align__(16) uint32_t lds[2 * MomLayout<D>::BUF_DW];
+  switch (threadIdx.x / kWave) {
+#define KVLR_MOM_WAVE(W)                                                  \
+  case W:                                                                 \
+    if constexpr (W < MomLayout<D>::WAVES)                                \
+      moments_run<D, W>(k, v, partial, n, Hkv, chunk_tokens, lds);        \
+    break;
+    KVLR_MOM_WAVE(0)
+    KVLR_MOM_WAVE(1)
+    KVLR_MOM_WAVE(2)
+    KVLR_MOM_WAVE(3)
+    KVLR_MOM_WAVE(4)
+    KVLR_MOM_WAVE(5)
+    KVLR_MOM_WAVE(6)
+    KVLR_MOM_WAVE(7)
+#undef KVLR_MOM_WAVE
   }
 }
 
@@ -203,14 +318,33 @@ __global__ __launch_bounds__(kValuThreads) void moments_valu_kernel(
     for (int j = 0; j < BS; ++j) out[static_cast<size_t>(bi * BS + i) * D + bj * BS + j] = acc[i][j];
 }
 
+// Adds the per-run partials in run order. The symmetric moments (V^T V,
+// K^T K) were formed only for block row <= block column: those sums are
+// also written to the mirrored position.
 __global__ __launch_bounds__(256) void moments_sum_kernel(const float* __restrict__ partial,
                                                           double* __restrict__ moments, int runs,
-                                                          size_t per_run, int accumulate) {
+                                                          int D, size_t per_run, int accumulate) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= per_run) return;
-  double s = accumulate ? moments[i] : 0.0;
-  for (int c = 0; c < runs; ++c) s += static_cast<double>(partial[static_cast<size_t>(c) * per_run + i]);
-  moments[i] = s;
+  const int col = static_cast<int>(i % D), row = static_cast<int>((i / D) % D);
+  const int m = static_cast<int>((i / (static_cast<size_t>(D) * D)) % 3);
+  const bool sym = m < 2;
+  if (sym && row / 16 > col / 16) return;
+  double s = 0.0;
+  int c = 0;
+  for (; c + 8 <= runs; c += 8) {  // eight loads in flight, summed in run order
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = partial[static_cast<size_t>(c + u) * per_run + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += static_cast<double>(p[u]);
+  }
+  for (; c < runs; ++c) s += static_cast<double>(partial[static_cast<size_t>(c) * per_run + i]);
+  moments[i] = (accumulate ? moments[i] : 0.0) + s;
+  if (sym && row / 16 < col / 16) {
+    const size_t mi = i - (static_cast<size_t>(row) * D + col) + static_cast<size_t>(col) * D + row;
+    moments[mi] = (accumulate ? moments[mi] : 0.0) + s;
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -455,9 +589,10 @@ void launch_valu(const FitArgs& a, int runs, int chunk, hipStream_t s) {
 }  // namespace
 
 FitRuns fit_runs(int Hkv, int n) {
-  // about 512 workgroups over the heads, but at least 2048 tokens per run
-  // while there are enough tokens (the partials are written and re-read)
-  const int max_runs = std::max(1, (512 + Hkv - 1) / Hkv);
+  // one workgroup per compute unit (256) over the heads, but at least 2048
+  // tokens per run while there are enough tokens (the partials are written
+  // and re-read)
+  const int max_runs = std::max(1, (kFitGrid + Hkv - 1) / Hkv);
   int runs = std::min(max_runs, std::max(1, n / 2048));
   int chunk = (n + runs - 1) / runs;
   chunk = std::max(kStageTok, (chunk + kStageTok - 1) / kStageTok * kStageTok);
@@ -483,7 +618,7 @@ hipError_t launch_fit_moments(const FitArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moments_sum_kernel, dim3(sum_grid), dim3(256), 0, s, a.partial, a.moments,
-                     fr.runs, per_run, a.accumulate);
+                     fr.runs, a.dm.D, per_run, a.accumulate);
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ SOURCES = {
     "route_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_route.hip"),
     "attn_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_attn.hip"),
     "encode_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_encode.hip"),
+    "moments_mfma_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_fit.hip"),
 }
 COPY_KERNEL_HINT = "neg_kernel"
 

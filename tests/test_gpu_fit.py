@@ -9,8 +9,12 @@ The argument has three links, each checked here or on the CPU:
      fit to 1e-10 on the CPU, tests/test_fit_host.py);
   3. end to end, the factors match the oracle's float64 fit of the samples
      within bf16 rounding (2^-8 relative) plus 2e-4 absolute: the moments'
-     relative error is about 1e-6 and the smallest relative eigenvalue gap
-     of the samples about 3e-2, so eigenvectors move by about 3e-5.
+     relative error is at most about 1e-6 and the smallest relative
+     eigenvalue gap of the samples about 3e-2, so eigenvectors move by about
+     3e-5. W_pred = (v^T v)^-1 v^T K also amplifies the moment error by the
+     condition number kappa = lam_v[0] / lam_v[-1] of v^T v (about 46 at
+     r_v = 64, 2300 at r_v = 128 for these spectra), so its absolute slack
+     is (2e-4 + 2e-6 kappa) times its largest entry.
 """
 
 import numpy as np
@@ -84,7 +88,11 @@ def _check_end_to_end(fit, k, v, heads):
         for name in ("A_v", "A_k", "W_pred"):
             if ref[name] is None:
                 continue
-            scale = np.abs(ref[name]).max() if name == "W_pred" else 1.0
+            if name == "W_pred":
+                kappa = ref["lam_v"][0] / ref["lam_v"][-1]
+                scale = np.abs(ref[name]).max() * (1.0 + 1e-2 * kappa)
+            else:
+                scale = 1.0
             err = np.abs(got[name][g] - ref[name])
             tol = rnd * np.abs(ref[name]) + 2e-4 * scale
             print(f"  head {g} {name}: max err {err.max():.3g} (scale {scale:.3g})", flush=True)
