@@ -26,6 +26,7 @@ KVLR_ERR_NUMERICAL = 5
 
 KVLR_DTYPE_BF16 = 0
 KVLR_DTYPE_F32 = 1
+KVLR_DTYPE_BF16_FP8 = 2
 KVLR_KEYS_LATENT = 0
 KVLR_KEYS_EXACT = 1
 

@@ -49,7 +49,10 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <class S, int G, int KW, int RV, bool ROWPAGE>
+// S: storage of the keys the scores read (original keys, or key latents);
+// SV: storage of the value latents. With FP8 latents S is BF16 (original
+// keys) or FP8 (key latents), SV is FP8, and the factors are bf16.
+template <class S, class SV, int G, int KW, int RV, bool ROWPAGE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(
     const uint8_t* __restrict__ keys, const uint8_t* __restrict__ v_lat,
     const float* __restrict__ qsrc, const int32_t* __restrict__ seq_lens,
@@ -60,6 +63,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     int log2P, int max_pages, int k_max,
     float scale_log2e, int rows_per_chunk, int max_splits, int batch) {
   constexpr int CH = S::CH;
+  static_assert(SV::CH == CH, "keys and value latents share the elements per chunk");
+  using SF = std::conditional_t<S::CB == 8, BF16, S>;  // factor storage
   constexpr int CKW = KW / CH;     // key chunks per token
   constexpr int CV = RV / CH;      // value-latent chunks per token
   constexpr int TPL = kWave / CV;  // token stride between a lane's P.V tokens
@@ -74,8 +79,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int ipr_log2 = 6 - log2P;  // items (pages) per row = 64 / P
-  const size_t slab_k = static_cast<size_t>(CKW) * P * 16;
-  const size_t slab_v = static_cast<size_t>(CV) * P * 16;
+  const size_t slab_k = static_cast<size_t>(CKW) * P * S::CB;
+  const size_t slab_v = static_cast<size_t>(CV) * P * SV::CB;
   const int my_c = lane % CV;
 
   // attended items (pages) of a (sequence, KV head) pair
@@ -107,7 +112,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float* __restrict__ qg = qsrc + static_cast<size_t>(b * Hq + g * G) * KW;
     const int row0 = split * rows_per_chunk;
     const int row1 = min(row0 + rows_per_chunk, nrows);
-    constexpr bool kMfma = ROWPAGE && S::CH == 8 && KVLR_ATTN_MFMA;
+    // (FP8 latents have only the matrix-core path)
+    constexpr bool kMfma = ROWPAGE && S::CH == 8 && (KVLR_ATTN_MFMA || SV::CB == 8);
 
     float m[G], lsum[G], z[G][CH];
 #pragma unroll
@@ -142,12 +148,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       return any;
     };
-    auto accumulate_pv = [&](const uint4 (&vc)[CV]) {
+    auto accumulate_pv = [&](const typename SV::Raw (&vc)[CV]) {
 #pragma unroll
       for (int k = 0; k < CV; ++k) {
         const int tok = lane / CV + k * TPL;
         float x[CH];
-        S::unpack(vc[k], x);
+        SV::unpack(vc[k], x);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float pp = s_p[wave][tok][h];
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       wave_lds_sync();
     };
-    auto score_keys = [&](const uint4 (&kc)[CKW], float (&s)[G]) {
+    auto score_keys = [&](const typename S::Raw (&kc)[CKW], float (&s)[G]) {
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = 0.f;
       static_for<0, CKW>([&](auto cc) {
@@ -219,27 +225,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (pg < 0) return RowRef{keys, v_lat, 0, 0};
         const size_t ph = static_cast<size_t>(pt[pg]);
         return RowRef{keys + (ph * Hkv + g) * slab_k,
-                      v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * 16, 1,
+                      v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * SV::CB, 1,
                       min(L - pg * kWave, kWave)};
       };
       auto a_addr = [&](const RowRef& rr, int j, int st) -> const uint8_t* {
         int ci = 4 * st + kq;
         if (ci >= CKW) ci = 0;
         return rr.kb + static_cast<uint32_t>(rr.on) *
-                           static_cast<uint32_t>((j * 16 + col) * 16 + ci * (kWave * 16));
+                           static_cast<uint32_t>((j * 16 + col) * S::CB + ci * (kWave * S::CB));
       };
       auto v_addr = [&](const RowRef& rr, int k) -> const uint8_t* {
-        return rr.vb + static_cast<uint32_t>(rr.on) * static_cast<uint32_t>((lane / CV + k * TPL) * 16);
+        return rr.vb + static_cast<uint32_t>(rr.on) * static_cast<uint32_t>((lane / CV + k * TPL) * SV::CB);
       };
       int r = row0 + wave;
-      uint4 A[4][KS], vc[CV];
+      typename S::Raw A[4][KS];
+      typename SV::Raw vc[CV];
       RowRef cur = row_ref(page_of(r));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int st = 0; st < KS; ++st) A[j][st] = load16_stream(a_addr(cur, j, st));
+        for (int st = 0; st < KS; ++st) A[j][st] = S::load_stream(a_addr(cur, j, st));
 #pragma unroll
-      for (int k = 0; k < CV; ++k) vc[k] = load16_stream(v_addr(cur, k));
+      for (int k = 0; k < CV; ++k) vc[k] = SV::load_stream(v_addr(cur, k));
       RowRef nxt = row_ref(page_of(r + kWaves));
       int pg2 = page_of(r + 2 * kWaves);
       float lcol = 0.f;  // sum of this lane's probabilities of head col
@@ -256,10 +263,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           const bf16x8 qlo = __builtin_bit_cast(bf16x8, s_qf[wave][st][1][lane]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, A[j][st]);
+            const bf16x8 a = S::to_bf16x8(A[j][st]);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi, acc[j], 0, 0, 0);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo, acc[j], 0, 0, 0);
-            A[j][st] = load16_stream(a_addr(nxt, j, st));
+            A[j][st] = S::load_stream(a_addr(nxt, j, st));
           }
         }
         // scaled score of (token 16j + 4kq + v, head col), -inf when masked
@@ -308,7 +315,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           const int tok = lane / CV + k * TPL;
           if (any) {
             float x[CH];
-            S::unpack(vc[k], x);
+            SV::unpack(vc[k], x);
             const bool tv = tok < cur.nvalid;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
               for (int e = 0; e < CH; ++e) z[h][e] = fmaf(pp, tv ? x[e] : 0.f, z[h][e]);
             }
           }
-          vc[k] = load16_stream(v_addr(nxt, k));
+          vc[k] = SV::load_stream(v_addr(nxt, k));
         }
         if (any) wave_lds_sync();
         cur = nxt;
@@ -532,12 +539,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (o_out) {
         // value compression tied to the output projection: o_h = z_h B_v, once per head
         __syncthreads();
-        const uint8_t* Bg = B_v + static_cast<size_t>(g) * RV * Dh * S::ELEM_BYTES;
+        const uint8_t* Bg = B_v + static_cast<size_t>(g) * RV * Dh * SF::ELEM_BYTES;
         for (int i = threadIdx.x; i < G * Dh; i += kThreads) {
           const int h = i / Dh, d = i - h * Dh;
           float acc = 0.f;
 #pragma unroll 8
-          for (int e = 0; e < RV; ++e) acc = fmaf(s_z[0][h][e], S::load1(Bg, static_cast<long>(e) * Dh + d), acc);
+          for (int e = 0; e < RV; ++e) acc = fmaf(s_z[0][h][e], SF::load1(Bg, static_cast<long>(e) * Dh + d), acc);
           o_out[(static_cast<size_t>(b) * Hq + g * G + h) * Dh + d] = acc;
         }
       }
@@ -547,21 +554,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <class S, int G, int KW, int RV>
+template <class S, class SV, int G, int KW, int RV>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   if (a.q_stride != KW) return hipErrorInvalidValue;  // queries are read with stride KW
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
   dim3 grid(a.grid);
+  if constexpr (SV::CB == 8) {  // FP8 latents: 64-token pages only
+    if (a.dm.P != kWave) return hipErrorInvalidValue;
+  }
   if (a.dm.P == kWave)
-    hipLaunchKernelGGL((attn_kernel<S, G, KW, RV, true>), grid, dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((attn_kernel<S, SV, G, KW, RV, true>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
                        a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials,
                        a.counters, a.z_out, a.lse_out, static_cast<const uint8_t*>(a.B_v), a.o_out,
                        a.dm.D, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
                        a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
-  else
-    hipLaunchKernelGGL((attn_kernel<S, G, KW, RV, false>), grid, dim3(kThreads), lds, s,
+  else if constexpr (SV::CB == 16)
+    hipLaunchKernelGGL((attn_kernel<S, SV, G, KW, RV, false>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
                        a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials,
                        a.counters, a.z_out, a.lse_out, static_cast<const uint8_t*>(a.B_v), a.o_out,
@@ -570,36 +580,38 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class S, int G, int RV>
+template <class S, class SV, int G, int RV>
 hipError_t by_kw(const AttnArgs& a, hipStream_t s) {
   // key width: head_dim for original keys, rank_k for key latents
   switch (a.dm.exact ? a.dm.D : a.dm.RK) {
-    case 16: return launch_t<S, G, 16, RV>(a, s);
-    case 32: return launch_t<S, G, 32, RV>(a, s);
-    case 64: return launch_t<S, G, 64, RV>(a, s);
-    case 128: return launch_t<S, G, 128, RV>(a, s);
+    case 16: return launch_t<S, SV, G, 16, RV>(a, s);
+    case 32: return launch_t<S, SV, G, 32, RV>(a, s);
+    case 64: return launch_t<S, SV, G, 64, RV>(a, s);
+    case 128: return launch_t<S, SV, G, 128, RV>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <class S, int G>
+template <class S, class SV, int G>
 hipError_t by_rv(const AttnArgs& a, hipStream_t s) {
   switch (a.dm.RV) {
-    case 16: return by_kw<S, G, 16>(a, s);
-    case 32: return by_kw<S, G, 32>(a, s);
-    case 64: return by_kw<S, G, 64>(a, s);
-    case 128: return by_kw<S, G, 128>(a, s);
+    case 16: return by_kw<S, SV, G, 16>(a, s);
+    case 32: return by_kw<S, SV, G, 32>(a, s);
+    case 64: return by_kw<S, SV, G, 64>(a, s);
+    case 128:
+      if constexpr (SV::CB == 16) return by_kw<S, SV, G, 128>(a, s);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
-template <class S>
+template <class S, class SV>
 hipError_t by_g(const AttnArgs& a, hipStream_t s) {
   switch (a.dm.G) {
-    case 1: return by_rv<S, 1>(a, s);
-    case 2: return by_rv<S, 2>(a, s);
-    case 4: return by_rv<S, 4>(a, s);
-    case 8: return by_rv<S, 8>(a, s);
+    case 1: return by_rv<S, SV, 1>(a, s);
+    case 2: return by_rv<S, SV, 2>(a, s);
+    case 4: return by_rv<S, SV, 4>(a, s);
+    case 8: return by_rv<S, SV, 8>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -612,8 +624,9 @@ int attn_rows_per_chunk(bool selected) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  if (a.dm.dtype == 0) return by_g<BF16>(a, s);
-  return by_g<F32>(a, s);
+  if (a.dm.lat == 2) return a.dm.exact ? by_g<BF16, FP8>(a, s) : by_g<FP8, FP8>(a, s);
+  if (a.dm.dtype == 0) return by_g<BF16, BF16>(a, s);
+  return by_g<F32, F32>(a, s);
 }
 
 }  // namespace kvlr

@@ -20,7 +20,10 @@
 // factor fragments of its head in LDS once, then loops over 64-token tiles,
 // 16 tokens per wave: the wave loads its tokens' rows straight into MFMA
 // A-operand registers, multiplies, rounds into a per-wave LDS tile and writes
-// each token's 16-byte chunks to its page slot.
+// each token's chunks to its page slot. With FP8 latents (bf16 inputs and
+// factors) the latents are rounded once from the float32 products to E4M3
+// (nearest even, saturating at +-448) and stored as 8-byte chunks; the
+// residual is taken against that stored latent, decoded exactly to bf16.
 
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
@@ -73,10 +76,36 @@ struct Mma<F32> {
   __device__ static float value(E e) { return e; }
 };
 
-template <class S, int D, int RV, int RK, bool ROUTED>
+// How rounded latents are held and stored: in the storage type S itself, or
+// (LS = FP8, with S = BF16) as E4M3 codes rounded once from the float32
+// products; the stored value latent is also the routed residual's operand.
+template <class S, class LS>
+struct Lat {
+  using MM = Mma<S>;
+  using E = typename MM::E;
+  static constexpr int CB = 16;
+  __device__ static E round(float f) { return MM::store(f); }
+  __device__ static typename MM::frag_t frag(const E* p) { return MM::lds(p); }
+  __device__ static void store_chunk(uint8_t* dst, const E* src) {
+    store16(dst, *reinterpret_cast<const uint4*>(src));
+  }
+};
+template <>
+struct Lat<BF16, FP8> {
+  using E = uint8_t;
+  static constexpr int CB = 8;
+  __device__ static E round(float f) { return static_cast<E>(f32_to_fp8_rne_sat(f)); }
+  __device__ static bf16x8 frag(const E* p) { return FP8::to_bf16x8(*reinterpret_cast<const uint2*>(p)); }
+  __device__ static void store_chunk(uint8_t* dst, const E* src) {
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+  }
+};
+
+template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 struct EncSmem {
   using MM = Mma<S>;
   using E = typename MM::E;
+  using LE = typename Lat<S, LS>::E;
   static constexpr int KSTEP = MM::KSTEP, KPL = MM::KPL, CH = S::CH;
   static constexpr int KSD = D / KSTEP;                    // k-steps over head_dim
   static constexpr int KSV = (RV + KSTEP - 1) / KSTEP;     // k-steps over rank_v (zero padded)
@@ -87,8 +116,8 @@ struct EncSmem {
   alignas(16) E mlo[(ROUTED && KPL > 1) ? KSV : 1][RK / 16][kWave][KPL];
   struct Tiles {
     // per-wave row-major tiles of the rounded latents (16 tokens)
-    alignas(16) E vt[kWaves][16][RV + CH];
-    alignas(16) E ct[kWaves][16][RK + CH];
+    alignas(16) LE vt[kWaves][16][RV + CH];
+    alignas(16) LE ct[kWaves][16][RK + CH];
   };
   union {
     float mstage[ROUTED ? RV : 1][RK + 1];  // set-up only
@@ -101,7 +130,7 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <class S, int D, int RV, int RK, bool ROUTED>
+template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(
     const uint8_t* __restrict__ A_v, const uint8_t* __restrict__ A_k,
     const uint8_t* __restrict__ W_pred, const uint8_t* __restrict__ k_new,
@@ -110,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     uint8_t* __restrict__ v_lat, uint8_t* __restrict__ k_lat, uint8_t* __restrict__ k_exact,
     int Hkv, int P, int log2P, int max_pages, int batch, int total_new) {
   using MM = Mma<S>;
-  using SM = EncSmem<S, D, RV, RK, ROUTED>;
+  using SM = EncSmem<S, LS, D, RV, RK, ROUTED>;
+  using LT = Lat<S, LS>;
   using E = typename MM::E;
   using frag_t = typename MM::frag_t;
   constexpr int KSTEP = MM::KSTEP, KPL = MM::KPL, CH = S::CH, EB = S::ELEM_BYTES;
@@ -202,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 
   // sequence of token i: largest b with cu_new[b] <= i (offsets staged in LDS);
   // returns its page-table entry (entry 0 of sequence 0 past the last token)
+  // and the token's slot in the page
   auto locate = [&](int tile, size_t& slot_off) -> const int32_t* {
     const int i = tile * 64 + wave * 16 + r;
     slot_off = 0;
@@ -212,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       if (s_seq[mid] <= i) lo = mid; else hi = mid;
     }
     const int pos = s_seq[batch + 1 + lo] + (i - s_seq[lo]);
-    slot_off = static_cast<size_t>(pos & (P - 1)) * 16;
+    slot_off = static_cast<size_t>(pos & (P - 1));
     return page_table + static_cast<size_t>(lo) * max_pages + (pos >> log2P);
   };
   // the first tile's page-table entry is requested before M is formed
@@ -253,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     // original key: stored straight from the loaded fragments
     if constexpr (ROUTED) {
       if (valid) {
-        uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off;
+        uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off * 16;
         if constexpr (FRAG_IS_CHUNK) {
           // fragment ks of this lane is chunk ks * KSTEP / CH + kq of the key row
 #pragma unroll
@@ -278,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.u.t.vt[wave][4 * kq + j][nt * 16 + r] = MM::store(vacc[nt][j]);
+      for (int j = 0; j < 4; ++j) sm.u.t.vt[wave][4 * kq + j][nt * 16 + r] = LT::round(vacc[nt][j]);
 
     // ---- residual latent (routed) or key latent (dense)
     f32x4 cacc[NTK];
@@ -290,19 +321,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       for (int nt = 0; nt < NTK; ++nt) cacc[nt] = MM::mma(kf[ks], MM::lds(&sm.ak[ks][nt][lane][0]), cacc[nt]);
     wave_lds_sync();
     if (valid) {
-      uint8_t* dst = v_lat + (phys * Hkv + g) * CV * P * 16 + slot_off;
+      uint8_t* dst = v_lat + (phys * Hkv + g) * CV * P * LT::CB + slot_off * LT::CB;
 #pragma unroll
       for (int c0 = 0; c0 < CV; c0 += 4) {
         const int c = c0 + kq;
-        if (c < CV)
-          store16(dst + static_cast<size_t>(c) * P * 16, *reinterpret_cast<const uint4*>(&sm.u.t.vt[wave][r][c * CH]));
+        if (c < CV) LT::store_chunk(dst + static_cast<size_t>(c) * P * LT::CB, &sm.u.t.vt[wave][r][c * CH]);
       }
     }
     if constexpr (ROUTED) {
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks) {
         const int k = ks * KSTEP + KPL * kq;
-        const frag_t a = (k < RV) ? MM::lds(&sm.u.t.vt[wave][r][k]) : MM::zero();
+        const frag_t a = (k < RV) ? LT::frag(&sm.u.t.vt[wave][r][k]) : MM::zero();
 #pragma unroll
         for (int nt = 0; nt < NTK; ++nt) {
           cacc[nt] = MM::mma(a, MM::lds(&sm.mhi[ks][nt][lane][0]), cacc[nt]);
@@ -313,15 +343,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm.u.t.ct[wave][4 * kq + j][nt * 16 + r] = MM::store(cacc[nt][j]);
+      for (int j = 0; j < 4; ++j) sm.u.t.ct[wave][4 * kq + j][nt * 16 + r] = LT::round(cacc[nt][j]);
     wave_lds_sync();
     if (valid) {
-      uint8_t* dst = k_lat + (phys * Hkv + g) * CK * P * 16 + slot_off;
+      uint8_t* dst = k_lat + (phys * Hkv + g) * CK * P * LT::CB + slot_off * LT::CB;
 #pragma unroll
       for (int c0 = 0; c0 < CK; c0 += 4) {
         const int c = c0 + kq;
-        if (c < CK)
-          store16(dst + static_cast<size_t>(c) * P * 16, *reinterpret_cast<const uint4*>(&sm.u.t.ct[wave][r][c * CH]));
+        if (c < CK) LT::store_chunk(dst + static_cast<size_t>(c) * P * LT::CB, &sm.u.t.ct[wave][r][c * CH]);
       }
     }
     wave_lds_sync();
@@ -338,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   }
 }
 
-template <class S, int D, int RV, int RK, bool ROUTED>
+template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   const int ntiles = (a.total_new + 63) / 64;
@@ -346,7 +375,7 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   if (per_head > ntiles) per_head = ntiles;
   dim3 grid(per_head, a.dm.Hkv);
   const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
-  hipLaunchKernelGGL((encode_kernel<S, D, RV, RK, ROUTED>), grid, dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((encode_kernel<S, LS, D, RV, RK, ROUTED>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(a.A_v), static_cast<const uint8_t*>(a.A_k),
                      static_cast<const uint8_t*>(a.W_pred), static_cast<const uint8_t*>(a.k_new),
                      static_cast<const uint8_t*>(a.v_new), a.cu_new, a.lens_before, a.page_table,
@@ -356,40 +385,40 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class S, int D, int RV, int RK>
+template <class S, class LS, int D, int RV, int RK>
 hipError_t by_mode(const EncodeArgs& a, hipStream_t s) {
-  return a.dm.exact ? launch_t<S, D, RV, RK, true>(a, s) : launch_t<S, D, RV, RK, false>(a, s);
+  return a.dm.exact ? launch_t<S, LS, D, RV, RK, true>(a, s) : launch_t<S, LS, D, RV, RK, false>(a, s);
 }
 
-template <class S, int D, int RV>
+template <class S, class LS, int D, int RV>
 hipError_t by_rk(const EncodeArgs& a, hipStream_t s) {
   switch (a.dm.RK) {
-    case 16: return by_mode<S, D, RV, 16>(a, s);
-    case 32: return by_mode<S, D, RV, 32>(a, s);
-    case 64: return by_mode<S, D, RV, 64>(a, s);
+    case 16: return by_mode<S, LS, D, RV, 16>(a, s);
+    case 32: return by_mode<S, LS, D, RV, 32>(a, s);
+    case 64: return by_mode<S, LS, D, RV, 64>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <class S, int D>
+template <class S, class LS, int D>
 hipError_t by_rv(const EncodeArgs& a, hipStream_t s) {
   switch (a.dm.RV) {
-    case 16: return by_rk<S, D, 16>(a, s);
-    case 32: return by_rk<S, D, 32>(a, s);
-    case 64: return by_rk<S, D, 64>(a, s);
+    case 16: return by_rk<S, LS, D, 16>(a, s);
+    case 32: return by_rk<S, LS, D, 32>(a, s);
+    case 64: return by_rk<S, LS, D, 64>(a, s);
     case 128:
       // full-width values: bf16 storage only (the f32 tiles would not fit in LDS)
-      if constexpr (D == 128 && S::CH == 8) return by_rk<S, D, 128>(a, s);
+      if constexpr (D == 128 && S::CH == 8 && LS::CB == 16) return by_rk<S, LS, D, 128>(a, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <class S>
+template <class S, class LS>
 hipError_t by_d(const EncodeArgs& a, hipStream_t s) {
   switch (a.dm.D) {
-    case 64: return by_rv<S, 64>(a, s);
-    case 128: return by_rv<S, 128>(a, s);
+    case 64: return by_rv<S, LS, 64>(a, s);
+    case 128: return by_rv<S, LS, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -398,8 +427,9 @@ hipError_t by_d(const EncodeArgs& a, hipStream_t s) {
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
   if (a.total_new == 0 || a.batch == 0) return hipSuccess;
-  if (a.dm.dtype == 0) return by_d<BF16>(a, s);
-  return by_d<F32>(a, s);
+  if (a.dm.lat == 2) return by_d<BF16, FP8>(a, s);
+  if (a.dm.dtype == 0) return by_d<BF16, BF16>(a, s);
+  return by_d<F32, F32>(a, s);
 }
 
 }  // namespace kvlr

@@ -304,8 +304,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   __shared__ int s_last;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
-  const size_t slab_v = static_cast<size_t>(CV) * P * 16;  // bytes of one head's page
-  const size_t slab_k = static_cast<size_t>(CK) * P * 16;
+  const size_t slab_v = static_cast<size_t>(CV) * P * S::CB;  // bytes of one head's page
+  const size_t slab_k = static_cast<size_t>(CK) * P * S::CB;
 
   build_chunk_prefix(batch, s_base, [&](int b) {
     const int rows = (seq_lens[b] + kWave - 1) / kWave;
@@ -326,21 +326,23 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
     float* __restrict__ sc = scores + static_cast<size_t>(pair) * max_pages;
     // the vector-ALU paths keep the projected queries spread over the lanes
-    constexpr bool kMfma = ROWPAGE && S::CH == 8 && KVLR_ROUTE_MFMA;
+    // (FP8 latents have only the matrix-core path)
+    constexpr bool kMfma = ROWPAGE && S::CH == 8 && (KVLR_ROUTE_MFMA || S::CB == 8);
     float qv[kMfma ? 1 : NQ];
     if constexpr (!kMfma) load_q_rows(qp, qv);
     const int row0 = split * rows_per_chunk;
     const int row1 = min(row0 + rows_per_chunk, nrows);
 
     if constexpr (kMfma) {
-      // Matrix-core scoring (bf16 storage, one page per row). A 64-token row
-      // is four 16-token tiles; per tile, scores[token][head] = sum over the
-      // concatenated [v | c] latent (K, in steps of 32) of latent x query,
+      // Matrix-core scoring (bf16 or FP8 latents, one page per row). A 64-token
+      // row is four 16-token tiles; per tile, scores[token][head] = sum over
+      // the concatenated [v | c] latent (K, in steps of 32) of latent x query,
       // as v_mfma_f32_16x16x32_bf16 with tokens as rows (lane l: token l%16,
-      // 8 latent elements from k-group l/16: one 16-byte chunk of the page)
-      // and heads as columns (the projected queries split into bf16 high and
-      // low halves, two products per step). Heads past the group and tokens
-      // past the sequence end are masked before the page max.
+      // 8 latent elements from k-group l/16: one chunk of the page, 16 bytes
+      // of bf16 or 8 bytes of FP8 decoded exactly to bf16) and heads as
+      // columns (the projected queries split into bf16 high and low halves,
+      // two products per step). Heads past the group and tokens past the
+      // sequence end are masked before the page max.
       // k-steps: ceil(CV/4) over the value latent, then ceil(CK/4) over the
       // residual, so each step reads one slab (a uniform base address)
       constexpr int KSV = (CV + 3) / 4, KSK = (CK + 3) / 4, KS = KSV + KSK;
@@ -381,16 +383,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         int ci = 4 * (on_v ? st : st - KSV) + kq;
         if (ci >= (on_v ? CV : CK)) ci = 0;
         const uint32_t off = static_cast<uint32_t>(rr.on) *
-                             static_cast<uint32_t>((j * 16 + col) * 16 + ci * (kWave * 16));
+                             static_cast<uint32_t>((j * 16 + col) * S::CB + ci * (kWave * S::CB));
         return (on_v ? rr.vb : rr.kb) + off;
       };
       int r = row0 + wave;
-      uint4 A[4][KS];
+      typename S::Raw A[4][KS];
       RowRef cur = row_ref(r);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int st = 0; st < KS; ++st) A[j][st] = load16_stream(a_addr(cur, j, st));
+        for (int st = 0; st < KS; ++st) A[j][st] = S::load_stream(a_addr(cur, j, st));
       RowRef nxt = row_ref(r + kWaves);
       for (; r < row1; r += kWaves) {
         const RowRef nn = row_ref(r + 2 * kWaves);  // page-table entry two rows ahead
@@ -400,10 +402,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
           acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int st = 0; st < KS; ++st) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, A[j][st]);
+            const bf16x8 a = S::to_bf16x8(A[j][st]);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[st], acc[j], 0, 0, 0);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[st], acc[j], 0, 0, 0);
-            A[j][st] = load16_stream(a_addr(nxt, j, st));
+            A[j][st] = S::load_stream(a_addr(nxt, j, st));
           }
         }
         const int nvalid = L - r * kWave;
@@ -560,18 +562,21 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
   dim3 grid(a.grid);
-  if (a.dm.P == kWave)
+  if (a.dm.P == kWave) {
     hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                        a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts, a.dm.Hq,
                        a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
                        a.rows_per_chunk, a.batch);
-  else
-    hipLaunchKernelGGL((route_kernel<S, G, RV, RK, false>), grid, dim3(kThreads), lds, s,
-                       static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
-                       a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts, a.dm.Hq,
-                       a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
-                       a.rows_per_chunk, a.batch);
+  } else {
+    if constexpr (S::CB == 8) return hipErrorInvalidValue;  // FP8 latents: 64-token pages only
+    else
+      hipLaunchKernelGGL((route_kernel<S, G, RV, RK, false>), grid, dim3(kThreads), lds, s,
+                         static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
+                         a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
+                         a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
+                         a.k_max, a.rows_per_chunk, a.batch);
+  }
   return hipGetLastError();
 }
 
@@ -615,7 +620,8 @@ int route_rows_per_chunk() { return KVLR_ROUTE_RPC; }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  if (a.dm.dtype == 0) return by_g<BF16>(a, s);
+  if (a.dm.lat == 2) return by_g<FP8>(a, s);
+  if (a.dm.lat == 0) return by_g<BF16>(a, s);
   return by_g<F32>(a, s);
 }
 

@@ -34,7 +34,8 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
       s->rank_v < 1 || s->rank_k < 1 || s->num_phys_pages < 1)
     return KVLR_ERR_INVALID_ARGUMENT;
   if (s->num_q_heads % s->num_kv_heads != 0) return KVLR_ERR_INVALID_ARGUMENT;
-  if (s->dtype != KVLR_DTYPE_BF16 && s->dtype != KVLR_DTYPE_F32) return KVLR_ERR_INVALID_ARGUMENT;
+  if (s->dtype != KVLR_DTYPE_BF16 && s->dtype != KVLR_DTYPE_F32 && s->dtype != KVLR_DTYPE_BF16_FP8)
+    return KVLR_ERR_INVALID_ARGUMENT;
   if (s->key_mode != KVLR_KEYS_LATENT && s->key_mode != KVLR_KEYS_EXACT) return KVLR_ERR_INVALID_ARGUMENT;
   if (s->rank_v > s->head_dim || s->rank_k > s->head_dim) return KVLR_ERR_INVALID_ARGUMENT;
   const int G = s->num_q_heads / s->num_kv_heads;
@@ -45,6 +46,8 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
     return KVLR_ERR_UNSUPPORTED;
   if (s->rank_v == 128 && s->dtype != KVLR_DTYPE_BF16) return KVLR_ERR_UNSUPPORTED;
   if (!one_of(s->page_size, 16, 32, 64)) return KVLR_ERR_UNSUPPORTED;
+  // FP8 latents run on the matrix-core paths, which take one 64-token page per row
+  if (s->dtype == KVLR_DTYPE_BF16_FP8 && s->page_size != 64) return KVLR_ERR_UNSUPPORTED;
   dm->Hq = s->num_q_heads;
   dm->Hkv = s->num_kv_heads;
   dm->G = G;
@@ -52,7 +55,8 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
   dm->P = s->page_size;
   dm->RV = s->rank_v;
   dm->RK = s->rank_k;
-  dm->dtype = s->dtype;
+  dm->dtype = s->dtype == KVLR_DTYPE_F32 ? 1 : 0;   // factors, original keys, new tokens
+  dm->lat = s->dtype == KVLR_DTYPE_BF16_FP8 ? 2 : dm->dtype;
   dm->exact = s->key_mode == KVLR_KEYS_EXACT ? 1 : 0;
   return KVLR_OK;
 }

@@ -10,10 +10,30 @@ namespace kvlr {
 
 constexpr int kWave = 64;
 
-// Storage policies. A chunk is 16 bytes: 8 bf16 or 4 f32 elements.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Streaming loads: marked non-temporal, for data read once per launch.
+__device__ inline uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 load8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// Storage policies. A chunk holds CH elements in CB bytes: 8 bf16 or 4 f32
+// in 16 bytes, or 8 FP8 latents in 8 bytes. Raw is the chunk as loaded.
 struct BF16 {
   static constexpr int CH = 8;
   static constexpr int ELEM_BYTES = 2;
+  static constexpr int CB = 16;
+  using Raw = uint4;
+  __device__ static inline Raw load_stream(const void* p) { return load16_stream(p); }
+  __device__ static inline bf16x8 to_bf16x8(const Raw& r) { return __builtin_bit_cast(bf16x8, r); }
   // element e of a chunk as float (bf16 -> f32 is a 16-bit shift, exact)
   __device__ static inline void unpack(const uint4& c, float (&x)[CH]) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -32,6 +52,9 @@ struct BF16 {
 struct F32 {
   static constexpr int CH = 4;
   static constexpr int ELEM_BYTES = 4;
+  static constexpr int CB = 16;
+  using Raw = uint4;
+  __device__ static inline Raw load_stream(const void* p) { return load16_stream(p); }
   __device__ static inline void unpack(const uint4& c, float (&x)[CH]) {
     x[0] = __uint_as_float(c.x);
     x[1] = __uint_as_float(c.y);
@@ -43,6 +66,50 @@ struct F32 {
   }
 };
 
+// OCP 8-bit floating point E4M3 (4 exponent bits, bias 7, 3 stored
+// significand bits, no infinities, largest finite value 448): latents only.
+// Every E4M3 value is exact in bfloat16 and float32, so decoding is exact:
+// v_cvt_pk_f32_fp8 decodes all 256 codes as OCP E4M3 on gfx950 (two per
+// instruction, bytes 0,1 or 2,3 of a word), and a bf16 operand is the upper
+// half of each float.
+struct FP8 {
+  static constexpr int CH = 8;
+  static constexpr int ELEM_BYTES = 1;
+  static constexpr int CB = 8;
+  using Raw = uint2;
+  __device__ static inline Raw load_stream(const void* p) { return load8_stream(p); }
+  __device__ static inline void unpack(const Raw& r, float (&x)[CH]) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const uint32_t w[2] = {r.x, r.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+      x[4 * i] = lo[0];
+      x[4 * i + 1] = lo[1];
+      x[4 * i + 2] = hi[0];
+      x[4 * i + 3] = hi[1];
+    }
+  }
+  // bytes 0..7 -> bf16 elements 0..7
+  __device__ static inline bf16x8 to_bf16x8(const Raw& r) {
+    float x[CH];
+    unpack(r, x);
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      h[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
+    return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  }
+};
+
+// float32 -> E4M3 code, round to nearest even, saturating at +-448 (the
+// converter itself maps magnitudes past 464 to NaN); NaN stays NaN.
+__device__ inline uint32_t f32_to_fp8_rne_sat(float f) {
+  const float c = (f != f) ? f : fminf(fmaxf(f, -448.f), 448.f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.f, 0, false)) & 0xffu;
+}
+
 // float32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ inline uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -50,9 +117,6 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // 8 floats as bfloat16: hi = RNE(x), lo = RNE(x - hi); hi + lo carries about
 // 16 significant bits of x, so a product with a bf16 latent through the two
@@ -79,12 +143,6 @@ __device__ inline void store16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
-// Streaming 16-byte load: marked non-temporal, for data read once per launch.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ inline uint4 load16_stream(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup hand-off without cache flushes.

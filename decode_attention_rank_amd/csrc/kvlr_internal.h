@@ -10,7 +10,8 @@ namespace kvlr {
 // Shape facts every launcher needs, already validated by the API layer.
 struct Dims {
   int Hq, Hkv, G, D, P, RV, RK;
-  int dtype;      // KVLR_DTYPE_*
+  int dtype;      // factors, original keys, new tokens: 0 bf16, 1 f32
+  int lat;        // latents (v_lat, k_lat): 0 bf16, 1 f32, 2 FP8 E4M3
   int exact;      // 1 = routed (residual latent + original keys)
 };
 

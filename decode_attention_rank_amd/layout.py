@@ -1,8 +1,9 @@
 """Host-side view of the paged cache layout that libkvlr reads and writes.
 
-Physical arrays have shape [num_phys_pages, H_kv, R / CH, P, CH], CH = 16 bytes
-of elements (8 bf16 or 4 f32): for each KV head, the P tokens of one 16-byte
-chunk column are contiguous. Logical page j of a sequence lives in physical
+Physical arrays have shape [num_phys_pages, H_kv, R / CH, P, CH]: a chunk is
+16 bytes of elements (8 bf16 or 4 f32), or 8 bytes for 8-bit latents (8 FP8
+E4M3 values); for each KV head, the P tokens of one chunk column are
+contiguous. Logical page j of a sequence lives in physical
 page page_table[b, j]. These helpers only move data (staging a prefix into
 pages, reading pages back); they compute nothing.
 """
@@ -15,7 +16,13 @@ CHUNK_BYTES = 16
 
 
 def chunk_elems(dtype: torch.dtype) -> int:
-    return CHUNK_BYTES // torch.empty(0, dtype=dtype).element_size()
+    es = torch.empty(0, dtype=dtype).element_size()
+    return 8 if es == 1 else CHUNK_BYTES // es
+
+
+def _bytes(t: torch.Tensor) -> torch.Tensor:
+    """8-bit tensors are moved as bytes (torch has no indexed copies for them)."""
+    return t.view(torch.uint8) if t.element_size() == 1 else t
 
 
 def alloc_pages(num_phys: int, num_kv_heads: int, width: int, page_size: int, dtype: torch.dtype,
@@ -47,7 +54,7 @@ def pack_sequence(phys: torch.Tensor, page_ids: torch.Tensor, rows: torch.Tensor
     x[:, :L] = rows.to(device=phys.device, dtype=phys.dtype)
     x = x.view(H, n_pg, P, nch, ch).permute(1, 0, 3, 2, 4).contiguous()
     idx = page_ids[:n_pg].to(device=phys.device, dtype=torch.long)
-    phys.index_copy_(0, idx, x)
+    _bytes(phys).index_copy_(0, idx, _bytes(x))
 
 
 def unpack_sequence(phys: torch.Tensor, page_ids: torch.Tensor, L: int, start: int = 0) -> torch.Tensor:
@@ -57,6 +64,6 @@ def unpack_sequence(phys: torch.Tensor, page_ids: torch.Tensor, L: int, start: i
         return phys.new_zeros((H, 0, nch * ch))
     n_pg = -(-L // P)
     idx = page_ids[:n_pg].to(device=phys.device, dtype=torch.long)
-    x = phys.index_select(0, idx)                      # [n_pg, H, nch, P, ch]
+    x = _bytes(phys).index_select(0, idx).view(phys.dtype)  # [n_pg, H, nch, P, ch]
     x = x.permute(1, 0, 3, 2, 4).reshape(H, n_pg * P, nch * ch)
     return x[:, start:L]

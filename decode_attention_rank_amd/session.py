@@ -21,6 +21,10 @@ from .workloads import Workload
 
 
 def kvlr_dtype(wl: Workload) -> int:
+    if wl.lat_storage == "fp8":
+        if wl.storage != "bf16":
+            raise ValueError("FP8 latents go with bf16 keys and factors")
+        return K.KVLR_DTYPE_BF16_FP8
     return K.KVLR_DTYPE_BF16 if wl.storage == "bf16" else K.KVLR_DTYPE_F32
 
 
@@ -45,6 +49,8 @@ class DecodeSession:
         self.num_phys = num_phys
         dt = synth.storage_dtype(wl)
         self.dtype = dt
+        lt = synth.latent_dtype(wl)
+        self.lat_dtype = lt
         self.shape = K.make_shape(
             num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
             page_size=wl.page_size, rank_v=wl.rank_v, rank_k=wl.rank_k, dtype=kvlr_dtype(wl),
@@ -60,8 +66,8 @@ class DecodeSession:
         self.Qv, self.Qk = synth.bases(wl)
 
         # paged cache
-        self.v_lat = layout.alloc_pages(num_phys, H, wl.rank_v, P, dt, dev, tail_fill)
-        self.k_lat = layout.alloc_pages(num_phys, H, wl.rank_k, P, dt, dev, tail_fill)
+        self.v_lat = layout.alloc_pages(num_phys, H, wl.rank_v, P, lt, dev, tail_fill)
+        self.k_lat = layout.alloc_pages(num_phys, H, wl.rank_k, P, lt, dev, tail_fill)
         self.k_exact = (layout.alloc_pages(num_phys, H, wl.head_dim, P, dt, dev, tail_fill)
                         if wl.exact else None)
         self.kcache = K.make_cache(self.v_lat, self.k_lat, self.k_exact)
@@ -232,27 +238,30 @@ class DecodeSession:
 
     def route_bytes(self) -> int:
         """Algorithmic bytes the routing kernel must read: both latents of every valid token."""
-        eb = torch.empty(0, dtype=self.dtype).element_size()
-        return sum(self.seq_lens) * self.wl.num_kv_heads * (self.wl.rank_v + self.wl.rank_k) * eb
+        lb = torch.empty(0, dtype=self.lat_dtype).element_size()
+        return sum(self.seq_lens) * self.wl.num_kv_heads * (self.wl.rank_v + self.wl.rank_k) * lb
 
     def attend_bytes(self) -> int:
         """Algorithmic bytes of attention: keys and value latents of the attended tokens."""
         wl = self.wl
         eb = torch.empty(0, dtype=self.dtype).element_size()
+        lb = torch.empty(0, dtype=self.lat_dtype).element_size()
         if not wl.routed:
-            key = wl.head_dim if wl.exact else wl.rank_k
-            return sum(self.seq_lens) * wl.num_kv_heads * (key + wl.rank_v) * eb
+            key = wl.head_dim * eb if wl.exact else wl.rank_k * lb
+            return sum(self.seq_lens) * wl.num_kv_heads * (key + wl.rank_v * lb)
         tot = 0
         P = wl.page_size
         for L in self.seq_lens:
             N = -(-L // P)
             k = 0 if N == 0 else min(N, max(1, -(-(N * wl.topk_num) // wl.topk_den)))
             tot += k * P  # upper bound for a ragged last page; exact when pages are full
-        return tot * wl.num_kv_heads * (wl.head_dim + wl.rank_v) * eb
+        return tot * wl.num_kv_heads * (wl.head_dim * eb + wl.rank_v * lb)
 
     def append_bytes(self) -> int:
         wl = self.wl
         eb = torch.empty(0, dtype=self.dtype).element_size()
+        lb = torch.empty(0, dtype=self.lat_dtype).element_size()
         read = self.total_new * wl.num_kv_heads * 2 * wl.head_dim * eb
-        write = self.total_new * wl.num_kv_heads * (wl.rank_v + wl.rank_k + (wl.head_dim if wl.exact else 0)) * eb
+        write = self.total_new * wl.num_kv_heads * ((wl.rank_v + wl.rank_k) * lb
+                                                   + (wl.head_dim * eb if wl.exact else 0))
         return read + write

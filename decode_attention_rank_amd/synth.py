@@ -21,6 +21,8 @@ Recipe (per KV head g; all draws seeded by (workload seed, role, sequence)):
     v = [C, 0] + s*N (width rank_v); routed key residual c = [E, 0] + s*N
     (width rank_k); dense key latent k = [kc, 0] + s*N; original key
     K = kc Q_k[:, :rs]^T + s*N. All rounded to the storage type.
+  * Latents are stored in the workload's latent type (bf16, f32, or FP8
+    E4M3 with bf16 keys and factors).
   * Factors: A_v = Q_v[:, :rank_v], B_v = A_v^T. Routed: W_pred rows
     i < shared_rank are Q_k[:, i]^T (zero below), A_k =
     Q_k[:, shared_rank:shared_rank + rank_k], B_k = A_k^T. Dense:
@@ -58,7 +60,7 @@ _ROLE = {"bases": 1, "q": 2, "coef": 3, "noise": 4, "lens": 5, "planted": 6,
 FIT_DECAY = 0.97      # per-coordinate scale ratio of the calibration samples
 FIT_KEY_SCALE = 0.8   # key-only coordinates relative to the shared ones
 
-TORCH_STORAGE = {"bf16": torch.bfloat16, "f32": torch.float32}
+TORCH_STORAGE = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}
 
 
 def _seed(wl_seed: int, role: str, *idx: int) -> int:
@@ -74,6 +76,12 @@ def _gen(device, wl_seed: int, role: str, *idx: int) -> torch.Generator:
 
 def storage_dtype(wl: Workload) -> torch.dtype:
     return TORCH_STORAGE[wl.storage]
+
+
+def latent_dtype(wl: Workload) -> torch.dtype:
+    """Type of the stored latents (torch's float32 -> float8 conversion rounds
+    to nearest even; synthetic latents stay far inside the E4M3 range)."""
+    return TORCH_STORAGE[wl.lat_storage]
 
 
 def bases(wl: Workload):
@@ -218,8 +226,9 @@ def synth_latent_cache(wl: Workload, b: int, n: int, device="cpu", *, q=None, Qk
     H, d, rv, rk, rs, ns, s = (wl.num_kv_heads, wl.head_dim, wl.rank_v, wl.rank_k,
                                wl.signal_rank, wl.shared_rank, wl.noise_std)
     dt = storage_dtype(wl)
-    v = torch.empty(H, n, rv, dtype=dt, device=device)
-    kl = torch.empty(H, n, rk, dtype=dt, device=device)
+    lt = latent_dtype(wl)
+    v = torch.empty(H, n, rv, dtype=lt, device=device)
+    kl = torch.empty(H, n, rk, dtype=lt, device=device)
     ke = torch.empty(H, n, d, dtype=dt, device=device) if wl.exact else None
     for g in range(H):
         C, kc = _coefficients(wl, b, g, 0, n, device, Qk, q)
@@ -227,12 +236,12 @@ def synth_latent_cache(wl: Workload, b: int, n: int, device="cpu", *, q=None, Qk
         vv = s * torch.randn(n, rv, generator=gen, device=device)
         m = min(rs, rv)
         vv[:, :m] += C[:, :m]
-        v[g] = vv.to(dt)
+        v[g] = vv.to(lt)
         kk = s * torch.randn(n, rk, generator=gen, device=device)
         src = kc[:, ns:] if wl.exact else kc
         m = min(src.shape[1], rk)
         kk[:, :m] += src[:, :m]
-        kl[g] = kk.to(dt)
+        kl[g] = kk.to(lt)
         if wl.exact:
             basis = Qk[g, :, :rs].to(torch.float32).to(device)
             K = kc @ basis.T.contiguous() + s * torch.randn(n, d, generator=gen, device=device)

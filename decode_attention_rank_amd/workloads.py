@@ -35,6 +35,7 @@ class Workload:
     route: bool = True          # exact keys: route (True) or attend every page (False)
     value_basis: str = "random"  # "identity": the value latent is the value itself
     hidden: int = 0             # output features of W_o (0: num_q_heads * head_dim)
+    latent_storage: str = ""    # "fp8": latents as OCP FP8 E4M3 (else as `storage`)
     ctx_min: int = 0
     ctx_max: int = 0
     seed: int = 0
@@ -51,6 +52,11 @@ class Workload:
     @property
     def routed(self) -> bool:
         return self.exact and self.route
+
+    @property
+    def lat_storage(self) -> str:
+        """Storage type of the latents (v_lat, k_lat)."""
+        return self.latent_storage or self.storage
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -97,6 +103,19 @@ WORKLOADS = {
         head_dim=128, page_size=64, rank_v=128, rank_k=16, storage="bf16",
         key_mode="exact", context=32768, route=False, value_basis="identity",
         signal_rank=48, shared_rank=16, noise_std=0.05, seed=5),
+    # The routed 8B and 70B-share caches with FP8 latents: same seeds, so the
+    # same inputs as their bf16 counterparts; keys and factors stay bf16.
+    "llama3-8b-routed-fp8-32k": Workload(
+        name="llama3-8b-routed-fp8-32k", batch=16, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, page_size=64, rank_v=64, rank_k=32, storage="bf16",
+        latent_storage="fp8", key_mode="exact", context=32768, topk_num=1, topk_den=8,
+        signal_rank=48, shared_rank=32, noise_std=0.05, seed=2),
+    "llama3-70b-share-routed-fp8-128k": Workload(
+        name="llama3-70b-share-routed-fp8-128k", batch=64, num_q_heads=8, num_kv_heads=1,
+        head_dim=128, page_size=64, rank_v=32, rank_k=32, storage="bf16",
+        latent_storage="fp8", key_mode="exact", context=131072, topk_num=1, topk_den=16,
+        signal_rank=48, shared_rank=32, noise_std=0.05,
+        planted_frac=0.05, planted_boost=4.0, hidden=8192, seed=3),
 }
 
 DEFAULT_BENCH_WORKLOAD = "llama3-8b-routed-32k"

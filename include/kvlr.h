@@ -28,14 +28,25 @@
  *
  * Storage types (kvlr_shape.dtype): KVLR_DTYPE_BF16 or KVLR_DTYPE_F32 for
  * the latents, the original keys, the factors and the new keys/values.
+ * KVLR_DTYPE_BF16_FP8 keeps everything bf16 except the latents (v_lat,
+ * k_lat), which are stored as OCP 8-bit floats E4M3 (4 exponent bits, bias
+ * 7, 3 significand bits, no infinities, largest finite value 448): the
+ * append encode rounds each latent once from its float32 value, to nearest
+ * even, saturating at +-448 (NaN stays NaN); readers decode exactly. This is
+ * a lossy latent codec in the spirit of the page "PackKV: Reducing KV Cache
+ * Memory Footprint through LLM-Aware Lossy Compression" (abstract); it halves
+ * the bytes that routing and the value side of attention stream. Supported
+ * with page_size 64 and rank_v <= 64 only.
  * Queries, projected queries, z, lse and outputs are float32.
  *
- * Cache layout (one "chunk" = 16 bytes = CH elements: 8 bf16 or 4 f32):
+ * Cache layout (one "chunk" = CH elements in 16 bytes: 8 bf16 or 4 f32; FP8
+ * latents: 8 elements in 8 bytes):
  *   v_lat   [num_phys_pages][H_kv][rank_v  / CH][page_size][CH]
  *   k_lat   [num_phys_pages][H_kv][rank_k  / CH][page_size][CH]
  *   k_exact [num_phys_pages][H_kv][head_dim/ CH][page_size][CH]
  * Token slot s of a page holds, for chunk c, elements c*CH .. c*CH+CH-1 of
- * its row, so the P tokens of one chunk column sit in P*16 contiguous bytes.
+ * its row, so the P tokens of one chunk column sit in P*16 (FP8: P*8)
+ * contiguous bytes.
  * Logical page j of sequence b (tokens j*P .. j*P+P-1) lives in physical page
  * page_table[b * max_pages_per_seq + j].
  *
@@ -81,6 +92,7 @@ typedef int32_t kvlr_status;
 
 #define KVLR_DTYPE_BF16 0
 #define KVLR_DTYPE_F32 1
+#define KVLR_DTYPE_BF16_FP8 2  /* bf16, except the latents: OCP FP8 E4M3 */
 
 #define KVLR_KEYS_LATENT 0
 #define KVLR_KEYS_EXACT 1

@@ -9,6 +9,7 @@ binding never import or call it, and it imports nothing from them.
 from .kvlr_oracle import (  # noqa: F401
     STORAGE_TYPES,
     round_bf16,
+    round_fp8_e4m3,
     round_to_storage,
     encode_tokens,
     append_tokens,

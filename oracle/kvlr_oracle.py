@@ -46,9 +46,10 @@ design notes):
       k . B_k and every page is attended;
   R13 an empty context (L_b = 0) gives z = 0, o = 0 and lse = -inf.
 
-Storage: latents are rounded to the storage type ("bf16", "f32", or "f64" for
-no rounding) with round-to-nearest-even; every input value (keys, values,
-factors, queries) is taken exactly as given.
+Storage: latents are rounded to the storage type ("bf16", "f32", "fp8" for
+OCP E4M3 saturating at +-448, or "f64" for no rounding) with
+round-to-nearest-even; every input value (keys, values, factors, queries) is
+taken exactly as given.
 """
 
 from __future__ import annotations
@@ -57,7 +58,7 @@ import math
 
 import numpy as np
 
-STORAGE_TYPES = ("bf16", "f32", "f64")
+STORAGE_TYPES = ("bf16", "f32", "fp8", "f64")
 
 # Largest finite bfloat16: significand 1.1111111b, exponent 127.
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -87,6 +88,36 @@ def round_bf16(x) -> np.ndarray:
     return np.where(np.isfinite(x), out, x)
 
 
+# Largest finite OCP 8-bit E4M3 value: significand 1.110b, exponent 8 (the
+# all-ones pattern is NaN; the format has no infinities).
+_FP8_E4M3_MAX = 448.0
+
+
+def round_fp8_e4m3(x) -> np.ndarray:
+    """Round to the nearest OCP 8-bit floating point E4M3 value, ties to even,
+    saturating at +-448; NaN stays NaN (infinities saturate). Result as
+    float64.
+
+    E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 stored significand bits.
+    For |x| in [2**(e-1), 2**e) the spacing is 2**(e-4); normal values start
+    at 2**-6 and below that the spacing stays 2**-9 (subnormals). The latent
+    codec of the FP8 variant (a lossy latent store in the spirit of the page
+    "PackKV: Reducing KV Cache Memory Footprint through LLM-Aware Lossy
+    Compression", abstract) rounds each latent once with this function.
+    Pinned against torch's float32 -> float8_e4m3fn conversion inside the
+    range, the format's printed extreme values, and tie cases.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    spacing = np.ldexp(1.0, np.maximum(e - 4, -9))
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = np.minimum(np.rint(ax / spacing) * spacing, _FP8_E4M3_MAX)
+        r = np.where(np.isinf(ax), _FP8_E4M3_MAX, r)
+        out = np.copysign(r, x)
+    return np.where(np.isnan(x), x, out)
+
+
 def round_to_storage(x, storage: str) -> np.ndarray:
     """Value that the cache holds after storing x in the given type."""
     x = np.asarray(x, dtype=np.float64)
@@ -96,6 +127,8 @@ def round_to_storage(x, storage: str) -> np.ndarray:
         return x.astype(np.float32).astype(np.float64)
     if storage == "bf16":
         return round_bf16(x)
+    if storage == "fp8":
+        return round_fp8_e4m3(x)
     raise ValueError(f"unknown storage type {storage!r}")
 
 

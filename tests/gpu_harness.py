@@ -46,7 +46,7 @@ def oracle_state(sess, b: int, g: int) -> dict:
         Vn = f64(sess.v_new[off:off + n, g])
         f = factors_np(sess, g)
         st = O.append_tokens(st, L0, Kn, Vn, f["A_v"], f["A_k"], f["W_pred"],
-                             key_mode=wl.key_mode, storage=wl.storage)
+                             key_mode=wl.key_mode, storage=wl.lat_storage)
     return st
 
 
@@ -93,19 +93,22 @@ def stage_oracle_sequence(sess, b: int) -> list:
 
 
 def new_token_slack(sess, b: int, g: int, st: dict) -> float:
-    """Bound on how far a routing score can move when the new tokens' latents
-    differ from the oracle's by at most one bf16 unit in the last place:
-    sum_i |q_hat_i| ulp(v_i) + sum_i |q_tilde_i| ulp(c_i), worst token and head."""
+    """How far a routing score can move because the GPU's stored latents of
+    the new tokens differ from the oracle's (check_encode bounds each
+    difference by one unit in the last place of the stored type plus the
+    float32 accumulation error): with the actual differences dv, dc,
+    sum_i |q_hat_i| |dv_i| + sum_i |q_tilde_i| |dc_i|, worst token and head."""
     wl = sess.wl
     n = sess.n_new[b]
-    if not wl.routed or n == 0 or wl.storage != "bf16":
+    if not wl.routed or n == 0:
         return 0.0
     f = factors_np(sess, g)
     qh, qt = O.project_queries(q_group(sess, b, g), f["W_pred"], f["B_k"])
     L0 = sess.lens_before[b]
-    v = st["v"][L0:L0 + n]
-    c = st["k_lat"][L0:L0 + n]
-    bound = np.abs(qh) @ bf16_ulp(v).T + np.abs(qt) @ bf16_ulp(c).T   # [G, n]
+    got = {k: f64(v[g]) for k, v in sess.read_rows(b, L0 + n, L0).items()}
+    dv = np.abs(got["v"] - st["v"][L0:L0 + n])
+    dc = np.abs(got["k_lat"] - st["k_lat"][L0:L0 + n])
+    bound = np.abs(qh) @ dv.T + np.abs(qt) @ dc.T   # [G, n]
     return float(bound.max()) * 1.01 + 1e-6
 
 
@@ -158,6 +161,12 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 8)
 
 
+def fp8_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of OCP E4M3 values at |x| (2**-9 in the subnormal range)."""
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(e - 4, -9))
+
+
 def check_encode(sess, b: int, g: int) -> dict:
     """GPU-written latents of (b, g)'s new tokens against the oracle's encode.
 
@@ -177,11 +186,14 @@ def check_encode(sess, b: int, g: int) -> dict:
     Kn = f64(sess.k_new[off:off + n, g])
     Vn = f64(sess.v_new[off:off + n, g])
     enc = O.encode_tokens(Kn, Vn, f["A_v"], f["A_k"], f["W_pred"], key_mode=wl.key_mode,
-                          storage=wl.storage)
+                          storage=wl.lat_storage)
     got = {k: f64(v[g]) for k, v in sess.read_rows(b, L0 + n, L0).items()}
     d, rv = wl.head_dim, wl.rank_v
     u = 2.0 ** -24
-    if wl.storage == "bf16":
+    if wl.lat_storage == "fp8":
+        def unit(x, y):
+            return fp8_ulp(np.maximum(np.abs(x), np.abs(y)))
+    elif wl.lat_storage == "bf16":
         def unit(x, y):
             return bf16_ulp(np.maximum(np.abs(x), np.abs(y)))
     else:

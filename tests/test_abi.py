@@ -216,3 +216,16 @@ def test_fit_arguments(lib):
     with pytest.raises(TypeError):
         K.kvlr_fit_solve(s, np.zeros((8, 3, 128, 128), np.float32), np.zeros((8, 128, 64)),
                          np.zeros((8, 128, 32)), np.zeros((8, 64, 128)))
+
+
+def test_fp8_latent_shapes(lib):
+    s = _shape(dtype=K.KVLR_DTYPE_BF16_FP8)
+    assert K.kvlr_qproj_width(s) == 96
+    assert K.kvlr_workspace_bytes(s, 16, 512) > 0
+    U = K.KVLR_ERR_UNSUPPORTED
+    f = K.make_factors()
+    for bad in (_shape(dtype=K.KVLR_DTYPE_BF16_FP8, page_size=16),
+                _shape(dtype=K.KVLR_DTYPE_BF16_FP8, rank_v=128)):
+        assert lib.kvlr_upproject(ctypes.byref(bad), ctypes.byref(f), None, None, 1, None) == U
+    assert lib.kvlr_upproject(ctypes.byref(_shape(dtype=3)), ctypes.byref(f), None, None, 1,
+                              None) == K.KVLR_ERR_INVALID_ARGUMENT

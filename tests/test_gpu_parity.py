@@ -28,18 +28,18 @@ def _say(*a):
 
 
 def make_wl(*, G, d, rv, rk, P, storage, routed, B=4, Hkv=2, topk=(1, 8), seed=11, planted=0.0,
-            exact=None, value_basis="random"):
+            exact=None, value_basis="random", latent=""):
     exact = routed if exact is None else exact
     rs = min(48, d // 2)
     ns = min(rv, rs // 2, d - rk) if exact else 0
     mode = ("routed" if routed else "exact-all") if exact else "latent"
     return Workload(
-        name=f"t-G{G}-d{d}-rv{rv}-rk{rk}-P{P}-{storage}-{mode}",
+        name=f"t-G{G}-d{d}-rv{rv}-rk{rk}-P{P}-{storage}{'-' + latent if latent else ''}-{mode}",
         batch=B, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, page_size=P, rank_v=rv,
         rank_k=rk, storage=storage, key_mode="exact" if exact else "latent", context=0,
         topk_num=topk[0], topk_den=topk[1], signal_rank=rs, shared_rank=ns, noise_std=0.05,
         planted_frac=planted, planted_boost=4.0 if planted else 0.0, seed=seed,
-        route=routed, value_basis=value_basis)
+        route=routed, value_basis=value_basis, latent_storage=latent)
 
 
 def run_and_check(sess, pairs=None, stage=True):
@@ -79,6 +79,18 @@ DENSE = [
 
 LENS = [1, 777, 640, 2049]
 
+# FP8 E4M3 latents (bf16 keys and factors): 64-token pages
+FP8_ROUTED = [
+    dict(G=4, d=128, rv=64, rk=32),
+    dict(G=8, d=128, rv=32, rk=32),
+    dict(G=1, d=64, rv=16, rk=16),
+    dict(G=2, d=64, rv=64, rk=64),
+]
+FP8_DENSE = [
+    dict(G=4, d=128, rv=64, rk=64),
+    dict(G=8, d=64, rv=32, rk=16),
+]
+
 
 @pytest.mark.parametrize("cfg", ROUTED, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_routed_small(cfg):
@@ -94,6 +106,32 @@ def test_dense_small(cfg):
     _say("case", wl.name)
     sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
     run_and_check(sess)
+
+
+@pytest.mark.parametrize("cfg", FP8_ROUTED, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_fp8_latents_routed(cfg):
+    wl = make_wl(routed=True, P=64, storage="bf16", latent="fp8", **cfg)
+    _say("case", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    assert sess.v_lat.dtype == torch.float8_e4m3fn
+    run_and_check(sess)
+
+
+@pytest.mark.parametrize("cfg", FP8_DENSE, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_fp8_latents_dense(cfg):
+    wl = make_wl(routed=False, P=64, storage="bf16", latent="fp8", **cfg)
+    _say("case", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    run_and_check(sess)
+
+
+def test_fp8_latents_nan_tails_and_permuted_pages():
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True, latent="fp8")
+    _say("case fp8 NaN tails")
+    sess = DecodeSession(wl, "cuda", seq_lens=[65, 777, 130, 1000], append_per_seq=9,
+                         spare_pages=7, tail_fill=float("nan"))
+    run_and_check(sess)
+    assert torch.isfinite(sess.o).all() and torch.isfinite(sess.z).all()
 
 
 def test_tiny_workload_all_pairs():

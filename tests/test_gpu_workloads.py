@@ -18,7 +18,8 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 FULL = ["llama3-8b-dense-32k", "llama3-8b-routed-32k", "llama3-70b-share-routed-128k",
-        "mixed-append-routed-ragged", "llama3-8b-uncompressed-32k"]
+        "mixed-append-routed-ragged", "llama3-8b-uncompressed-32k", "llama3-8b-routed-fp8-32k",
+        "llama3-70b-share-routed-fp8-128k"]
 
 
 def _sample(sess):

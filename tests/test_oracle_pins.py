@@ -56,6 +56,52 @@ def test_round_bf16_matches_torch_rne():
     np.testing.assert_array_equal(got, want)
 
 
+def test_round_fp8_e4m3_known_values():
+    # OCP 8-bit floating point, E4M3: largest normal S.1111.110 = 448, smallest
+    # normal S.0001.000 = 2**-6, largest subnormal S.0000.111 = 0.875 * 2**-6,
+    # smallest subnormal S.0000.001 = 2**-9; spacing on [1, 2) is 2**-3.
+    R = O.round_fp8_e4m3
+    assert R(448.0) == 448.0
+    assert R(2.0 ** -6) == 2.0 ** -6
+    assert R(0.875 * 2.0 ** -6) == 0.875 * 2.0 ** -6
+    assert R(2.0 ** -9) == 2.0 ** -9
+    assert R(1 + 2 ** -4) == 1.0                  # tie -> even (1.0)
+    assert R(1 + 3 * 2 ** -4) == 1.25             # tie -> even (k = 2)
+    assert R(1 + 2 ** -4 + 2 ** -10) == 1.125
+    assert R(-(1 + 3 * 2 ** -4)) == -1.25
+    assert R(2.0 ** -10) == 0.0                   # half the smallest subnormal -> 0
+    assert R(3 * 2.0 ** -10) == 2.0 ** -8         # tie between 1 and 2 subnormal units -> 2
+    assert R(464.0) == 448.0                      # tie with 480 (not a finite value) -> 448
+    assert R(465.0) == 448.0 and R(1e6) == 448.0 and R(-1e6) == -448.0   # saturation
+    assert R(np.inf) == 448.0 and R(-np.inf) == -448.0
+    assert np.isnan(R(np.nan))
+
+
+def test_round_fp8_e4m3_matches_torch_inside_the_range():
+    """torch's float32 -> float8_e4m3fn conversion rounds to nearest even and
+    maps magnitudes from 464 up to NaN; inside (-464, 464) the two agree."""
+    rng = np.random.default_rng(5)
+    parts = [rng.standard_normal(20000) * sc for sc in (1e-3, 0.1, 1.0, 30.0)]
+    parts.append(rng.uniform(-463.0, 463.0, 5000))
+    x = np.concatenate(parts).astype(np.float32)
+    vals = torch.arange(127, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    vals = vals.to(torch.float64).numpy()       # codes 0..126: every finite value >= 0
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)  # exact ties
+    x = np.concatenate([x, mids, -mids])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.round_fp8_e4m3(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_round_fp8_e4m3_fixes_every_code():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    codes = codes.to(torch.float64).numpy()
+    assert np.isnan(codes).sum() == 2          # S.1111.111 only
+    fin = codes[~np.isnan(codes)]
+    np.testing.assert_array_equal(O.round_fp8_e4m3(fin), fin)
+    assert fin.max() == 448.0 and np.abs(fin[fin != 0]).min() == 2.0 ** -9
+
+
 def test_round_to_storage_f32_is_ieee_single():
     rng = np.random.default_rng(1)
     x = rng.standard_normal(1000)
