@@ -516,15 +516,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const float* allp = partials + static_cast<size_t>(pair) * max_splits * G * PW;
       for (int i = threadIdx.x; i < G * RV; i += kThreads) {
         const int h = i / RV, e = i - h * RV;
+        // the splits' records are read eight at a time, every load in flight
+        // before the first is used (one at a time, each coherent load would
+        // wait out a full memory latency); indices past the last split
+        // re-read it: no effect on the max, skipped in the sums
         float M = kNegInf;
-        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, load_shared_f32(&allp[(sp * G + h) * PW]));
+        for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+          float mm[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            mm[u] = load_shared_f32(&allp[(min(sp0 + u, nsplit - 1) * G + h) * PW]);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) M = fmaxf(M, mm[u]);
+        }
         float Z = 0.f, Ls = 0.f;
         if (M != kNegInf) {
-          for (int sp = 0; sp < nsplit; ++sp) {
-            const float* r = allp + (sp * G + h) * PW;
-            const float f = fast_exp2(load_shared_f32(&r[0]) - M);
-            Z += f * load_shared_f32(&r[2 + e]);
-            Ls += f * load_shared_f32(&r[1]);
+          for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+            float mm[8], ll[8], zz[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const float* r = allp + (min(sp0 + u, nsplit - 1) * G + h) * PW;
+              mm[u] = load_shared_f32(&r[0]);
+              ll[u] = load_shared_f32(&r[1]);
+              zz[u] = load_shared_f32(&r[2 + e]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              if (sp0 + u < nsplit) {
+                const float f = fast_exp2(mm[u] - M);
+                Z += f * zz[u];
+                Ls += f * ll[u];
+              }
+            }
           }
         }
         const int qh = g * G + h;

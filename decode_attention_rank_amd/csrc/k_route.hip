@@ -171,8 +171,24 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
   __shared__ int lds4[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-#pragma unroll 8
-  for (int j = tid; j < N; j += kThreads) s_keys[j] = order_key(load_shared_f32(&scores[j]));
+  // The scores are read with coherent device-scope loads through a global
+  // (not generic) pointer, eight per thread at a time, all issued before the
+  // first is used: one at a time, each would wait out a full memory latency.
+  // Indices past N re-read score N-1 and are not kept.
+  typedef __attribute__((address_space(1))) float gfloat;
+  gfloat* gs = (gfloat*)scores;
+  for (int j0 = 0; j0 < N; j0 += 8 * kThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __hip_atomic_load(gs + min(j0 + u * kThreads + tid, N - 1), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * kThreads + tid;
+      if (j < N) s_keys[j] = order_key(v[u]);
+    }
+  }
   __syncthreads();
 
   const bool take_all = (k >= N);
