@@ -35,7 +35,7 @@ EXPORTED = (
     "kvlr_decode_attn", "kvlr_decode_attn_upproject", "kvlr_upproject", "kvlr_workspace_bytes",
     "kvlr_workspace_init", "kvlr_fold_output_weights", "kvlr_output_projection",
     "kvlr_status_string", "kvlr_version", "kvlr_fit_workspace_bytes", "kvlr_fit_moments",
-    "kvlr_fit_solve", "kvlr_fit_factors",
+    "kvlr_fit_solve", "kvlr_fit_factors", "kvlr_choose_residual_ranks",
 )
 
 
@@ -52,7 +52,8 @@ class kvlr_shape(ctypes.Structure):
 
 
 class kvlr_cache(ctypes.Structure):
-    _fields_ = [("v_lat", ctypes.c_void_p), ("k_lat", ctypes.c_void_p), ("k_exact", ctypes.c_void_p)]
+    _fields_ = [("v_lat", ctypes.c_void_p), ("k_lat", ctypes.c_void_p), ("k_exact", ctypes.c_void_p),
+                ("k_lat_ranks", ctypes.POINTER(ctypes.c_int32))]
 
 
 class kvlr_factors(ctypes.Structure):
@@ -92,6 +93,7 @@ _SIG = {
     "kvlr_fit_solve": ([ctypes.POINTER(kvlr_shape), _P, _P, _P, _P, _P, _P], _I),
     "kvlr_fit_factors": ([ctypes.POINTER(kvlr_shape), _P, _P, _I, ctypes.POINTER(kvlr_factor_buffers),
                           _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "kvlr_choose_residual_ranks": ([ctypes.POINTER(kvlr_shape), _P, ctypes.c_double, _P], _I),
 }
 
 
@@ -152,8 +154,15 @@ def make_shape(*, num_q_heads, num_kv_heads, head_dim, page_size, rank_v, rank_k
                       key_mode, num_phys_pages)
 
 
-def make_cache(v_lat=None, k_lat=None, k_exact=None) -> kvlr_cache:
-    return kvlr_cache(_ptr(v_lat), _ptr(k_lat), _ptr(k_exact))
+def make_cache(v_lat=None, k_lat=None, k_exact=None, k_lat_ranks=None) -> kvlr_cache:
+    """k_lat_ranks: per-KV-head residual ranks (a sequence of ints) or None."""
+    ranks = None
+    if k_lat_ranks is not None:
+        ranks = (ctypes.c_int32 * len(k_lat_ranks))(*[int(r) for r in k_lat_ranks])
+    c = kvlr_cache(_ptr(v_lat), _ptr(k_lat), _ptr(k_exact),
+                   ctypes.cast(ranks, ctypes.POINTER(ctypes.c_int32)) if ranks is not None else None)
+    c._ranks = ranks  # keep the host array alive as long as the struct
+    return c
 
 
 def make_factors(A_v=None, B_v=None, A_k=None, B_k=None, W_pred=None) -> kvlr_factors:
@@ -264,3 +273,13 @@ def kvlr_fit_factors(shape, k, v, n, out, lam_v, lam_k, workspace, ws_bytes, str
     _check("kvlr_fit_factors", lib().kvlr_fit_factors(
         ctypes.byref(shape), _ptr(k), _ptr(v), n, ctypes.byref(out), _ptr(lam_v), _ptr(lam_k),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvlr_choose_residual_ranks(shape, lam_k, energy_frac) -> list:
+    """Host call: per-head residual ranks from the fit's residual eigenvalues
+    (lam_k host float64 [H_kv][rank_k])."""
+    lam_k = _host_f64(lam_k, "lam_k")
+    out = (ctypes.c_int32 * shape.num_kv_heads)()
+    _check("kvlr_choose_residual_ranks", lib().kvlr_choose_residual_ranks(
+        ctypes.byref(shape), _ptr(lam_k), float(energy_frac), ctypes.cast(out, ctypes.c_void_p)))
+    return list(out)

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     const uint8_t* __restrict__ v_new, const int32_t* __restrict__ cu_new,
     const int32_t* __restrict__ lens_before, const int32_t* __restrict__ page_table,
     uint8_t* __restrict__ v_lat, uint8_t* __restrict__ k_lat, uint8_t* __restrict__ k_exact,
-    int Hkv, int P, int log2P, int max_pages, int batch, int total_new) {
+    int Hkv, int P, int log2P, int max_pages, int batch, int total_new, KLayout kl) {
   using MM = Mma<S>;
   using SM = EncSmem<S, LS, D, RV, RK, ROUTED>;
   using LT = Lat<S, LS>;
@@ -346,11 +346,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       for (int j = 0; j < 4; ++j) sm.u.t.ct[wave][4 * kq + j][nt * 16 + r] = LT::round(cacc[nt][j]);
     wave_lds_sync();
     if (valid) {
-      uint8_t* dst = k_lat + (phys * Hkv + g) * CK * P * LT::CB + slot_off * LT::CB;
+      // per-head residual ranks: this head keeps its first ckg chunks, at its
+      // own offset in the page
+      const int ckg = kl.adaptive ? kl.ck[g] : CK;
+      const size_t page_chunks = kl.adaptive ? static_cast<size_t>(kl.page_chunks) : static_cast<size_t>(Hkv) * CK;
+      const size_t koff = kl.adaptive ? static_cast<size_t>(kl.off[g]) : static_cast<size_t>(g) * CK;
+      uint8_t* dst = k_lat + (phys * page_chunks + koff) * P * LT::CB + slot_off * LT::CB;
 #pragma unroll
       for (int c0 = 0; c0 < CK; c0 += 4) {
         const int c = c0 + kq;
-        if (c < CK) LT::store_chunk(dst + static_cast<size_t>(c) * P * LT::CB, &sm.u.t.ct[wave][r][c * CH]);
+        if (c < ckg) LT::store_chunk(dst + static_cast<size_t>(c) * P * LT::CB, &sm.u.t.ct[wave][r][c * CH]);
       }
     }
     wave_lds_sync();
@@ -381,7 +386,7 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
                      static_cast<const uint8_t*>(a.v_new), a.cu_new, a.lens_before, a.page_table,
                      static_cast<uint8_t*>(a.v_lat), static_cast<uint8_t*>(a.k_lat),
                      static_cast<uint8_t*>(a.k_exact), a.dm.Hkv, a.dm.P, log2P, a.max_pages,
-                     a.batch, a.total_new);
+                     a.batch, a.total_new, a.kl);
   return hipGetLastError();
 }
 

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int32_t* __restrict__ sel_counts,
     int Hq, int Hkv, int P,
     int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_chunk,
-    int batch) {
+    int batch, KLayout kl) {
   constexpr int CH = S::CH;
   constexpr int CV = RV / CH;
   constexpr int CK = RK / CH;
@@ -323,9 +323,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const size_t slab_v = static_cast<size_t>(CV) * P * S::CB;  // bytes of one head's page
   const size_t slab_k = static_cast<size_t>(CK) * P * S::CB;
 
+  // work chunks of head g span rpc(g) rows: rows_per_chunk, or with per-head
+  // residual ranks a count that gives every chunk about the same bytes
+  auto rpc_of = [&](int g) { return kl.adaptive ? kl.rpc[g] : rows_per_chunk; };
+  auto splits_of = [&](int rows, int g) { return max(1, (rows + rpc_of(g) - 1) / rpc_of(g)); };
   build_chunk_prefix(batch, s_base, [&](int b) {
     const int rows = (seq_lens[b] + kWave - 1) / kWave;
-    return Hkv * max(1, (rows + rows_per_chunk - 1) / rows_per_chunk);
+    if (!kl.adaptive) return Hkv * splits_of(rows, 0);
+    int n = 0;
+    for (int g = 0; g < Hkv; ++g) n += splits_of(rows, g);
+    return n;
   });
   const int total = s_base[batch];
 
@@ -333,10 +340,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const int b = find_sequence(s_base, batch, w);
     const int L = seq_lens[b];
     const int nrows = (L + kWave - 1) / kWave;
-    const int nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
-    const int local = w - s_base[b];
-    const int g = local / nsplit;
-    const int split = local - g * nsplit;
+    int local = w - s_base[b];
+    int g, nsplit;
+    if (!kl.adaptive) {
+      nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
+      g = local / nsplit;
+      local -= g * nsplit;
+    } else {
+      g = 0;
+      nsplit = splits_of(nrows, 0);
+      while (local >= nsplit) {
+        local -= nsplit;
+        nsplit = splits_of(nrows, ++g);
+      }
+    }
+    const int split = local;
+    const int rpc = rpc_of(g);
     const int pair = b * Hkv + g;
     const float* __restrict__ qp = q_proj + static_cast<size_t>(b * Hq + g * G) * W;
     const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
@@ -346,8 +365,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     constexpr bool kMfma = ROWPAGE && S::CH == 8 && (KVLR_ROUTE_MFMA || S::CB == 8);
     float qv[kMfma ? 1 : NQ];
     if constexpr (!kMfma) load_q_rows(qp, qv);
-    const int row0 = split * rows_per_chunk;
-    const int row1 = min(row0 + rows_per_chunk, nrows);
+    const int row0 = split * rpc;
+    const int row1 = min(row0 + rpc, nrows);
 
     if constexpr (kMfma) {
       // Matrix-core scoring (bf16 or FP8 latents, one page per row). A 64-token
@@ -360,15 +379,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       // two products per step). Heads past the group and tokens past the
       // sequence end are masked before the page max.
       // k-steps: ceil(CV/4) over the value latent, then ceil(CK/4) over the
-      // residual, so each step reads one slab (a uniform base address)
+      // residual, so each step reads one slab (a uniform base address). With
+      // per-head residual ranks this head's slab has ckg <= CK chunks at its
+      // own offset; chunks past ckg are not read (their query half is zero).
       constexpr int KSV = (CV + 3) / 4, KSK = (CK + 3) / 4, KS = KSV + KSK;
       const int kq = lane >> 4, col = lane & 15;
+      const int ckg = kl.adaptive ? kl.ck[g] : CK;
+      const size_t kpage = kl.adaptive ? static_cast<size_t>(kl.page_chunks) * P * S::CB : Hkv * slab_k;
+      const size_t koff = kl.adaptive ? static_cast<size_t>(kl.off[g]) * P * S::CB : g * slab_k;
       bf16x8 qhi[KS], qlo[KS];
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
         const bool on_v = st < KSV;
         const int ci = 4 * (on_v ? st : st - KSV) + kq;  // chunk within the slab
-        const bool have = col < G && ci < (on_v ? CV : CK);
+        const bool have = col < G && ci < (on_v ? CV : ckg);
         const float* src = qp + col * W + (on_v ? 0 : RV) + ci * 8;
         float x[8];
         if (have) {
@@ -392,23 +416,28 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       auto row_ref = [&](int row) -> RowRef {
         if (row >= row1) return RowRef{v_lat, k_lat, 0};
         const size_t phys = static_cast<size_t>(pt[row]);
-        return RowRef{v_lat + (phys * Hkv + g) * slab_v, k_lat + (phys * Hkv + g) * slab_k, 1};
+        return RowRef{v_lat + (phys * Hkv + g) * slab_v, k_lat + phys * kpage + koff, 1};
       };
       auto a_addr = [&](const RowRef& rr, int j, int st) -> const uint8_t* {
         const bool on_v = st < KSV;
         int ci = 4 * (on_v ? st : st - KSV) + kq;
-        if (ci >= (on_v ? CV : CK)) ci = 0;
+        if (ci >= (on_v ? CV : ckg)) ci = 0;
         const uint32_t off = static_cast<uint32_t>(rr.on) *
                              static_cast<uint32_t>((j * 16 + col) * S::CB + ci * (kWave * S::CB));
         return (on_v ? rr.vb : rr.kb) + off;
       };
       int r = row0 + wave;
       typename S::Raw A[4][KS];
+      // residual k-steps past this head's rank (per-head ranks) are skipped:
+      // a wave-uniform test, compiled only where the residual spans 2+ steps
+      const int ks_used = KSV + (ckg + 3) / 4;
+      auto step_on = [&](int st) { return st <= KSV || st < ks_used; };
       RowRef cur = row_ref(r);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int st = 0; st < KS; ++st) A[j][st] = S::load_stream(a_addr(cur, j, st));
+        for (int st = 0; st < KS; ++st)
+          if (step_on(st)) A[j][st] = S::load_stream(a_addr(cur, j, st));
       RowRef nxt = row_ref(r + kWaves);
       for (; r < row1; r += kWaves) {
         const RowRef nn = row_ref(r + 2 * kWaves);  // page-table entry two rows ahead
@@ -418,6 +447,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
           acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int st = 0; st < KS; ++st) {
+            if (!step_on(st)) continue;
             const bf16x8 a = S::to_bf16x8(A[j][st]);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[st], acc[j], 0, 0, 0);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[st], acc[j], 0, 0, 0);
@@ -583,7 +613,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                        static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                        a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts, a.dm.Hq,
                        a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
-                       a.rows_per_chunk, a.batch);
+                       a.rows_per_chunk, a.batch, a.kl);
   } else {
     if constexpr (S::CB == 8) return hipErrorInvalidValue;  // FP8 latents: 64-token pages only
     else
@@ -591,7 +621,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
                          a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
-                         a.k_max, a.rows_per_chunk, a.batch);
+                         a.k_max, a.rows_per_chunk, a.batch, a.kl);
   }
   return hipGetLastError();
 }

@@ -106,6 +106,36 @@ Plan plan_for(const Dims& dm, int batch, int max_pages) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Residual-latent layout from the cache's per-head rank table (NULL:
+// uniform). Per-head ranks need routed keys, 64-token pages, bf16 keys and
+// bf16 or FP8 latents, at most kMaxAdaptiveHeads KV heads, and each rank in
+// {16, 32, 64} and at most rank_k.
+kvlr_status residual_layout(const Dims& dm, const kvlr_cache* cache, kvlr::KLayout* kl) {
+  *kl = kvlr::KLayout{};
+  if (!cache->k_lat_ranks) return KVLR_OK;
+  if (!dm.exact || dm.P != 64 || dm.dtype != 0 || dm.Hkv > kvlr::kMaxAdaptiveHeads)
+    return KVLR_ERR_UNSUPPORTED;
+  kl->adaptive = 1;
+  int off = 0;
+  for (int g = 0; g < dm.Hkv; ++g) {
+    const int r = cache->k_lat_ranks[g];
+    if (!one_of(r, 16, 32, 64) || r > dm.RK) return KVLR_ERR_INVALID_ARGUMENT;
+    kl->ck[g] = r / 8;  // 8 elements per chunk for bf16 and FP8 latents
+    kl->off[g] = off;
+    off += kl->ck[g];
+  }
+  kl->page_chunks = off;
+  // routing work chunks of equal bytes: rows per chunk scaled by the
+  // smallest head's (rank_v + r) over this head's
+  int rmin = 64;
+  for (int g = 0; g < dm.Hkv; ++g) rmin = cache->k_lat_ranks[g] < rmin ? cache->k_lat_ranks[g] : rmin;
+  for (int g = 0; g < dm.Hkv; ++g) {
+    const int rpc = kvlr::route_rows_per_chunk() * (dm.RV + rmin) / (dm.RV + cache->k_lat_ranks[g]);
+    kl->rpc[g] = rpc > 1 ? rpc : 1;
+  }
+  return KVLR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +192,8 @@ kvlr_status kvlr_append_encode(const kvlr_shape* shape, const kvlr_factors* fact
     return KVLR_ERR_INVALID_ARGUMENT;
   if (dm.exact && (!ok_ptr(factors->W_pred) || !ok_ptr(cache->k_exact))) return KVLR_ERR_INVALID_ARGUMENT;
   kvlr::EncodeArgs a{};
+  st = residual_layout(dm, cache, &a.kl);
+  if (st != KVLR_OK) return st;
   a.dm = dm;
   a.A_v = factors->A_v;
   a.A_k = factors->A_k;
@@ -227,6 +259,8 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   kvlr::RouteArgs a{};
+  st = residual_layout(dm, cache, &a.kl);
+  if (st != KVLR_OK) return st;
   a.dm = dm;
   a.v_lat = cache->v_lat;
   a.k_lat = cache->k_lat;
@@ -244,8 +278,11 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.batch = batch;
   const int max_rows = ceil_div(static_cast<long long>(max_pages_per_seq) * dm.P, 64);
   a.rows_per_chunk = kvlr::route_rows_per_chunk();
-  const long long chunks = static_cast<long long>(batch) * dm.Hkv *
-                           (max_rows > 0 ? ceil_div(max_rows, a.rows_per_chunk) : 1);
+  long long chunks = 0;
+  for (int g = 0; g < dm.Hkv; ++g) {
+    const int rpc = a.kl.adaptive ? a.kl.rpc[g] : a.rows_per_chunk;
+    chunks += static_cast<long long>(batch) * (max_rows > 0 ? ceil_div(max_rows, rpc) : 1);
+  }
   a.grid = static_cast<int>(chunks < kPersistentGrid ? chunks : kPersistentGrid);
   return hip_status(kvlr::launch_route(a, as_stream(stream)));
 }
@@ -414,6 +451,32 @@ kvlr_status kvlr_fit_moments(const kvlr_shape* shape, const void* k, const void*
   a.moments = moments;
   a.accumulate = accumulate;
   return hip_status(kvlr::launch_fit_moments(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_choose_residual_ranks(const kvlr_shape* shape, const double* lam_k,
+                                       double energy_frac, int32_t* ranks_out) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!dm.exact) return KVLR_ERR_UNSUPPORTED;
+  if (!lam_k || !ranks_out || !(energy_frac > 0.0) || energy_frac > 1.0) return KVLR_ERR_INVALID_ARGUMENT;
+  for (int g = 0; g < dm.Hkv; ++g) {
+    const double* lam = lam_k + static_cast<size_t>(g) * dm.RK;
+    double total = 0.0;
+    for (int i = 0; i < dm.RK; ++i) total += lam[i] > 0.0 ? lam[i] : 0.0;
+    int pick = dm.RK;
+    double run = 0.0;
+    int i = 0;
+    for (int r = 16; r <= dm.RK; r *= 2) {
+      for (; i < r; ++i) run += lam[i] > 0.0 ? lam[i] : 0.0;
+      if (run >= energy_frac * total) {
+        pick = r;
+        break;
+      }
+    }
+    ranks_out[g] = pick;
+  }
+  return KVLR_OK;
 }
 
 kvlr_status kvlr_fit_solve(const kvlr_shape* shape, const double* moments, double* A_v,

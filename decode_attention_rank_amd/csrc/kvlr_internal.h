@@ -15,6 +15,19 @@ struct Dims {
   int exact;      // 1 = routed (residual latent + original keys)
 };
 
+// Residual-latent (k_lat) layout of a routed cache. Uniform: every KV head
+// keeps rank_k / CH chunk columns, head g at chunk offset g * that. Adaptive
+// (per-head residual ranks): head g keeps ck[g] chunk columns at chunk offset
+// off[g] of its page, and a page holds page_chunks chunk columns in all.
+constexpr int kMaxAdaptiveHeads = 16;
+struct KLayout {
+  int adaptive;
+  int page_chunks;
+  int ck[kMaxAdaptiveHeads];
+  int off[kMaxAdaptiveHeads];
+  int rpc[kMaxAdaptiveHeads];  // routing rows per work chunk of head g (equal bytes per chunk)
+};
+
 struct QprojArgs {
   Dims dm;
   const void* W_pred;  // [Hkv][RV][D] (exact only)
@@ -38,6 +51,7 @@ struct RouteArgs {
   int32_t* sel_counts;  // optional [B][Hkv]
   float* scores;        // [B][Hkv][max_pages]
   uint32_t* counters;   // [B * Hkv], zero between calls
+  KLayout kl;
   int batch;
   int rows_per_chunk;   // 64-token rows per work chunk
   int grid;             // persistent workgroups
@@ -116,6 +130,7 @@ struct EncodeArgs {
   void* k_exact;
   int batch;
   int total_new;
+  KLayout kl;
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 

@@ -67,10 +67,19 @@ class DecodeSession:
 
         # paged cache
         self.v_lat = layout.alloc_pages(num_phys, H, wl.rank_v, P, lt, dev, tail_fill)
-        self.k_lat = layout.alloc_pages(num_phys, H, wl.rank_k, P, lt, dev, tail_fill)
+        if wl.residual_ranks:
+            # per-head residual ranks: one compact run of chunk columns per page,
+            # head g's r_g / CH columns after those of heads 0 .. g-1
+            ch = layout.chunk_elems(lt)
+            self.k_off = [sum(wl.residual_ranks[:g]) // ch for g in range(H)]
+            flat = layout.alloc_pages(num_phys, 1, sum(wl.residual_ranks), P, lt, dev, tail_fill)
+            self.k_lat = flat[:, 0]
+        else:
+            self.k_lat = layout.alloc_pages(num_phys, H, wl.rank_k, P, lt, dev, tail_fill)
         self.k_exact = (layout.alloc_pages(num_phys, H, wl.head_dim, P, dt, dev, tail_fill)
                         if wl.exact else None)
-        self.kcache = K.make_cache(self.v_lat, self.k_lat, self.k_exact)
+        self.kcache = K.make_cache(self.v_lat, self.k_lat, self.k_exact,
+                                   wl.residual_ranks if wl.residual_ranks else None)
 
         # lengths and page table on the device
         self.page_table = page_table.to(dev)
@@ -122,19 +131,40 @@ class DecodeSession:
             rows = self.prefix_rows(b)
             self.write_rows(b, rows)
 
+    def k_lat_head(self, g: int) -> torch.Tensor:
+        """Pages of KV head g's residual latents, [num_phys, 1, r_g / CH, P, CH]."""
+        if not self.wl.residual_ranks:
+            return self.k_lat[:, g:g + 1]
+        nch = self.wl.k_rank(g) // layout.chunk_elems(self.lat_dtype)
+        return self.k_lat[:, self.k_off[g]:self.k_off[g] + nch].unsqueeze(1)
+
     def write_rows(self, b: int, rows: dict, tail_fill: float | None = None):
         tail_fill = self.tail_fill if tail_fill is None else tail_fill
         pages = self.page_table_cpu[b]
         layout.pack_sequence(self.v_lat, pages, rows["v"], tail_fill)
-        layout.pack_sequence(self.k_lat, pages, rows["k_lat"], tail_fill)
+        if self.wl.residual_ranks:
+            for g in range(self.wl.num_kv_heads):
+                r = self.wl.k_rank(g)
+                layout.pack_sequence(self.k_lat_head(g), pages, rows["k_lat"][g:g + 1, :, :r], tail_fill)
+        else:
+            layout.pack_sequence(self.k_lat, pages, rows["k_lat"], tail_fill)
         if self.wl.exact:
             layout.pack_sequence(self.k_exact, pages, rows["k_exact"], tail_fill)
 
     def read_rows(self, b: int, L: int | None = None, start: int = 0) -> dict:
         L = self.seq_lens[b] if L is None else L
         pages = self.page_table_cpu[b]
-        out = {"v": layout.unpack_sequence(self.v_lat, pages, L, start),
-               "k_lat": layout.unpack_sequence(self.k_lat, pages, L, start)}
+        if self.wl.residual_ranks:
+            # each head's kept coordinates, zero-padded to rank_k
+            heads = []
+            for g in range(self.wl.num_kv_heads):
+                x = layout.unpack_sequence(self.k_lat_head(g), pages, L, start)
+                pad = x.new_zeros((1, x.shape[1], self.wl.rank_k - x.shape[2]))
+                heads.append(torch.cat([x, pad], dim=2))
+            k_lat = torch.cat(heads, dim=0)
+        else:
+            k_lat = layout.unpack_sequence(self.k_lat, pages, L, start)
+        out = {"v": layout.unpack_sequence(self.v_lat, pages, L, start), "k_lat": k_lat}
         if self.wl.exact:
             out["k_exact"] = layout.unpack_sequence(self.k_exact, pages, L, start)
         return out
@@ -239,7 +269,9 @@ class DecodeSession:
     def route_bytes(self) -> int:
         """Algorithmic bytes the routing kernel must read: both latents of every valid token."""
         lb = torch.empty(0, dtype=self.lat_dtype).element_size()
-        return sum(self.seq_lens) * self.wl.num_kv_heads * (self.wl.rank_v + self.wl.rank_k) * lb
+        wl = self.wl
+        per_token = sum(wl.rank_v + wl.k_rank(g) for g in range(wl.num_kv_heads))
+        return sum(self.seq_lens) * per_token * lb
 
     def attend_bytes(self) -> int:
         """Algorithmic bytes of attention: keys and value latents of the attended tokens."""
@@ -262,6 +294,6 @@ class DecodeSession:
         eb = torch.empty(0, dtype=self.dtype).element_size()
         lb = torch.empty(0, dtype=self.lat_dtype).element_size()
         read = self.total_new * wl.num_kv_heads * 2 * wl.head_dim * eb
-        write = self.total_new * wl.num_kv_heads * ((wl.rank_v + wl.rank_k) * lb
-                                                   + (wl.head_dim * eb if wl.exact else 0))
+        lat = sum(wl.rank_v + wl.k_rank(g) for g in range(wl.num_kv_heads)) * lb
+        write = self.total_new * (lat + wl.num_kv_heads * (wl.head_dim * eb if wl.exact else 0))
         return read + write

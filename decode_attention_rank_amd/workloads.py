@@ -36,6 +36,7 @@ class Workload:
     value_basis: str = "random"  # "identity": the value latent is the value itself
     hidden: int = 0             # output features of W_o (0: num_q_heads * head_dim)
     latent_storage: str = ""    # "fp8": latents as OCP FP8 E4M3 (else as `storage`)
+    residual_ranks: tuple = ()  # per-KV-head residual ranks (routed; () = rank_k for all)
     ctx_min: int = 0
     ctx_max: int = 0
     seed: int = 0
@@ -52,6 +53,10 @@ class Workload:
     @property
     def routed(self) -> bool:
         return self.exact and self.route
+
+    def k_rank(self, g: int) -> int:
+        """Residual (or key-latent) rank kept for KV head g."""
+        return self.residual_ranks[g] if self.residual_ranks else self.rank_k
 
     @property
     def lat_storage(self) -> str:
@@ -110,6 +115,13 @@ WORKLOADS = {
         head_dim=128, page_size=64, rank_v=64, rank_k=32, storage="bf16",
         latent_storage="fp8", key_mode="exact", context=32768, topk_num=1, topk_den=8,
         signal_rank=48, shared_rank=32, noise_std=0.05, seed=2),
+    # Per-head residual ranks (at most 64) on the 8B routed shapes: mean 28.
+    "llama3-8b-routed-adaptive-32k": Workload(
+        name="llama3-8b-routed-adaptive-32k", batch=16, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, page_size=64, rank_v=64, rank_k=64, storage="bf16",
+        key_mode="exact", context=32768, topk_num=1, topk_den=8,
+        signal_rank=48, shared_rank=32, noise_std=0.05,
+        residual_ranks=(16, 32, 16, 64, 16, 32, 16, 32), seed=2),
     "llama3-70b-share-routed-fp8-128k": Workload(
         name="llama3-70b-share-routed-fp8-128k", batch=64, num_q_heads=8, num_kv_heads=1,
         head_dim=128, page_size=64, rank_v=32, rank_k=32, storage="bf16",

@@ -64,6 +64,21 @@
  *   KVLR_KEYS_LATENT dense low-rank keys: k_lat holds k = K . A_k; no
  *                    routing, no original keys.
  *
+ * Per-head residual ranks (kvlr_cache.k_lat_ranks != NULL): an adaptive
+ * residual in the sense of BasisKV's method details (key design: a residual
+ * mechanism that adapts to what the value cannot recover), read as a rank
+ * chosen per KV head. KV head g keeps only the first r_g = k_lat_ranks[g]
+ * residual coordinates (r_g in {16, 32, 64}, r_g <= rank_k): k_lat becomes
+ *   k_lat [num_phys_pages][sum_g r_g / 8][page_size][8 elements]
+ * with head g's r_g / 8 chunk columns at chunk offset sum_{g' < g} r_g' / 8.
+ * The factors keep their rank_k-wide shapes; residual coordinates at or past
+ * r_g are neither stored nor read (their factor columns are ignored), so
+ * routing streams (rank_v + r_g) latent elements per token of head g. Needs
+ * KVLR_KEYS_EXACT, page_size 64, bf16 or FP8 latents with bf16 factors, and
+ * at most 16 KV heads; other shapes return KVLR_ERR_UNSUPPORTED. Only
+ * kvlr_append_encode and kvlr_route_pages read the table (attention of a
+ * routed cache reads original keys and value latents only).
+ *
  * Query-head h belongs to KV head h / G, G = num_q_heads / num_kv_heads.
  * Supported: head_dim in {64, 128}; rank_v, rank_k in {16, 32, 64} and
  * <= head_dim, and rank_v = 128 with bf16 storage (values kept at full
@@ -113,6 +128,7 @@ typedef struct kvlr_cache {
   void* v_lat;
   void* k_lat;
   void* k_exact;          /* KVLR_KEYS_EXACT only, else NULL */
+  const int32_t* k_lat_ranks;  /* host [H_kv] per-head residual ranks, or NULL */
 } kvlr_cache;
 
 typedef struct kvlr_factors {
@@ -367,6 +383,19 @@ kvlr_status kvlr_fit_moments(const kvlr_shape* shape, const void* k, const void*
  */
 kvlr_status kvlr_fit_solve(const kvlr_shape* shape, const double* moments, double* A_v,
                            double* A_k, double* W_pred, double* lam_v, double* lam_k);
+
+/*
+ * Host only: per-head residual ranks for an adaptive residual (see the
+ * kvlr_cache.k_lat_ranks comment) from the fit's residual spectrum. For each
+ * KV head g, ranks_out[g] is the smallest r in {16, 32, 64}, r <= rank_k,
+ * whose top-r residual eigenvalues carry at least energy_frac of the energy
+ * of the top rank_k (negative eigenvalues count as zero), else rank_k.
+ *   lam_k     host [H_kv][rank_k], largest first (kvlr_fit_solve's lam_k)
+ *   ranks_out host out [H_kv]
+ * KVLR_KEYS_EXACT only; energy_frac in (0, 1].
+ */
+kvlr_status kvlr_choose_residual_ranks(const kvlr_shape* shape, const double* lam_k,
+                                       double energy_frac, int32_t* ranks_out);
 
 /*
  * The whole fit in one synchronous call: kvlr_fit_moments into the

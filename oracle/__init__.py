@@ -28,4 +28,5 @@ from .kvlr_oracle import (  # noqa: F401
     fold_output_weights,
     latent_output_projection,
     fit_factors,
+    choose_residual_ranks,
 )

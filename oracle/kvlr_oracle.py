@@ -426,3 +426,24 @@ def fit_factors(K, V, r_v: int, r_k: int, *, key_mode: str):
         out["W_pred"] = None
     out.update(A_k=A_k, B_k=A_k.T.copy(), lam_k=lam_k)
     return out
+
+
+def choose_residual_ranks(lam_k, energy_frac: float, allowed=(16, 32, 64)):
+    """Per-head residual ranks for an adaptive residual (BasisKV method
+    details, key design: a residual mechanism that adapts to what the value
+    cannot recover; read here as a rank per KV head). lam_k: [H, r_max]
+    residual eigenvalues, largest first. Head g gets the smallest allowed
+    r <= r_max whose top-r eigenvalues hold at least energy_frac of the
+    energy of all r_max (negative eigenvalues count as zero), else r_max."""
+    lam = np.maximum(np.asarray(lam_k, np.float64), 0.0)
+    H, r_max = lam.shape
+    out = []
+    for g in range(H):
+        total = lam[g].sum()
+        pick = r_max
+        for r in allowed:
+            if r <= r_max and lam[g, :r].sum() >= energy_frac * total:
+                pick = r
+                break
+        out.append(pick)
+    return out

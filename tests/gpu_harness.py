@@ -31,7 +31,18 @@ def f64(t: torch.Tensor) -> np.ndarray:
 
 
 def factors_np(sess, g: int) -> dict:
-    return {k: (None if v is None else f64(v[g])) for k, v in sess.factors.items()}
+    """KV head g's factors; with per-head residual ranks only the kept
+    residual coordinates (the GPU ignores the rest of A_k and B_k)."""
+    f = {k: (None if v is None else f64(v[g])) for k, v in sess.factors.items()}
+    r = sess.wl.k_rank(g)
+    f["A_k"] = f["A_k"][:, :r]
+    f["B_k"] = f["B_k"][:r]
+    return f
+
+
+def k_cols(sess, g: int, x: np.ndarray) -> np.ndarray:
+    """The kept residual (or key-latent) coordinates of head g's rows."""
+    return x[..., :sess.wl.k_rank(g)]
 
 
 def oracle_state(sess, b: int, g: int) -> dict:
@@ -40,6 +51,7 @@ def oracle_state(sess, b: int, g: int) -> dict:
     L0, n = sess.lens_before[b], sess.n_new[b]
     rows = sess.prefix_rows(b)
     st = {k: f64(v[g]) for k, v in rows.items()}
+    st["k_lat"] = k_cols(sess, g, st["k_lat"])
     if n:
         off = sum(sess.n_new[:b])
         Kn = f64(sess.k_new[off:off + n, g])
@@ -86,8 +98,14 @@ def stage_oracle_sequence(sess, b: int) -> list:
     so a following GPU decode reads exactly the oracle's stored values.
     Returns the per-head oracle states."""
     states = [oracle_state(sess, b, g) for g in range(sess.wl.num_kv_heads)]
-    rows = {k: torch.from_numpy(np.stack([st[k][:sess.seq_lens[b]] for st in states]))
-            for k in states[0]}
+    L = sess.seq_lens[b]
+
+    def head_rows(st, k):
+        x = st[k][:L]
+        if k == "k_lat":  # per-head residual ranks: pad to the full width
+            x = np.pad(x, ((0, 0), (0, sess.wl.rank_k - x.shape[1])))
+        return x
+    rows = {k: torch.from_numpy(np.stack([head_rows(st, k) for st in states])) for k in states[0]}
     sess.write_rows(b, rows)
     return states
 
@@ -106,6 +124,7 @@ def new_token_slack(sess, b: int, g: int, st: dict) -> float:
     qh, qt = O.project_queries(q_group(sess, b, g), f["W_pred"], f["B_k"])
     L0 = sess.lens_before[b]
     got = {k: f64(v[g]) for k, v in sess.read_rows(b, L0 + n, L0).items()}
+    got["k_lat"] = k_cols(sess, g, got["k_lat"])
     dv = np.abs(got["v"] - st["v"][L0:L0 + n])
     dc = np.abs(got["k_lat"] - st["k_lat"][L0:L0 + n])
     bound = np.abs(qh) @ dv.T + np.abs(qt) @ dc.T   # [G, n]
@@ -188,6 +207,7 @@ def check_encode(sess, b: int, g: int) -> dict:
     enc = O.encode_tokens(Kn, Vn, f["A_v"], f["A_k"], f["W_pred"], key_mode=wl.key_mode,
                           storage=wl.lat_storage)
     got = {k: f64(v[g]) for k, v in sess.read_rows(b, L0 + n, L0).items()}
+    got["k_lat"] = k_cols(sess, g, got["k_lat"])
     d, rv = wl.head_dim, wl.rank_v
     u = 2.0 ** -24
     if wl.lat_storage == "fp8":

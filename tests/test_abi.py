@@ -229,3 +229,29 @@ def test_fp8_latent_shapes(lib):
         assert lib.kvlr_upproject(ctypes.byref(bad), ctypes.byref(f), None, None, 1, None) == U
     assert lib.kvlr_upproject(ctypes.byref(_shape(dtype=3)), ctypes.byref(f), None, None, 1,
                               None) == K.KVLR_ERR_INVALID_ARGUMENT
+
+
+def test_per_head_residual_rank_arguments(lib):
+    fake = 1 << 20
+    ws = 1 << 40  # size checks pass; nothing below reaches a launch
+    f = K.make_factors(fake, fake, fake, fake, fake)
+
+    def route(shape, ranks):
+        c = K.make_cache(fake, fake, fake, ranks)
+        return lib.kvlr_route_pages(ctypes.byref(shape), ctypes.byref(c), fake, fake, fake, 512, 1, 8,
+                                    64, fake, None, None, fake, ws, 4, None)
+
+    def encode(shape, ranks):
+        c = K.make_cache(fake, fake, fake, ranks)
+        return lib.kvlr_append_encode(ctypes.byref(shape), ctypes.byref(f), ctypes.byref(c), fake, fake,
+                                      fake, fake, fake, 512, 4, 4, None)
+
+    U, E = K.KVLR_ERR_UNSUPPORTED, K.KVLR_ERR_INVALID_ARGUMENT
+    s = _shape(rank_k=64)
+    for call in (route, encode):
+        assert call(s, [16, 32, 64, 48, 16, 16, 16, 16]) == E      # 48 is not a chunk-tile rank
+        assert call(_shape(rank_k=32), [64] * 8) == E                # above rank_k
+        assert call(_shape(rank_k=64, page_size=32), [16] * 8) == U  # 64-token pages only
+        assert call(_shape(rank_k=64, dtype=K.KVLR_DTYPE_F32), [16] * 8) == U
+        assert call(_shape(rank_k=64, num_q_heads=68, num_kv_heads=17), [16] * 17) == U  # > 16 heads
+    assert encode(_shape(rank_k=64, key_mode=K.KVLR_KEYS_LATENT), [16] * 8) == U   # routed keys only

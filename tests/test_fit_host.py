@@ -137,3 +137,25 @@ def test_diagonal_moments_give_coordinate_axes(lib):
         order = np.argsort(-diag)[:16]
         np.testing.assert_allclose(lam, diag[order], rtol=1e-14)
         np.testing.assert_allclose(A, np.eye(64)[:, order], atol=1e-14)
+
+
+def test_choose_residual_ranks_cases_and_library(lib):
+    from oracle import choose_residual_ranks
+    # hand-made spectra: energy within the top 64 = 100 units
+    lam = np.zeros((4, 64))
+    lam[0, :16] = 100 / 16                   # all of it in the first 16
+    lam[1, :32] = 100 / 32                   # half in 0..15, half in 16..31
+    lam[2, :] = 100 / 64                     # flat: 25 % per 16
+    lam[3, :16] = 89 / 16
+    lam[3, 16:] = 11 / 48                    # 89 % in the first 16
+    assert choose_residual_ranks(lam, 0.9) == [16, 32, 64, 32]
+    assert choose_residual_ranks(lam, 0.5) == [16, 16, 32, 16]
+    # r_max 32: head 3 keeps 89 of 92.7 units in its top 16 (96 %)
+    assert choose_residual_ranks(lam[:, :32], 0.9) == [16, 32, 32, 16]
+    s = fit_shape(_wl(num_kv_heads=4, num_q_heads=16, rank_k=64))
+    assert K.kvlr_choose_residual_ranks(s, np.ascontiguousarray(lam), 0.9) == [16, 32, 64, 32]
+    rng = np.random.default_rng(9)
+    for frac in (0.5, 0.8, 0.95, 1.0):
+        lam = -np.sort(-rng.exponential(size=(4, 64)) * rng.uniform(0.05, 1, (4, 1)) ** 8, axis=1)
+        assert K.kvlr_choose_residual_ranks(s, np.ascontiguousarray(lam), frac) == \
+            choose_residual_ranks(lam, frac)

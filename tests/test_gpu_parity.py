@@ -28,7 +28,7 @@ def _say(*a):
 
 
 def make_wl(*, G, d, rv, rk, P, storage, routed, B=4, Hkv=2, topk=(1, 8), seed=11, planted=0.0,
-            exact=None, value_basis="random", latent=""):
+            exact=None, value_basis="random", latent="", ranks=()):
     exact = routed if exact is None else exact
     rs = min(48, d // 2)
     ns = min(rv, rs // 2, d - rk) if exact else 0
@@ -39,7 +39,7 @@ def make_wl(*, G, d, rv, rk, P, storage, routed, B=4, Hkv=2, topk=(1, 8), seed=1
         rank_k=rk, storage=storage, key_mode="exact" if exact else "latent", context=0,
         topk_num=topk[0], topk_den=topk[1], signal_rank=rs, shared_rank=ns, noise_std=0.05,
         planted_frac=planted, planted_boost=4.0 if planted else 0.0, seed=seed,
-        route=routed, value_basis=value_basis, latent_storage=latent)
+        route=routed, value_basis=value_basis, latent_storage=latent, residual_ranks=tuple(ranks))
 
 
 def run_and_check(sess, pairs=None, stage=True):
@@ -122,6 +122,26 @@ def test_fp8_latents_dense(cfg):
     wl = make_wl(routed=False, P=64, storage="bf16", latent="fp8", **cfg)
     _say("case", wl.name)
     sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    run_and_check(sess)
+
+
+# per-head residual ranks (adaptive residual), routed, 64-token pages
+ADAPTIVE = [
+    dict(G=4, d=128, rv=64, rk=64, Hkv=2, ranks=(16, 64), latent=""),
+    dict(G=8, d=64, rv=32, rk=32, Hkv=2, ranks=(32, 16), latent="fp8"),
+    dict(G=2, d=128, rv=32, rk=64, Hkv=4, ranks=(16, 32, 64, 16), latent=""),
+    dict(G=1, d=128, rv=64, rk=64, Hkv=4, ranks=(64, 16, 16, 32), latent="fp8"),
+]
+
+
+@pytest.mark.parametrize("cfg", ADAPTIVE, ids=lambda c: "-".join(
+    f"{k}{'_'.join(map(str, v)) if isinstance(v, tuple) else v}" for k, v in c.items()))
+def test_per_head_residual_ranks(cfg):
+    wl = make_wl(routed=True, P=64, storage="bf16", **cfg)
+    _say("case", wl.name, wl.residual_ranks)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37, spare_pages=3,
+                         tail_fill=float("nan"))
+    assert sess.k_lat.shape[1] == sum(wl.residual_ranks) // 8
     run_and_check(sess)
 
 

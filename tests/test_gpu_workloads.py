@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 FULL = ["llama3-8b-dense-32k", "llama3-8b-routed-32k", "llama3-70b-share-routed-128k",
         "mixed-append-routed-ragged", "llama3-8b-uncompressed-32k", "llama3-8b-routed-fp8-32k",
-        "llama3-70b-share-routed-fp8-128k"]
+        "llama3-70b-share-routed-fp8-128k", "llama3-8b-routed-adaptive-32k"]
 
 
 def _sample(sess):
