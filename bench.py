@@ -104,8 +104,10 @@ def _oracle_inputs(sess, b, g, memo):
     st_rows = memo["rows"]
     off = sum(sess.n_new[:b])
     n = sess.n_new[b]
+    prefix = {k: H.f64(v[g]) for k, v in st_rows.items()}
+    prefix["k_lat"] = H.k_cols(sess, g, prefix["k_lat"])  # the head's kept residual coordinates
     return {
-        "prefix": {k: H.f64(v[g]) for k, v in st_rows.items()},
+        "prefix": prefix,
         "L_before": sess.lens_before[b], "L": sess.seq_lens[b],
         "K": H.f64(sess.k_new[off:off + n, g]), "V": H.f64(sess.v_new[off:off + n, g]),
         "f": H.factors_np(sess, g), "q": H.q_group(sess, b, g),
@@ -118,7 +120,7 @@ def _oracle_pair(wl, scale, it):
 
     f = it["f"]
     st = O.append_tokens(it["prefix"], it["L_before"], it["K"], it["V"], f["A_v"], f["A_k"],
-                         f["W_pred"], key_mode=wl.key_mode, storage=wl.storage)
+                         f["W_pred"], key_mode=wl.key_mode, storage=wl.lat_storage)
     res = O.decode_pair(it["q"], st, f, it["L"], wl.page_size, key_mode=wl.key_mode, scale=scale,
                         topk=(wl.topk_num, wl.topk_den))
     O.upproject(res["z"], f["B_v"])

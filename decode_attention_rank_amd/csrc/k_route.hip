@@ -302,7 +302,10 @@ __device__ inline float row_score(const float (&qv)[NQ], const uint4 (&vc)[RV / 
 // ROWPAGE: page_size == 64, so a row is exactly one page; its page-table
 // entry and base address are wave-uniform, and the next row's loads are
 // issued before the current row is scored.
-template <class S, int G, int RV, int RK, bool ROWPAGE>
+// ADAPT: per-head residual ranks (the residual's chunk count and offset are
+// per head); uniform caches keep them compile-time, so address offsets fold
+// into the load instructions.
+template <class S, int G, int RV, int RK, bool ROWPAGE, bool ADAPT = false>
 __global__ __launch_bounds__(kThreads) void route_kernel(
     const uint8_t* __restrict__ v_lat, const uint8_t* __restrict__ k_lat,
     const float* __restrict__ q_proj, const int32_t* __restrict__ seq_lens,
@@ -325,11 +328,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   // work chunks of head g span rpc(g) rows: rows_per_chunk, or with per-head
   // residual ranks a count that gives every chunk about the same bytes
-  auto rpc_of = [&](int g) { return kl.adaptive ? kl.rpc[g] : rows_per_chunk; };
+  auto rpc_of = [&](int g) { return ADAPT ? kl.rpc[g] : rows_per_chunk; };
   auto splits_of = [&](int rows, int g) { return max(1, (rows + rpc_of(g) - 1) / rpc_of(g)); };
   build_chunk_prefix(batch, s_base, [&](int b) {
     const int rows = (seq_lens[b] + kWave - 1) / kWave;
-    if (!kl.adaptive) return Hkv * splits_of(rows, 0);
+    if (!ADAPT) return Hkv * splits_of(rows, 0);
     int n = 0;
     for (int g = 0; g < Hkv; ++g) n += splits_of(rows, g);
     return n;
@@ -337,12 +340,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   const int total = s_base[batch];
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int b = find_sequence(s_base, batch, w);
+    const int b = __builtin_amdgcn_readfirstlane(find_sequence(s_base, batch, w));
     const int L = seq_lens[b];
     const int nrows = (L + kWave - 1) / kWave;
-    int local = w - s_base[b];
+    int local = __builtin_amdgcn_readfirstlane(w - s_base[b]);
     int g, nsplit;
-    if (!kl.adaptive) {
+    if (!ADAPT) {
       nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
       g = local / nsplit;
       local -= g * nsplit;
@@ -354,15 +357,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         nsplit = splits_of(nrows, ++g);
       }
     }
-    const int split = local;
+    // every value here is the same across the workgroup; saying so keeps the
+    // per-head table reads and what derives from them in scalar registers
+    g = __builtin_amdgcn_readfirstlane(g);
+    nsplit = __builtin_amdgcn_readfirstlane(nsplit);
+    const int split = __builtin_amdgcn_readfirstlane(local);
     const int rpc = rpc_of(g);
     const int pair = b * Hkv + g;
     const float* __restrict__ qp = q_proj + static_cast<size_t>(b * Hq + g * G) * W;
     const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
     float* __restrict__ sc = scores + static_cast<size_t>(pair) * max_pages;
     // the vector-ALU paths keep the projected queries spread over the lanes
-    // (FP8 latents have only the matrix-core path)
-    constexpr bool kMfma = ROWPAGE && S::CH == 8 && (KVLR_ROUTE_MFMA || S::CB == 8);
+    // (FP8 latents and per-head residual ranks have only the matrix-core path)
+    constexpr bool kMfma = ROWPAGE && S::CH == 8 && (KVLR_ROUTE_MFMA || S::CB == 8 || ADAPT);
     float qv[kMfma ? 1 : NQ];
     if constexpr (!kMfma) load_q_rows(qp, qv);
     const int row0 = split * rpc;
@@ -384,9 +391,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       // own offset; chunks past ckg are not read (their query half is zero).
       constexpr int KSV = (CV + 3) / 4, KSK = (CK + 3) / 4, KS = KSV + KSK;
       const int kq = lane >> 4, col = lane & 15;
-      const int ckg = kl.adaptive ? kl.ck[g] : CK;
-      const size_t kpage = kl.adaptive ? static_cast<size_t>(kl.page_chunks) * P * S::CB : Hkv * slab_k;
-      const size_t koff = kl.adaptive ? static_cast<size_t>(kl.off[g]) * P * S::CB : g * slab_k;
+      const int ckg = ADAPT ? kl.ck[g] : CK;
+      const size_t kpage = ADAPT ? static_cast<size_t>(kl.page_chunks) * P * S::CB : Hkv * slab_k;
+      const size_t koff = ADAPT ? static_cast<size_t>(kl.off[g]) * P * S::CB : g * slab_k;
       bf16x8 qhi[KS], qlo[KS];
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
@@ -609,11 +616,22 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
   dim3 grid(a.grid);
   if (a.dm.P == kWave) {
-    hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true>), grid, dim3(kThreads), lds, s,
-                       static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
-                       a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts, a.dm.Hq,
-                       a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max,
-                       a.rows_per_chunk, a.batch, a.kl);
+    if (a.kl.adaptive) {
+      if constexpr (S::CH == 8)  // per-head ranks: matrix-core path (bf16 or FP8 latents) only
+        hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true, true>), grid, dim3(kThreads), lds, s,
+                           static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
+                           a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel,
+                           a.sel_counts, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num,
+                           a.topk_den, a.k_max, a.rows_per_chunk, a.batch, a.kl);
+      else
+        return hipErrorInvalidValue;
+    } else {
+      hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true>), grid, dim3(kThreads), lds, s,
+                         static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
+                         a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
+                         a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
+                         a.k_max, a.rows_per_chunk, a.batch, a.kl);
+    }
   } else {
     if constexpr (S::CB == 8) return hipErrorInvalidValue;  // FP8 latents: 64-token pages only
     else
