@@ -35,7 +35,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstring>
 #include <thread>
 #include <vector>
 
