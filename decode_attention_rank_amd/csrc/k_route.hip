@@ -379,17 +379,21 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       // Matrix-core scoring (bf16 or FP8 latents, one page per row). A 64-token
       // row is four 16-token tiles; per tile, scores[token][head] = sum over
       // the concatenated [v | c] latent (K, in steps of 32) of latent x query,
-      // as v_mfma_f32_16x16x32_bf16 with tokens as rows (lane l: token l%16,
-      // 8 latent elements from k-group l/16: one chunk of the page, 16 bytes
-      // of bf16 or 8 bytes of FP8 decoded exactly to bf16) and heads as
+      // as v_mfma_f32_16x16x32_bf16 with tokens as rows (lane l: row l%16, 8
+      // latent elements from k-group l/16: one chunk of the page) and heads as
       // columns (the projected queries split into bf16 high and low halves,
-      // two products per step). Heads past the group and tokens past the
-      // sequence end are masked before the page max.
+      // two products per step). A lane's 16-byte load holds TPL consecutive
+      // tokens of one chunk column (1 bf16 chunk, or 2 FP8 chunks decoded
+      // exactly to bf16), and tile t = p*TPL + h takes the tokens
+      // TPL*(16p + row) + h, so one load feeds TPL tiles. Heads past the
+      // group and tokens past the sequence end are masked before the page max.
       // k-steps: ceil(CV/4) over the value latent, then ceil(CK/4) over the
       // residual, so each step reads one slab (a uniform base address). With
       // per-head residual ranks this head's slab has ckg <= CK chunks at its
       // own offset; chunks past ckg are not read (their query half is zero).
       constexpr int KSV = (CV + 3) / 4, KSK = (CK + 3) / 4, KS = KSV + KSK;
+      constexpr int TPL = 16 / S::CB;  // tokens per 16-byte load
+      constexpr int NL = 4 / TPL;      // loads per k-step and row
       const int kq = lane >> 4, col = lane & 15;
       const int ckg = ADAPT ? kl.ck[g] : CK;
       const size_t kpage = ADAPT ? static_cast<size_t>(kl.page_chunks) * P * S::CB : Hkv * slab_k;
@@ -425,50 +429,57 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         const size_t phys = static_cast<size_t>(pt[row]);
         return RowRef{v_lat + (phys * Hkv + g) * slab_v, k_lat + phys * kpage + koff, 1};
       };
-      auto a_addr = [&](const RowRef& rr, int j, int st) -> const uint8_t* {
+      auto a_addr = [&](const RowRef& rr, int p, int st) -> const uint8_t* {
         const bool on_v = st < KSV;
         int ci = 4 * (on_v ? st : st - KSV) + kq;
         if (ci >= (on_v ? CV : ckg)) ci = 0;
         const uint32_t off = static_cast<uint32_t>(rr.on) *
-                             static_cast<uint32_t>((j * 16 + col) * S::CB + ci * (kWave * S::CB));
+                             static_cast<uint32_t>(TPL * (p * 16 + col) * S::CB + ci * (kWave * S::CB));
         return (on_v ? rr.vb : rr.kb) + off;
       };
       int r = row0 + wave;
-      typename S::Raw A[4][KS];
+      uint4 A[NL][KS];
       // residual k-steps past this head's rank (per-head ranks) are skipped:
       // a wave-uniform test, compiled only where the residual spans 2+ steps
       const int ks_used = KSV + (ckg + 3) / 4;
       auto step_on = [&](int st) { return st <= KSV || st < ks_used; };
       RowRef cur = row_ref(r);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int p = 0; p < NL; ++p)
 #pragma unroll
         for (int st = 0; st < KS; ++st)
-          if (step_on(st)) A[j][st] = S::load_stream(a_addr(cur, j, st));
+          if (step_on(st)) A[p][st] = load16_stream(a_addr(cur, p, st));
       RowRef nxt = row_ref(r + kWaves);
       for (; r < row1; r += kWaves) {
         const RowRef nn = row_ref(r + 2 * kWaves);  // page-table entry two rows ahead
         f32x4 acc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NL; ++p) {
 #pragma unroll
           for (int st = 0; st < KS; ++st) {
             if (!step_on(st)) continue;
-            const bf16x8 a = S::to_bf16x8(A[j][st]);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[st], acc[j], 0, 0, 0);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[st], acc[j], 0, 0, 0);
-            A[j][st] = S::load_stream(a_addr(nxt, j, st));
+#pragma unroll
+            for (int h = 0; h < TPL; ++h) {
+              const bf16x8 a = S::frag_of16(A[p][st], h);
+              f32x4& c = acc[p * TPL + h];
+              c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[st], c, 0, 0, 0);
+              c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[st], c, 0, 0, 0);
+            }
+            A[p][st] = load16_stream(a_addr(nxt, p, st));
           }
         }
         const int nvalid = L - r * kWave;
         float m = -__builtin_huge_valf();
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const bool ok = col < G && (j * 16 + 4 * kq + v) < nvalid;
-            m = ok ? fmaxf(m, acc[j][v]) : m;
+            // output row 4*kq + v of tile t is token TPL*(16*(t/TPL) + 4*kq + v) + t%TPL
+            const int tok = TPL * (16 * (t / TPL) + 4 * kq + v) + t % TPL;
+            const bool ok = col < G && tok < nvalid;
+            m = ok ? fmaxf(m, acc[t][v]) : m;
           }
         m = wave_max_u(m);
         if (lane == 0) store_shared_f32(&sc[r], m);

@@ -34,6 +34,8 @@ struct BF16 {
   using Raw = uint4;
   __device__ static inline Raw load_stream(const void* p) { return load16_stream(p); }
   __device__ static inline bf16x8 to_bf16x8(const Raw& r) { return __builtin_bit_cast(bf16x8, r); }
+  // 16 loaded bytes hold one token's chunk: fragment h = 0 only
+  __device__ static inline bf16x8 frag_of16(const uint4& r, int) { return __builtin_bit_cast(bf16x8, r); }
   // element e of a chunk as float (bf16 -> f32 is a 16-bit shift, exact)
   __device__ static inline void unpack(const uint4& c, float (&x)[CH]) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -100,6 +102,10 @@ struct FP8 {
     for (int i = 0; i < 4; ++i)
       h[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
     return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  }
+  // 16 loaded bytes hold two tokens' chunks: fragment h of token h
+  __device__ static inline bf16x8 frag_of16(const uint4& r, int h) {
+    return to_bf16x8(h ? make_uint2(r.z, r.w) : make_uint2(r.x, r.y));
   }
 };
 
