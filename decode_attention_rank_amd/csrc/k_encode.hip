@@ -16,7 +16,7 @@
 // for bf16, split into a high and a low bf16 part so the product with the
 // stored (bf16) latent v keeps about 16 significant bits of the matrix.
 //
-// Work split: grid (token-tile groups, KV head). A workgroup stages the
+// Work split: grid (KV head, token-tile groups). A workgroup stages the
 // factor fragments of its head in LDS once, then loops over 64-token tiles,
 // 16 tokens per wave: the wave loads its tokens' rows straight into MFMA
 // A-operand registers, multiplies, rounds into a per-wave LDS tile and writes
@@ -150,7 +150,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   __shared__ SM sm;
   extern __shared__ int s_seq[];  // cu_new[0..batch], then lens_before[0..batch)
 
-  const int g = blockIdx.y;
+  // KV heads vary fastest over the grid: workgroups launched together take
+  // the same tokens of every head, so the new rows (all heads of a token are
+  // adjacent) and the pages written are read and written in whole spans
+  const int g = blockIdx.x;
+  const int tile0 = blockIdx.y, tile_step = gridDim.y;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   // this workgroup's first tile, and the W_pred rows of M = W_pred A_k, are
   // requested before the set-up below
   frag_t vf[KSD], kf[KSD];
-  load_tile(blockIdx.x, vf, kf);
+  load_tile(tile0, vf, kf);
   constexpr int MT = ROUTED ? (NTV * NTK + kWaves - 1) / kWaves : 0;  // M tiles per wave
   frag_t wa[MT > 0 ? MT : 1][KSD];
   if constexpr (ROUTED) {
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   };
   // the first tile's page-table entry is requested before M is formed
   size_t slot0 = 0;
-  const int phys0 = *locate(blockIdx.x, slot0);
+  const int phys0 = *locate(tile0, slot0);
 
   if constexpr (ROUTED) {
     // M = W_pred A_k  [RV x RK], 16x16 tiles spread over the waves
@@ -361,14 +365,29 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     wave_lds_sync();
   };
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    size_t slot = slot0;
-    int phys = phys0;
-    if (tile != static_cast<int>(blockIdx.x)) {
-      load_tile(tile, vf, kf);
-      phys = *locate(tile, slot);
+  // Tiles of this workgroup, with the next tile's rows and page-table entry
+  // requested before the current tile is processed: two register sets take
+  // turns (the loop body runs two tiles), so the loads stay in flight under
+  // the products and stores of the tile before.
+  auto run = [&](int tile, const frag_t (&vc)[KSD], const frag_t (&kc)[KSD], int phys, size_t slot,
+                 frag_t (&vn)[KSD], frag_t (&kn)[KSD], int& phys_n, size_t& slot_n) -> bool {
+    const int next = tile + tile_step;
+    const bool more = next < ntiles;  // uniform over the workgroup
+    if (more) {
+      load_tile(next, vn, kn);
+      phys_n = *locate(next, slot_n);
     }
-    process(tile, vf, kf, static_cast<size_t>(phys), slot);
+    process(tile, vc, kc, static_cast<size_t>(phys), slot);
+    return more;
+  };
+  frag_t vf2[KSD], kf2[KSD];
+  int tile = tile0, phys = phys0, phys2 = 0;
+  size_t slot = slot0, slot2 = 0;
+  for (;;) {
+    if (!run(tile, vf, kf, phys, slot, vf2, kf2, phys2, slot2)) break;
+    tile += tile_step;
+    if (!run(tile, vf2, kf2, phys2, slot2, vf, kf, phys, slot)) break;
+    tile += tile_step;
   }
 }
 
@@ -378,7 +397,7 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   const int ntiles = (a.total_new + 63) / 64;
   int per_head = (KVLR_ENCODE_WGS + a.dm.Hkv - 1) / a.dm.Hkv;
   if (per_head > ntiles) per_head = ntiles;
-  dim3 grid(per_head, a.dm.Hkv);
+  dim3 grid(a.dm.Hkv, per_head);
   const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
   hipLaunchKernelGGL((encode_kernel<S, LS, D, RV, RK, ROUTED>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(a.A_v), static_cast<const uint8_t*>(a.A_k),
