@@ -365,29 +365,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     wave_lds_sync();
   };
 
-  // Tiles of this workgroup, with the next tile's rows and page-table entry
-  // requested before the current tile is processed: two register sets take
-  // turns (the loop body runs two tiles), so the loads stay in flight under
-  // the products and stores of the tile before.
-  auto run = [&](int tile, const frag_t (&vc)[KSD], const frag_t (&kc)[KSD], int phys, size_t slot,
-                 frag_t (&vn)[KSD], frag_t (&kn)[KSD], int& phys_n, size_t& slot_n) -> bool {
-    const int next = tile + tile_step;
-    const bool more = next < ntiles;  // uniform over the workgroup
-    if (more) {
-      load_tile(next, vn, kn);
-      phys_n = *locate(next, slot_n);
+  for (int tile = tile0; tile < ntiles; tile += tile_step) {
+    size_t slot = slot0;
+    int phys = phys0;
+    if (tile != tile0) {
+      load_tile(tile, vf, kf);
+      phys = *locate(tile, slot);
     }
-    process(tile, vc, kc, static_cast<size_t>(phys), slot);
-    return more;
-  };
-  frag_t vf2[KSD], kf2[KSD];
-  int tile = tile0, phys = phys0, phys2 = 0;
-  size_t slot = slot0, slot2 = 0;
-  for (;;) {
-    if (!run(tile, vf, kf, phys, slot, vf2, kf2, phys2, slot2)) break;
-    tile += tile_step;
-    if (!run(tile, vf2, kf2, phys2, slot2, vf, kf, phys, slot)) break;
-    tile += tile_step;
+    process(tile, vf, kf, static_cast<size_t>(phys), slot);
   }
 }
 
