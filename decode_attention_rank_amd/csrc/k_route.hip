@@ -159,15 +159,17 @@ __device__ inline int block_excl_sum(int v, int* total, int* lds4) {
 
 constexpr int kSelectLds = 4096;  // largest page count selected from LDS
 
-// select_pages for N <= kSelectLds: the order keys are read once into LDS;
-// the radix passes run on LDS, and the ascending compaction gives thread t
-// the contiguous pages t*per .. t*per+per-1 (two block-wide scans place them).
+// select_pages for N <= kSelectLds: the order keys are read once into LDS and
+// the radix passes run there. Each pass has its own histogram (all four are
+// cleared up front), so a pass costs one barrier: after it every wave scans
+// the histogram itself and finds the same bin. The passes stop early once
+// the bin holding the k-th largest key is taken whole. The ascending
+// compaction gives thread t the contiguous pages t*per .. t*per+per-1, placed
+// by one block-wide scan of the packed (above, equal) counts.
 __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max_pages,
                                  int32_t* sel) {
   __shared__ uint32_t s_keys[kSelectLds];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_kk;
+  __shared__ uint4 hist4[4][kWave];  // per pass: 256 bins, lane l owns bins 4l .. 4l+3
   __shared__ int lds4[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -177,6 +179,7 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
   // Indices past N re-read score N-1 and are not kept.
   typedef __attribute__((address_space(1))) float gfloat;
   gfloat* gs = (gfloat*)scores;
+  if (tid < 4 * kWave) (&hist4[0][0])[tid] = make_uint4(0, 0, 0, 0);
   for (int j0 = 0; j0 < N; j0 += 8 * kThreads) {
     float v[8];
 #pragma unroll
@@ -192,65 +195,65 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
   __syncthreads();
 
   const bool take_all = (k >= N);
+  // the kept pages: (key & pmask) > prefix, then the kk lowest-index pages
+  // with (key & pmask) == prefix
   uint32_t prefix = 0, pmask = 0;
   int kk = k;
   if (!take_all && k > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;  // kThreads == 256 bins
-      __syncthreads();
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      uint32_t* h = reinterpret_cast<uint32_t*>(&hist4[pass][0]);
       for (int j = tid; j < N; j += kThreads) {
         const uint32_t key = s_keys[j];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid < kWave) {
-        // lane l owns bins 4l .. 4l+3; suffix sums from the top bin down
-        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-        const uint32_t local = h0 + h1 + h2 + h3;
-        uint32_t suf = local;
+      // every wave: suffix sums from the top bin down, then the bin holding
+      // the kk-th largest candidate (lane 0's suffix is every candidate, so
+      // some lane qualifies)
+      const uint4 hb = hist4[pass][lane];
+      const uint32_t local = hb.x + hb.y + hb.z + hb.w;
+      uint32_t suf = local;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const uint32_t o = __shfl_down(suf, off, kWave);
-          if (lane + off < kWave) suf += o;
-        }
-        const uint64_t hit = __ballot(suf >= static_cast<uint32_t>(kk));
-        const int top = 63 - __clzll(hit);
-        if (lane == top) {
-          // the bin (4*lane + d) holding the kk-th largest key, scanning d = 3 .. 0
-          const uint32_t a3 = suf - local, a2 = a3 + h3, a1 = a2 + h2, a0 = a1 + h1;
-          const uint32_t need = static_cast<uint32_t>(kk);
-          const int d = (a3 + h3 >= need) ? 3 : (a2 + h2 >= need) ? 2 : (a1 + h1 >= need) ? 1 : 0;
-          const uint32_t above = (d == 3) ? a3 : (d == 2) ? a2 : (d == 1) ? a1 : a0;
-          s_digit = static_cast<uint32_t>(4 * lane + d);
-          s_kk = kk - static_cast<int>(above);
-        }
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_down(suf, off, kWave);
+        if (lane + off < kWave) suf += o;
       }
-      __syncthreads();
-      prefix |= s_digit << shift;
+      const uint32_t need = static_cast<uint32_t>(kk);
+      const int top = 63 - __clzll(__ballot(suf >= need));
+      // bins 4l+3 .. 4l of lane l, scanned from the top
+      const uint32_t a3 = suf - local, a2 = a3 + hb.w, a1 = a2 + hb.z, a0 = a1 + hb.y;
+      const int d = (a3 + hb.w >= need) ? 3 : (a2 + hb.z >= need) ? 2 : (a1 + hb.y >= need) ? 1 : 0;
+      const uint32_t above = (d == 3) ? a3 : (d == 2) ? a2 : (d == 1) ? a1 : a0;
+      const uint32_t cnt = (d == 3) ? hb.w : (d == 2) ? hb.z : (d == 1) ? hb.y : hb.x;
+      const uint32_t digit = static_cast<uint32_t>(__builtin_amdgcn_readlane(4 * lane + d, top));
+      const int above_t = __builtin_amdgcn_readlane(static_cast<int>(above), top);
+      const int cnt_t = __builtin_amdgcn_readlane(static_cast<int>(cnt), top);
+      prefix |= digit << shift;
       pmask |= 255u << shift;
-      kk = s_kk;
-      __syncthreads();
+      kk -= above_t;
+      if (cnt_t == kk) break;  // the whole bin is kept: the same in every wave
     }
   }
-  // prefix = key of the k-th largest score; the kk lowest-index pages with
-  // exactly that key are taken, with every page above it
   const int per = (N + kThreads - 1) / kThreads;
   const int jb = min(tid * per, N), je = min(jb + per, N);
   const bool use_eq = !take_all && k > 0;
   int n_gt = 0, n_eq = 0;
   for (int j = jb; j < je; ++j) {
-    const uint32_t key = s_keys[j];
+    const uint32_t key = s_keys[j] & pmask;
     n_gt += (take_all || key > prefix) ? 1 : 0;
     n_eq += (use_eq && key == prefix) ? 1 : 0;
   }
+  // one scan of both counts (each sum is at most N <= 4096 < 2^16); the
+  // equal keys are taken in index order, so the threads before this one
+  // took min(kk, equal keys before) of them
   int tot = 0;
-  const int eq_before = block_excl_sum(n_eq, &tot, lds4);
-  const int eq_take = min(max(kk - eq_before, 0), n_eq);
-  int pos = block_excl_sum(n_gt + eq_take, &tot, lds4);
+  const int packed = block_excl_sum((n_gt << 16) | n_eq, &tot, lds4);
+  const int gt_before = packed >> 16, eq_before = packed & 0xffff;
+  int pos = gt_before + min(kk, eq_before);
   int eq_rank = eq_before;
   for (int j = jb; j < je; ++j) {
-    const uint32_t key = s_keys[j];
+    const uint32_t key = s_keys[j] & pmask;
     const bool gt = take_all || key > prefix;
     const bool eq = use_eq && key == prefix;
     const bool take = gt || (eq && eq_rank < kk);
