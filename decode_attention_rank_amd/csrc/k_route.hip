@@ -694,7 +694,10 @@ hipError_t by_g(const RouteArgs& a, hipStream_t s) {
 #ifndef KVLR_ROUTE_RPC
 #define KVLR_ROUTE_RPC 64
 #endif
-int route_rows_per_chunk() { return KVLR_ROUTE_RPC; }
+// Rows of at most 8 KB (rank_v + rank_k <= 64 with bf16 latents, <= 128 with
+// FP8) take twice as many per chunk: a chunk's fixed costs (sequence lookup,
+// query fragments, the hand-off) then weigh less per byte read.
+int route_rows_per_chunk(int row_bytes) { return row_bytes <= 8192 ? 2 * KVLR_ROUTE_RPC : KVLR_ROUTE_RPC; }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;

@@ -106,6 +106,12 @@ Plan plan_for(const Dims& dm, int batch, int max_pages) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Bytes of one 64-token routing row holding `width` latent elements per token.
+int route_row_bytes(const Dims& dm, int width) {
+  const int elem = dm.lat == 2 ? 1 : dm.lat == 1 ? 4 : 2;
+  return 64 * width * elem;
+}
+
 // Residual-latent layout from the cache's per-head rank table (NULL:
 // uniform). Per-head ranks need routed keys, 64-token pages, bf16 keys and
 // bf16 or FP8 latents, at most kMaxAdaptiveHeads KV heads, and each rank in
@@ -130,7 +136,8 @@ kvlr_status residual_layout(const Dims& dm, const kvlr_cache* cache, kvlr::KLayo
   int rmin = 64;
   for (int g = 0; g < dm.Hkv; ++g) rmin = cache->k_lat_ranks[g] < rmin ? cache->k_lat_ranks[g] : rmin;
   for (int g = 0; g < dm.Hkv; ++g) {
-    const int rpc = kvlr::route_rows_per_chunk() * (dm.RV + rmin) / (dm.RV + cache->k_lat_ranks[g]);
+    const int rpc = kvlr::route_rows_per_chunk(route_row_bytes(dm, dm.RV + rmin)) * (dm.RV + rmin) /
+                    (dm.RV + cache->k_lat_ranks[g]);
     kl->rpc[g] = rpc > 1 ? rpc : 1;
   }
   return KVLR_OK;
@@ -277,7 +284,7 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.counters = reinterpret_cast<uint32_t*>(ws + plan.route_cnt);
   a.batch = batch;
   const int max_rows = ceil_div(static_cast<long long>(max_pages_per_seq) * dm.P, 64);
-  a.rows_per_chunk = kvlr::route_rows_per_chunk();
+  a.rows_per_chunk = kvlr::route_rows_per_chunk(route_row_bytes(dm, dm.RV + dm.RK));
   long long chunks = 0;
   for (int g = 0; g < dm.Hkv; ++g) {
     const int rpc = a.kl.adaptive ? a.kl.rpc[g] : a.rows_per_chunk;

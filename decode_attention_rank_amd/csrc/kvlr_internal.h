@@ -57,7 +57,7 @@ struct RouteArgs {
   int grid;             // persistent workgroups
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
-int route_rows_per_chunk();
+int route_rows_per_chunk(int row_bytes);  // row_bytes: one 64-token row of [v | c] latents
 
 struct AttnArgs {
   Dims dm;
