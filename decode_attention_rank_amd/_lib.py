@@ -31,7 +31,7 @@ KVLR_KEYS_LATENT = 0
 KVLR_KEYS_EXACT = 1
 
 EXPORTED = (
-    "kvlr_append_encode", "kvlr_project_queries", "kvlr_qproj_width", "kvlr_route_pages",
+    "kvlr_append_encode", "kvlr_append_encode_project", "kvlr_project_queries", "kvlr_qproj_width", "kvlr_route_pages",
     "kvlr_decode_attn", "kvlr_decode_attn_upproject", "kvlr_upproject", "kvlr_workspace_bytes",
     "kvlr_workspace_init", "kvlr_fold_output_weights", "kvlr_output_projection",
     "kvlr_status_string", "kvlr_version", "kvlr_fit_workspace_bytes", "kvlr_fit_moments",
@@ -71,6 +71,9 @@ _I = ctypes.c_int32
 _SIG = {
     "kvlr_append_encode": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
                             ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _P, _I, _I, _I, _P], _I),
+    "kvlr_append_encode_project": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
+                                    ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _P, _I, _I, _I, _P,
+                                    _P, _P], _I),
     "kvlr_project_queries": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_qproj_width": ([ctypes.POINTER(kvlr_shape)], _I),
     "kvlr_route_pages": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _I, _I,
@@ -195,6 +198,15 @@ def kvlr_append_encode(shape, factors, cache, k_new, v_new, cu_new, seq_lens_bef
         ctypes.byref(shape), ctypes.byref(factors), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
         _ptr(cu_new), _ptr(seq_lens_before), _ptr(page_table), max_pages_per_seq, batch, total_new,
         _stream(stream)))
+
+
+def kvlr_append_encode_project(shape, factors, cache, k_new, v_new, cu_new, seq_lens_before,
+                               page_table, max_pages_per_seq, batch, total_new, q, q_proj,
+                               stream=None):
+    _check("kvlr_append_encode_project", lib().kvlr_append_encode_project(
+        ctypes.byref(shape), ctypes.byref(factors), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
+        _ptr(cu_new), _ptr(seq_lens_before), _ptr(page_table), max_pages_per_seq, batch, total_new,
+        _ptr(q), _ptr(q_proj), _stream(stream)))
 
 
 def kvlr_project_queries(shape, factors, q, q_proj, batch, stream=None):

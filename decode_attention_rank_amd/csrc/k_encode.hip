@@ -24,8 +24,12 @@
 // factors) the latents are rounded once from the float32 products to E4M3
 // (nearest even, saturating at +-448) and stored as 8-byte chunks; the
 // residual is taken against that stored latent, decoded exactly to bf16.
+// A launch may also carry the step's query projection: its first grid rows
+// then compute 16 x 16 tiles of q_proj (one per wave, on the float32 matrix
+// cores), independent of the encode, which saves the projection's own launch.
 
 #include "kvlr_device.h"
+#include "kvlr_gemm_tile.h"
 #include "kvlr_internal.h"
 
 #ifndef KVLR_ENCODE_WGS
@@ -130,6 +134,16 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Query-projection tiles carried by the same launch (kvlr_append_encode_project):
+// the first qy grid rows hold them, one 16 x 16 tile of q_proj per wave; the
+// encode's tile groups follow. qy = 0: none.
+struct QTiles {
+  const uint8_t* B_k;
+  const float* q;
+  float* q_proj;
+  int batch, Hq, G, row_tiles, col_tiles, qy;
+};
+
 template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(
     const uint8_t* __restrict__ A_v, const uint8_t* __restrict__ A_k,
@@ -137,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     const uint8_t* __restrict__ v_new, const int32_t* __restrict__ cu_new,
     const int32_t* __restrict__ lens_before, const int32_t* __restrict__ page_table,
     uint8_t* __restrict__ v_lat, uint8_t* __restrict__ k_lat, uint8_t* __restrict__ k_exact,
-    int Hkv, int P, int log2P, int max_pages, int batch, int total_new, KLayout kl) {
+    int Hkv, int P, int log2P, int max_pages, int batch, int total_new, KLayout kl, QTiles qt) {
   using MM = Mma<S>;
   using SM = EncSmem<S, LS, D, RV, RK, ROUTED>;
   using LT = Lat<S, LS>;
@@ -150,11 +164,24 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   __shared__ SM sm;
   extern __shared__ int s_seq[];  // cu_new[0..batch], then lens_before[0..batch)
 
+  if (static_cast<int>(blockIdx.y) < qt.qy) {  // a workgroup of query-projection tiles
+    const int t = (static_cast<int>(blockIdx.y) * static_cast<int>(gridDim.x) +
+                   static_cast<int>(blockIdx.x)) * kWaves + static_cast<int>(threadIdx.x) / kWave;
+    const int per_head = qt.row_tiles * qt.col_tiles;
+    if (t < per_head * Hkv) {
+      const int hg = t / per_head, rem = t - hg * per_head;
+      const int ct = rem / qt.row_tiles;
+      qproj_tile<S, D>(W_pred, qt.B_k, qt.q, qt.q_proj, qt.batch, qt.Hq, qt.G, RV, RK, ROUTED ? 1 : 0,
+                       rem - ct * qt.row_tiles, ct, hg);
+    }
+    return;
+  }
   // KV heads vary fastest over the grid: workgroups launched together take
   // the same tokens of every head, so the new rows (all heads of a token are
   // adjacent) and the pages written are read and written in whole spans
   const int g = blockIdx.x;
-  const int tile0 = blockIdx.y, tile_step = gridDim.y;
+  const int tile0 = static_cast<int>(blockIdx.y) - qt.qy;
+  const int tile_step = static_cast<int>(gridDim.y) - qt.qy;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
@@ -382,7 +409,21 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   const int ntiles = (a.total_new + 63) / 64;
   int per_head = (KVLR_ENCODE_WGS + a.dm.Hkv - 1) / a.dm.Hkv;
   if (per_head > ntiles) per_head = ntiles;
-  dim3 grid(a.dm.Hkv, per_head);
+  QTiles qt{};
+  if (a.q) {
+    qt.B_k = static_cast<const uint8_t*>(a.B_k);
+    qt.q = a.q;
+    qt.q_proj = a.q_proj;
+    qt.batch = a.batch;
+    qt.Hq = a.dm.Hq;
+    qt.G = a.dm.G;
+    qt.row_tiles = (a.batch * a.dm.G + 15) / 16;
+    qt.col_tiles = ((ROUTED ? RV : 0) + RK) / 16;
+    const int tiles = qt.row_tiles * qt.col_tiles * a.dm.Hkv;
+    qt.qy = (tiles + kWaves * a.dm.Hkv - 1) / (kWaves * a.dm.Hkv);
+  }
+  if (per_head + qt.qy == 0) return hipSuccess;
+  dim3 grid(a.dm.Hkv, per_head + qt.qy);
   const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
   hipLaunchKernelGGL((encode_kernel<S, LS, D, RV, RK, ROUTED>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(a.A_v), static_cast<const uint8_t*>(a.A_k),
@@ -390,7 +431,7 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
                      static_cast<const uint8_t*>(a.v_new), a.cu_new, a.lens_before, a.page_table,
                      static_cast<uint8_t*>(a.v_lat), static_cast<uint8_t*>(a.k_lat),
                      static_cast<uint8_t*>(a.k_exact), a.dm.Hkv, a.dm.P, log2P, a.max_pages,
-                     a.batch, a.total_new, a.kl);
+                     a.batch, a.total_new, a.kl, qt);
   return hipGetLastError();
 }
 
@@ -435,7 +476,7 @@ hipError_t by_d(const EncodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
-  if (a.total_new == 0 || a.batch == 0) return hipSuccess;
+  if (a.batch == 0 || (a.total_new == 0 && !a.q)) return hipSuccess;
   if (a.dm.lat == 2) return by_d<BF16, FP8>(a, s);
   if (a.dm.dtype == 0) return by_d<BF16, BF16>(a, s);
   return by_d<F32, F32>(a, s);

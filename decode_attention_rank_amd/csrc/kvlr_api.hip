@@ -181,6 +181,37 @@ kvlr_status kvlr_workspace_init(void* workspace, size_t ws_bytes, void* stream) 
   return hip_status(kvlr::launch_zero_fill(workspace, ws_bytes, as_stream(stream)));
 }
 
+// Checks the append's buffers and fills the encode part of *a (total_new > 0).
+static kvlr_status encode_args(const Dims& dm, const kvlr_factors* factors, const kvlr_cache* cache,
+                               const void* k_new, const void* v_new, const int32_t* cu_new,
+                               const int32_t* seq_lens_before, const int32_t* page_table,
+                               int32_t max_pages_per_seq, int32_t batch, int32_t total_new,
+                               kvlr::EncodeArgs* a) {
+  if (!ok_ptr(factors->A_v) || !ok_ptr(factors->A_k) || !ok_ptr(cache->v_lat) ||
+      !ok_ptr(cache->k_lat) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(cu_new) ||
+      !ok_ptr(seq_lens_before) || !ok_ptr(page_table))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (dm.exact && (!ok_ptr(factors->W_pred) || !ok_ptr(cache->k_exact))) return KVLR_ERR_INVALID_ARGUMENT;
+  const kvlr_status st = residual_layout(dm, cache, &a->kl);
+  if (st != KVLR_OK) return st;
+  a->dm = dm;
+  a->A_v = factors->A_v;
+  a->A_k = factors->A_k;
+  a->W_pred = factors->W_pred;
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->cu_new = cu_new;
+  a->lens_before = seq_lens_before;
+  a->page_table = page_table;
+  a->max_pages = max_pages_per_seq;
+  a->v_lat = cache->v_lat;
+  a->k_lat = cache->k_lat;
+  a->k_exact = cache->k_exact;
+  a->batch = batch;
+  a->total_new = total_new;
+  return KVLR_OK;
+}
+
 kvlr_status kvlr_append_encode(const kvlr_shape* shape, const kvlr_factors* factors,
                                const kvlr_cache* cache, const void* k_new, const void* v_new,
                                const int32_t* cu_new, const int32_t* seq_lens_before,
@@ -193,29 +224,41 @@ kvlr_status kvlr_append_encode(const kvlr_shape* shape, const kvlr_factors* fact
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
   if (batch == 0 || total_new == 0) return KVLR_OK;
   if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
-  if (!ok_ptr(factors->A_v) || !ok_ptr(factors->A_k) || !ok_ptr(cache->v_lat) ||
-      !ok_ptr(cache->k_lat) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(cu_new) ||
-      !ok_ptr(seq_lens_before) || !ok_ptr(page_table))
-    return KVLR_ERR_INVALID_ARGUMENT;
-  if (dm.exact && (!ok_ptr(factors->W_pred) || !ok_ptr(cache->k_exact))) return KVLR_ERR_INVALID_ARGUMENT;
   kvlr::EncodeArgs a{};
-  st = residual_layout(dm, cache, &a.kl);
+  st = encode_args(dm, factors, cache, k_new, v_new, cu_new, seq_lens_before, page_table,
+                   max_pages_per_seq, batch, total_new, &a);
   if (st != KVLR_OK) return st;
-  a.dm = dm;
-  a.A_v = factors->A_v;
-  a.A_k = factors->A_k;
-  a.W_pred = factors->W_pred;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.cu_new = cu_new;
-  a.lens_before = seq_lens_before;
-  a.page_table = page_table;
-  a.max_pages = max_pages_per_seq;
-  a.v_lat = cache->v_lat;
-  a.k_lat = cache->k_lat;
-  a.k_exact = cache->k_exact;
-  a.batch = batch;
-  a.total_new = total_new;
+  return hip_status(kvlr::launch_encode(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_append_encode_project(const kvlr_shape* shape, const kvlr_factors* factors,
+                                       const kvlr_cache* cache, const void* k_new,
+                                       const void* v_new, const int32_t* cu_new,
+                                       const int32_t* seq_lens_before, const int32_t* page_table,
+                                       int32_t max_pages_per_seq, int32_t batch, int32_t total_new,
+                                       const float* q, float* q_proj, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!factors || !cache || batch < 0 || total_new < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return KVLR_OK;
+  if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
+  if (!ok_ptr(factors->B_k) || !ok_ptr(q) || !ok_ptr(q_proj)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (dm.exact && !ok_ptr(factors->W_pred)) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::EncodeArgs a{};
+  if (total_new > 0) {
+    st = encode_args(dm, factors, cache, k_new, v_new, cu_new, seq_lens_before, page_table,
+                     max_pages_per_seq, batch, total_new, &a);
+    if (st != KVLR_OK) return st;
+  } else {
+    a.dm = dm;
+    a.W_pred = factors->W_pred;
+    a.batch = batch;
+  }
+  a.B_k = factors->B_k;
+  a.q = q;
+  a.q_proj = q_proj;
   return hip_status(kvlr::launch_encode(a, as_stream(stream)));
 }
 

@@ -131,6 +131,10 @@ struct EncodeArgs {
   int batch;
   int total_new;
   KLayout kl;
+  // optional: the step's query images from the same launch (q NULL: none)
+  const void* B_k;      // [Hkv][RK][D]
+  const float* q;       // [B][Hq][D]
+  float* q_proj;        // [B][Hq][width]
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 

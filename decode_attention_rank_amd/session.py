@@ -2,8 +2,8 @@
 
 A DecodeSession owns the paged cache, the factors, the per-step inputs and
 outputs and the workspace for one workload on one GPU, and runs the step as
-the library's five calls in order:
-  append_encode -> project_queries -> route_pages (routed only)
+the library's calls in order:
+  append_encode + project_queries (one launch) -> route_pages (routed only)
   -> decode_attn -> upproject.
 It stages seeded synthetic inputs (from `synth`) into device memory; every
 step of the method itself runs in the HIP kernels.
@@ -205,12 +205,19 @@ class DecodeSession:
     def upproject(self, stream=None):
         K.kvlr_upproject(self.shape, self.kfactors, self.z, self.o, self.wl.batch, stream)
 
+    def append_and_project(self, stream=None):
+        K.kvlr_append_encode_project(self.shape, self.kfactors, self.kcache, self.k_new, self.v_new,
+                                     self.cu_new, self.lens_before_dev, self.page_table,
+                                     self.max_pages, self.wl.batch, self.total_new, self.q,
+                                     self.q_proj, stream)
+
     def prepare(self, stream=None):
-        """Append-encode and query projection of one step (one stream: a second
-        stream joined by events costs more than the projection it would hide)."""
-        self.append(stream)
+        """Append-encode and query projection of one step, in one launch where
+        both are needed (they are independent)."""
         if self.needs_qproj:
-            self.project_queries(stream)
+            self.append_and_project(stream)
+        else:
+            self.append(stream)
 
     def attend_upproject(self, stream=None):
         """Attention with the up-projection applied in the same launch."""

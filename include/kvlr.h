@@ -183,6 +183,23 @@ kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* fa
 int32_t kvlr_qproj_width(const kvlr_shape* shape);
 
 /*
+ * kvlr_append_encode and kvlr_project_queries of one decode step, in one
+ * launch. The two are independent (the new tokens' latents and the query
+ * images), so the projection's tiles run beside the encode's workgroups
+ * instead of in a launch of their own.
+ * Arguments as for the two calls; q and q_proj are required, the append's
+ * buffers only when total_new > 0 (total_new = 0 runs the projection alone).
+ * The outputs are exactly those of the two calls: the same kernels' code
+ * computes them. A shape the encode does not support fails as it does there.
+ */
+kvlr_status kvlr_append_encode_project(const kvlr_shape* shape, const kvlr_factors* factors,
+                                       const kvlr_cache* cache, const void* k_new,
+                                       const void* v_new, const int32_t* cu_new,
+                                       const int32_t* seq_lens_before, const int32_t* page_table,
+                                       int32_t max_pages_per_seq, int32_t batch, int32_t total_new,
+                                       const float* q, float* q_proj, void* stream);
+
+/*
  * Page routing (KVLR_KEYS_EXACT only). BasisKV English abstract: the value
  * latent's key prediction plus the key-specific residual rank the key pages,
  * and only the chosen pages are read exactly.

@@ -97,6 +97,9 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None, None,
                                   None, None, None, 512, 16, 16, None) == E
     assert lib.kvlr_project_queries(ctypes.byref(s), ctypes.byref(f), None, None, 16, None) == E
+    assert lib.kvlr_append_encode_project(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None,
+                                          None, None, None, None, 512, 16, 16, None, None,
+                                          None) == E
     # k_max below the routing bound, or above max pages
     fake = 1 << 20  # aligned non-null placeholder; never dereferenced on these paths
     c2 = K.make_cache(fake, fake, fake)
@@ -158,6 +161,8 @@ def test_empty_batches_are_no_ops(lib):
     assert lib.kvlr_project_queries(ctypes.byref(s), ctypes.byref(f), None, None, 0, None) == 0
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None, None,
                                   None, None, None, 512, 16, 0, None) == 0
+    assert lib.kvlr_append_encode_project(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None,
+                                          None, None, None, None, 512, 0, 0, None, None, None) == 0
     assert lib.kvlr_workspace_init(None, 0, None) == 0
 
 

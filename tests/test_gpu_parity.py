@@ -225,6 +225,40 @@ def test_step_is_deterministic():
         assert torch.equal(getattr(s, n), t), n
 
 
+FUSED_CASES = [
+    dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True),
+    dict(G=8, d=128, rv=32, rk=32, P=64, storage="bf16", routed=True, latent="fp8"),
+    dict(G=2, d=64, rv=32, rk=16, P=16, storage="f32", routed=True),
+    dict(G=4, d=64, rv=32, rk=32, P=16, storage="bf16", routed=False, exact=False),
+]
+
+
+@pytest.mark.parametrize("kw", FUSED_CASES, ids=["bf16-routed", "fp8-G8", "f32-P16", "latent-keys"])
+def test_append_and_projection_in_one_launch(kw):
+    """kvlr_append_encode_project gives exactly the two separate calls'
+    outputs (cache pages and query images), and with no new tokens the
+    projection alone."""
+    wl = make_wl(**kw)
+    _say("case append+project", wl.name)
+    lens = [300, 1000, 77, 129]
+    one = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=70)
+    two = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=70)
+    one.append()
+    one.project_queries()
+    two.append_and_project()
+    torch.cuda.synchronize()
+    assert torch.equal(one.v_lat, two.v_lat)
+    assert torch.equal(one.k_lat, two.k_lat)
+    if wl.exact:
+        assert torch.equal(one.k_exact, two.k_exact)
+    assert torch.equal(one.q_proj, two.q_proj)
+    two.q_proj.fill_(float("nan"))
+    K.kvlr_append_encode_project(two.shape, two.kfactors, two.kcache, None, None, None, None,
+                                 two.page_table, two.max_pages, wl.batch, 0, two.q, two.q_proj)
+    torch.cuda.synchronize()
+    assert torch.equal(one.q_proj, two.q_proj)
+
+
 @pytest.mark.parametrize("routed", [True, False])
 def test_chunked_append_equals_one_shot(routed):
     wl = make_wl(G=4, d=128, rv=64, rk=32 if routed else 64, P=64, storage="bf16", routed=routed)
