@@ -13,7 +13,8 @@
  * Conventions shared by every entry point
  *   - Every pointer argument is a device pointer unless marked "host".
  *     The caller owns every buffer; the library allocates no device memory
- *     and keeps no mutable global state. Calls are thread-safe.
+ *     and keeps no mutable global state (only the text of each calling
+ *     thread's last HIP error, kept per thread). Calls are thread-safe.
  *   - Each call validates its arguments on the host, then enqueues its
  *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
  *     returns without synchronising. Outputs are valid once the stream has
@@ -299,7 +300,8 @@ size_t kvlr_workspace_bytes(const kvlr_shape* shape, int32_t batch, int32_t max_
 /* Zero-fills a workspace with a kernel (no memset node), once after allocation. */
 kvlr_status kvlr_workspace_init(void* workspace, size_t ws_bytes, void* stream);
 
-/* Static text for a status; the last HIP error text for KVLR_ERR_HIP. */
+/* Static text for a status; for KVLR_ERR_HIP, the text of the calling
+ * thread's last HIP error (valid until that thread's next failing call). */
 const char* kvlr_status_string(kvlr_status status);
 
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
