@@ -401,25 +401,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       const int ckg = ADAPT ? kl.ck[g] : CK;
       const size_t kpage = ADAPT ? static_cast<size_t>(kl.page_chunks) * P * S::CB : Hkv * slab_k;
       const size_t koff = ADAPT ? static_cast<size_t>(kl.off[g]) * P * S::CB : g * slab_k;
-      bf16x8 qhi[KS], qlo[KS];
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bool on_v = st < KSV;
-        const int ci = 4 * (on_v ? st : st - KSV) + kq;  // chunk within the slab
-        const bool have = col < G && ci < (on_v ? CV : ckg);
-        const float* src = qp + col * W + (on_v ? 0 : RV) + ci * 8;
-        float x[8];
-        if (have) {
-          const float4 a = *reinterpret_cast<const float4*>(src);
-          const float4 c = *reinterpret_cast<const float4*>(src + 4);
-          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-          x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
-        split_bf16x8(x, qhi[st], qlo[st]);
-      }
       // Past the slab's last chunk a lane re-reads chunk 0 (its query half is
       // zero); past the last row every lane reads one shared address.
       struct RowRef {
@@ -453,6 +434,26 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         for (int st = 0; st < KS; ++st)
           if (step_on(st)) A[p][st] = load16_stream(a_addr(cur, p, st));
       RowRef nxt = row_ref(r + kWaves);
+      // the query fragments are formed while the first row is in flight
+      bf16x8 qhi[KS], qlo[KS];
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const bool on_v = st < KSV;
+        const int ci = 4 * (on_v ? st : st - KSV) + kq;  // chunk within the slab
+        const bool have = col < G && ci < (on_v ? CV : ckg);
+        const float* src = qp + col * W + (on_v ? 0 : RV) + ci * 8;
+        float x[8];
+        if (have) {
+          const float4 a = *reinterpret_cast<const float4*>(src);
+          const float4 c = *reinterpret_cast<const float4*>(src + 4);
+          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+          x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        split_bf16x8(x, qhi[st], qlo[st]);
+      }
       for (; r < row1; r += kWaves) {
         const RowRef nn = row_ref(r + 2 * kWaves);  // page-table entry two rows ahead
         f32x4 acc[4];
