@@ -68,12 +68,27 @@ struct F32 {
   }
 };
 
+// Two E4M3 codes (bytes 0,1 of w, or bytes 2,3 with HI) to two bf16 in one
+// instruction, with scale 1 (exact: every E4M3 value is a bf16). Written as
+// assembly because the compiler's builtin for it is followed by a permute
+// that copies the first element into both halves; checked on all 256 codes
+// in each byte position against the float32 decode.
+template <bool HI>
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  uint32_t r;
+  if (HI)
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+  else
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  return r;
+}
+
 // OCP 8-bit floating point E4M3 (4 exponent bits, bias 7, 3 stored
 // significand bits, no infinities, largest finite value 448): latents only.
 // Every E4M3 value is exact in bfloat16 and float32, so decoding is exact:
 // v_cvt_pk_f32_fp8 decodes all 256 codes as OCP E4M3 on gfx950 (two per
-// instruction, bytes 0,1 or 2,3 of a word), and a bf16 operand is the upper
-// half of each float.
+// instruction, bytes 0,1 or 2,3 of a word); matrix-core operands take the
+// codes to bf16 directly, two per instruction.
 struct FP8 {
   static constexpr int CH = 8;
   static constexpr int ELEM_BYTES = 1;
@@ -95,13 +110,8 @@ struct FP8 {
   }
   // bytes 0..7 -> bf16 elements 0..7
   __device__ static inline bf16x8 to_bf16x8(const Raw& r) {
-    float x[CH];
-    unpack(r, x);
-    uint32_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      h[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
-    return __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    return __builtin_bit_cast(bf16x8, make_uint4(fp8x2_to_bf16x2<false>(r.x), fp8x2_to_bf16x2<true>(r.x),
+                                                 fp8x2_to_bf16x2<false>(r.y), fp8x2_to_bf16x2<true>(r.y)));
   }
   // 16 loaded bytes hold two tokens' chunks: fragment h of token h
   __device__ static inline bf16x8 frag_of16(const uint4& r, int h) {
