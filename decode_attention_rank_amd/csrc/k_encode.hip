@@ -119,19 +119,32 @@ struct EncSmem {
   alignas(16) E mhi[ROUTED ? KSV : 1][RK / 16][kWave][KPL];
   alignas(16) E mlo[(ROUTED && KPL > 1) ? KSV : 1][RK / 16][kWave][KPL];
   struct Tiles {
-    // per-wave row-major tiles of the rounded latents (16 tokens)
+    // per-wave row-major tiles of the rounded latents (16 tokens each; read
+    // across the waves as one 64-token tile)
     alignas(16) LE vt[kWaves][16][RV + CH];
     alignas(16) LE ct[kWaves][16][RK + CH];
   };
+  // bf16: the tile's original keys, one 16-byte chunk per entry (64 tokens;
+  // one spare entry per row keeps rows on rotating banks)
+  static constexpr int KT_COLS = (KPL == CH) ? D / CH + 1 : 1;
   union {
     float mstage[ROUTED ? RV : 1][RK + 1];  // set-up only
     Tiles t;
+    uint4 kt[(KPL == CH) ? 64 : 1][KT_COLS];
   } u;
+  int tok_page[64];  // physical page of each token of the tile, -1 past the end
+  int tok_slot[64];  // its slot in the page
 };
 
 __device__ inline void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Workgroup barrier for LDS hand-offs only: global stores already issued
+// stay in flight across it.
+__device__ inline void block_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Query-projection tiles carried by the same launch (kvlr_append_encode_project):
@@ -156,6 +169,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   using SM = EncSmem<S, LS, D, RV, RK, ROUTED>;
   using LT = Lat<S, LS>;
   using E = typename MM::E;
+  using LE = typename LT::E;
   using frag_t = typename MM::frag_t;
   constexpr int KSTEP = MM::KSTEP, KPL = MM::KPL, CH = S::CH, EB = S::ELEM_BYTES;
   constexpr int KSD = SM::KSD, KSV = SM::KSV;
@@ -307,29 +321,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     __syncthreads();
   }
 
-  // one tile: multiply, round, store (latents via the wave's LDS tile)
-  auto process = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
-                     size_t slot_off) {
-    const int i = tile * 64 + wave * 16 + r;
-    const bool valid = i < total_new;
-    // original key: stored straight from the loaded fragments
-    if constexpr (ROUTED) {
-      if (valid) {
-        uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off * 16;
-        if constexpr (FRAG_IS_CHUNK) {
-          // fragment ks of this lane is chunk ks * KSTEP / CH + kq of the key row
-#pragma unroll
-          for (int ks = 0; ks < KSD; ++ks)
-            store16(kd + static_cast<size_t>(ks * (KSTEP / CH) + kq) * P * 16,
-                    __builtin_bit_cast(uint4, kf[ks]));
-        } else {
-          const size_t row_off = (static_cast<size_t>(i) * Hkv + g) * D * EB;
-          for (int c = kq; c < CD; c += 4)
-            store16(kd + static_cast<size_t>(c) * P * 16, load16(k_new + row_off + c * 16));
-        }
-      }
-    }
-    // ---- v = V A_v
+  // v = V A_v and the residual (routed) or key latent (dense), rounded into
+  // the wave's rows of the LDS tiles; `after_v` runs once the v rows are
+  // written (the routed residual reads them back)
+  auto products = [&](const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], auto after_v) {
     f32x4 vacc[NTV];
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) vacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -341,8 +336,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.u.t.vt[wave][4 * kq + j][nt * 16 + r] = LT::round(vacc[nt][j]);
-
-    // ---- residual latent (routed) or key latent (dense)
     f32x4 cacc[NTK];
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt) cacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -351,14 +344,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
       for (int nt = 0; nt < NTK; ++nt) cacc[nt] = MM::mma(kf[ks], MM::lds(&sm.ak[ks][nt][lane][0]), cacc[nt]);
     wave_lds_sync();
-    if (valid) {
-      uint8_t* dst = v_lat + (phys * Hkv + g) * CV * P * LT::CB + slot_off * LT::CB;
-#pragma unroll
-      for (int c0 = 0; c0 < CV; c0 += 4) {
-        const int c = c0 + kq;
-        if (c < CV) LT::store_chunk(dst + static_cast<size_t>(c) * P * LT::CB, &sm.u.t.vt[wave][r][c * CH]);
-      }
-    }
+    after_v();
     if constexpr (ROUTED) {
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks) {
@@ -376,13 +362,87 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.u.t.ct[wave][4 * kq + j][nt * 16 + r] = LT::round(cacc[nt][j]);
     wave_lds_sync();
+  };
+  // per-head residual ranks: head g keeps its first ckg chunks, at its own
+  // offset in the page
+  const int ckg = kl.adaptive ? kl.ck[g] : CK;
+  const size_t kpage = kl.adaptive ? static_cast<size_t>(kl.page_chunks) : static_cast<size_t>(Hkv) * CK;
+  const size_t koff = kl.adaptive ? static_cast<size_t>(kl.off[g]) : static_cast<size_t>(g) * CK;
+
+  // one tile, bf16 storage: the workgroup gathers the tile's 64 tokens in
+  // LDS, then each wave writes whole chunk columns of the pages (a column is
+  // P consecutive slots, so a store instruction covers up to 64 slots: 1 KB
+  // of bf16, 512 bytes of FP8), taking every fourth column
+  auto process_cols = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+                          size_t slot_off) {
+    const int i = tile * 64 + wave * 16 + r;
+    const bool valid = i < total_new;
+    const int t_own = wave * 16 + r;  // this lane's token within the tile
+    if (kq == 0) {
+      sm.tok_page[t_own] = valid ? static_cast<int>(phys) : -1;
+      sm.tok_slot[t_own] = static_cast<int>(slot_off);
+    }
+    if constexpr (ROUTED && FRAG_IS_CHUNK) {
+      // fragment ks of this lane is chunk ks * KSTEP / CH + kq of the key row
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+        sm.u.kt[t_own][ks * (KSTEP / CH) + kq] = __builtin_bit_cast(uint4, kf[ks]);
+    }
+    block_lds_sync();
+    const int pg = sm.tok_page[lane];  // lane = token of the tile from here on
+    const size_t slot = static_cast<size_t>(sm.tok_slot[lane]);
+    if constexpr (ROUTED && FRAG_IS_CHUNK) {
+      constexpr int NCOL = CD / kWaves;  // key chunk columns per wave
+      static_assert(CD % kWaves == 0, "key chunk columns split evenly over the waves");
+      if (pg >= 0) {
+        uint8_t* kd = k_exact + (static_cast<size_t>(pg) * Hkv + g) * CD * P * 16 + slot * 16;
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j)
+          store16(kd + static_cast<size_t>(wave + j * kWaves) * P * 16, sm.u.kt[lane][wave + j * kWaves]);
+      }
+      block_lds_sync();  // the latent tiles overwrite kt
+    }
+    products(vf, kf, [] {});
+    block_lds_sync();
+    if (pg >= 0) {
+      const LE* vrow = &sm.u.t.vt[0][0][0] + lane * (RV + CH);
+      const LE* crow = &sm.u.t.ct[0][0][0] + lane * (RK + CH);
+      uint8_t* vd = v_lat + (static_cast<size_t>(pg) * Hkv + g) * CV * P * LT::CB + slot * LT::CB;
+      uint8_t* cd = k_lat + (static_cast<size_t>(pg) * kpage + koff) * P * LT::CB + slot * LT::CB;
+#pragma unroll
+      for (int c = wave; c < CV; c += kWaves) LT::store_chunk(vd + static_cast<size_t>(c) * P * LT::CB, vrow + c * CH);
+#pragma unroll
+      for (int c = wave; c < CK; c += kWaves)
+        if (c < ckg) LT::store_chunk(cd + static_cast<size_t>(c) * P * LT::CB, crow + c * CH);
+    }
+    block_lds_sync();  // the next tile rewrites the tiles and locations
+  };
+
+  // one tile, f32 storage: each wave stores its 16 tokens' chunks
+  auto process_rows = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+                          size_t slot_off) {
+    const int i = tile * 64 + wave * 16 + r;
+    const bool valid = i < total_new;
+    if constexpr (ROUTED) {
+      if (valid) {
+        uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off * 16;
+        const size_t row_off = (static_cast<size_t>(i) * Hkv + g) * D * EB;
+        for (int c = kq; c < CD; c += 4)
+          store16(kd + static_cast<size_t>(c) * P * 16, load16(k_new + row_off + c * 16));
+      }
+    }
+    products(vf, kf, [&] {
+      if (valid) {
+        uint8_t* dst = v_lat + (phys * Hkv + g) * CV * P * LT::CB + slot_off * LT::CB;
+#pragma unroll
+        for (int c0 = 0; c0 < CV; c0 += 4) {
+          const int c = c0 + kq;
+          if (c < CV) LT::store_chunk(dst + static_cast<size_t>(c) * P * LT::CB, &sm.u.t.vt[wave][r][c * CH]);
+        }
+      }
+    });
     if (valid) {
-      // per-head residual ranks: this head keeps its first ckg chunks, at its
-      // own offset in the page
-      const int ckg = kl.adaptive ? kl.ck[g] : CK;
-      const size_t page_chunks = kl.adaptive ? static_cast<size_t>(kl.page_chunks) : static_cast<size_t>(Hkv) * CK;
-      const size_t koff = kl.adaptive ? static_cast<size_t>(kl.off[g]) : static_cast<size_t>(g) * CK;
-      uint8_t* dst = k_lat + (phys * page_chunks + koff) * P * LT::CB + slot_off * LT::CB;
+      uint8_t* dst = k_lat + (phys * kpage + koff) * P * LT::CB + slot_off * LT::CB;
 #pragma unroll
       for (int c0 = 0; c0 < CK; c0 += 4) {
         const int c = c0 + kq;
@@ -390,6 +450,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       }
     }
     wave_lds_sync();
+  };
+  auto process = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+                     size_t slot_off) {
+    if constexpr (FRAG_IS_CHUNK) process_cols(tile, vf, kf, phys, slot_off);
+    else process_rows(tile, vf, kf, phys, slot_off);
   };
 
   for (int tile = tile0; tile < ntiles; tile += tile_step) {
