@@ -19,8 +19,11 @@
 // Work split: grid (KV head, token-tile groups). A workgroup stages the
 // factor fragments of its head in LDS once, then loops over 64-token tiles,
 // 16 tokens per wave: the wave loads its tokens' rows straight into MFMA
-// A-operand registers, multiplies, rounds into a per-wave LDS tile and writes
-// each token's chunks to its page slot. With FP8 latents (bf16 inputs and
+// A-operand registers, multiplies and rounds into its rows of the LDS tiles.
+// With bf16 inputs the whole tile is then written column by column (each
+// wave takes every fourth chunk column of the pages, one token per lane, so
+// a store covers up to 64 consecutive slots); with f32 inputs each wave
+// writes its own tokens' chunks. With FP8 latents (bf16 inputs and
 // factors) the latents are rounded once from the float32 products to E4M3
 // (nearest even, saturating at +-448) and stored as 8-byte chunks; the
 // residual is taken against that stored latent, decoded exactly to bf16.
