@@ -128,13 +128,14 @@ struct EncSmem {
     alignas(16) LE ct[kWaves][16][RK + CH];
   };
   // bf16: the tile's original keys, one 16-byte chunk per entry (64 tokens;
-  // one spare entry per row keeps rows on rotating banks)
+  // one spare entry per row keeps rows on rotating banks). Kept apart from
+  // the latent tiles, so all of a tile's stores go out as one batch.
   static constexpr int KT_COLS = (KPL == CH) ? D / CH + 1 : 1;
   union {
     float mstage[ROUTED ? RV : 1][RK + 1];  // set-up only
     Tiles t;
-    uint4 kt[(KPL == CH) ? 64 : 1][KT_COLS];
   } u;
+  uint4 kt[(KPL == CH && ROUTED) ? 64 : 1][KT_COLS];
   int tok_page[64];  // physical page of each token of the tile, -1 past the end
   int tok_slot[64];  // its slot in the page
 };
@@ -375,7 +376,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   // one tile, bf16 storage: the workgroup gathers the tile's 64 tokens in
   // LDS, then each wave writes whole chunk columns of the pages (a column is
   // P consecutive slots, so a store instruction covers up to 64 slots: 1 KB
-  // of bf16, 512 bytes of FP8), taking every fourth column
+  // of bf16, 512 bytes of FP8), taking every fourth column. The original
+  // keys and the latents go out together after the products: the in-order
+  // memory counter then waits for a tile's stores once, not per phase.
   auto process_cols = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
                           size_t slot_off) {
     const int i = tile * 64 + wave * 16 + r;
@@ -389,11 +392,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       // fragment ks of this lane is chunk ks * KSTEP / CH + kq of the key row
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks)
-        sm.u.kt[t_own][ks * (KSTEP / CH) + kq] = __builtin_bit_cast(uint4, kf[ks]);
+        sm.kt[t_own][ks * (KSTEP / CH) + kq] = __builtin_bit_cast(uint4, kf[ks]);
     }
     block_lds_sync();
     const int pg = sm.tok_page[lane];  // lane = token of the tile from here on
     const size_t slot = static_cast<size_t>(sm.tok_slot[lane]);
+    products(vf, kf, [] {});
+    block_lds_sync();
     if constexpr (ROUTED && FRAG_IS_CHUNK) {
       constexpr int NCOL = CD / kWaves;  // key chunk columns per wave
       static_assert(CD % kWaves == 0, "key chunk columns split evenly over the waves");
@@ -401,12 +406,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
         uint8_t* kd = k_exact + (static_cast<size_t>(pg) * Hkv + g) * CD * P * 16 + slot * 16;
 #pragma unroll
         for (int j = 0; j < NCOL; ++j)
-          store16(kd + static_cast<size_t>(wave + j * kWaves) * P * 16, sm.u.kt[lane][wave + j * kWaves]);
+          store16(kd + static_cast<size_t>(wave + j * kWaves) * P * 16, sm.kt[lane][wave + j * kWaves]);
       }
-      block_lds_sync();  // the latent tiles overwrite kt
     }
-    products(vf, kf, [] {});
-    block_lds_sync();
     if (pg >= 0) {
       const LE* vrow = &sm.u.t.vt[0][0][0] + lane * (RV + CH);
       const LE* crow = &sm.u.t.ct[0][0][0] + lane * (RK + CH);
