@@ -36,7 +36,7 @@
 #include "kvlr_internal.h"
 
 #ifndef KVLR_ENCODE_WGS
-#define KVLR_ENCODE_WGS 3072  // workgroups over all KV heads (each loops over tiles)
+#define KVLR_ENCODE_WGS 0  // workgroups over all KV heads; 0: as many as stay resident at once
 #endif
 
 namespace kvlr {
@@ -477,7 +477,22 @@ template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   const int ntiles = (a.total_new + 63) / 64;
-  int per_head = (KVLR_ENCODE_WGS + a.dm.Hkv - 1) / a.dm.Hkv;
+  const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
+  // A persistent grid: the workgroups that fit on the device at once, each
+  // looping over tiles (a second, partial round of workgroups left most of
+  // the device idle behind it, and fewer, longer-lived workgroups stage the
+  // factors fewer times).
+  int wgs = KVLR_ENCODE_WGS;
+  if (wgs <= 0) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_kernel<S, LS, D, RV, RK, ROUTED>,
+                                                     kThreads, lds) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipGetLastError();
+    wgs = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  }
+  int per_head = (wgs + a.dm.Hkv - 1) / a.dm.Hkv;
   if (per_head > ntiles) per_head = ntiles;
   QTiles qt{};
   if (a.q) {
@@ -494,7 +509,6 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   }
   if (per_head + qt.qy == 0) return hipSuccess;
   dim3 grid(a.dm.Hkv, per_head + qt.qy);
-  const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
   hipLaunchKernelGGL((encode_kernel<S, LS, D, RV, RK, ROUTED>), grid, dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(a.A_v), static_cast<const uint8_t*>(a.A_k),
                      static_cast<const uint8_t*>(a.W_pred), static_cast<const uint8_t*>(a.k_new),
