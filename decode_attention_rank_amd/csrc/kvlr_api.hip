@@ -67,7 +67,10 @@ constexpr int kMaxBatch = 4096;          // per-sequence offsets and work lists 
 #define KVLR_ROUTE_GRID 2048
 #endif
 constexpr long long kPersistentGrid = KVLR_ROUTE_GRID;  // about 8 workgroups per CU
-constexpr long long kAttnGrid = 1024;        // attention holds more registers per wave
+#ifndef KVLR_ATTN_GRID
+#define KVLR_ATTN_GRID 1024
+#endif
+constexpr long long kAttnGrid = KVLR_ATTN_GRID;        // attention holds more registers per wave
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
