@@ -186,6 +186,27 @@ def test_empty_sequence_in_batch():
     assert (sess.z[0] == 0).all() and (sess.o[0] == 0).all()
 
 
+def test_maximum_batch():
+    """The largest batch the boundary accepts (4096 sequences: per-sequence
+    offsets and work lists live in LDS), with short ragged contexts, empty
+    ones included. Every pair's page count is checked against its closed
+    form; sampled pairs, the first and the last against the oracle."""
+    B = 4096
+    wl = make_wl(G=1, d=64, rv=16, rk=16, P=16, storage="bf16", routed=True, B=B, Hkv=1,
+                 topk=(1, 4))
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(0, 120, size=B)]
+    lens[0], lens[-1] = 119, 0
+    _say("case maximum batch", B)
+    sess = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=1)
+    pairs = [(b, 0) for b in sorted({0, 1, B - 2, *rng.choice(B, 40, replace=False).tolist()})]
+    run_and_check(sess, pairs=pairs)
+    N = -(-np.array(lens) // 16)
+    k = np.where(N > 0, np.minimum(N, np.maximum(1, -(-N // 4))), 0)
+    assert (sess.sel_counts.cpu().numpy().reshape(B) == k).all()
+    assert (sess.sel[B - 1].cpu() == -1).all()
+
+
 def test_nan_in_unused_slots_and_pages_is_ignored():
     wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
     _say("case NaN tails")
