@@ -77,11 +77,11 @@ _SIG = {
     "kvlr_project_queries": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_qproj_width": ([ctypes.POINTER(kvlr_shape)], _I),
     "kvlr_route_pages": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _I, _I,
-                          _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
+                          _I, _P, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_decode_attn": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I,
-                          _P, _P, _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
+                          _P, _P, _P, _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_decode_attn_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
-                                    ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _I,
+                                    ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _P, _I,
                                     ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I, _I], ctypes.c_size_t),
@@ -215,32 +215,34 @@ def kvlr_project_queries(shape, factors, q, q_proj, batch, stream=None):
 
 
 def kvlr_route_pages(shape, cache, q_proj, seq_lens, page_table, max_pages_per_seq, topk_num,
-                     topk_den, k_max, sel_pages, sel_counts, page_scores, workspace, ws_bytes,
-                     batch, stream=None):
+                     topk_den, k_pages, k_max, sel_pages, sel_counts, sel_phys, page_scores,
+                     workspace, ws_bytes, batch, stream=None):
     _check("kvlr_route_pages", lib().kvlr_route_pages(
         ctypes.byref(shape), ctypes.byref(cache), _ptr(q_proj), _ptr(seq_lens), _ptr(page_table),
-        max_pages_per_seq, topk_num, topk_den, k_max, _ptr(sel_pages), _ptr(sel_counts),
-        _ptr(page_scores), _ptr(workspace), ws_bytes, batch, _stream(stream)))
+        max_pages_per_seq, topk_num, topk_den, _ptr(k_pages), k_max, _ptr(sel_pages),
+        _ptr(sel_counts), _ptr(sel_phys), _ptr(page_scores), _ptr(workspace), ws_bytes, batch,
+        _stream(stream)))
 
 
 def kvlr_decode_attn(shape, cache, q, q_proj, seq_lens, page_table, max_pages_per_seq, sel_pages,
-                     sel_counts, k_max, softmax_scale, z_out, lse_out, workspace, ws_bytes, batch,
-                     stream=None):
+                     sel_phys, sel_counts, k_max, softmax_scale, z_out, lse_out, workspace,
+                     ws_bytes, batch, stream=None):
     _check("kvlr_decode_attn", lib().kvlr_decode_attn(
         ctypes.byref(shape), ctypes.byref(cache), _ptr(q), _ptr(q_proj), _ptr(seq_lens),
-        _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_counts), k_max,
-        float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(workspace), ws_bytes, batch,
+        _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_phys), _ptr(sel_counts),
+        k_max, float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(workspace), ws_bytes, batch,
         _stream(stream)))
 
 
 def kvlr_decode_attn_upproject(shape, factors, cache, q, q_proj, seq_lens, page_table,
-                               max_pages_per_seq, sel_pages, sel_counts, k_max, softmax_scale,
-                               z_out, lse_out, o_out, workspace, ws_bytes, batch, stream=None):
+                               max_pages_per_seq, sel_pages, sel_phys, sel_counts, k_max,
+                               softmax_scale, z_out, lse_out, o_out, workspace, ws_bytes, batch,
+                               stream=None):
     _check("kvlr_decode_attn_upproject", lib().kvlr_decode_attn_upproject(
         ctypes.byref(shape), ctypes.byref(factors), ctypes.byref(cache), _ptr(q), _ptr(q_proj),
-        _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_counts),
-        k_max, float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(o_out), _ptr(workspace),
-        ws_bytes, batch, _stream(stream)))
+        _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_phys),
+        _ptr(sel_counts), k_max, float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(o_out),
+        _ptr(workspace), ws_bytes, batch, _stream(stream)))
 
 
 def kvlr_upproject(shape, factors, z, o_out, batch, stream=None):

@@ -21,8 +21,16 @@
 // With one page per row (page_size 64) every key and value register is
 // re-requested with the wave's next row as soon as it has been used, so each
 // wave keeps a row in flight.
-// Waves and workgroups then merge their (max, sum, z) partials; the last
-// workgroup of a pair (atomic ticket) merges the chunks into z and lse.
+// The waves of a workgroup merge their (max, sum, z) partials in LDS and the
+// workgroup writes one partial record per chunk; merge_kernel (a second
+// launch) combines a pair's chunk records into z and lse, and with B_v given
+// applies the up-projection o_h = z_h B_v there, once per query head.
+//
+// Chunk plan: with page ids and no per-pair counts, every pair walks k_max
+// rows (ids of -1 are skipped), so a chunk's pair and split follow from its
+// index alone and nothing is read before the chunk's own page ids; with
+// counts (ragged batches) or without page ids (every page), each workgroup
+// first builds the per-sequence prefix of chunk counts in LDS.
 
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
@@ -49,6 +57,17 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Chunks of one pair when chunk counts come from the per-sequence plan: the
+// most items (pages) over the sequence's KV heads, in rows of 64 tokens,
+// split into runs of rows_per_chunk rows (at least one chunk).
+template <class ItemsFn>
+__device__ inline int attn_splits(ItemsFn items_of, int b, int Hkv, int ipr_log2, int rpc) {
+  int items = 0;
+  for (int g = 0; g < Hkv; ++g) items = max(items, items_of(b, g));
+  const int rows = (items + (1 << ipr_log2) - 1) >> ipr_log2;
+  return max(1, (rows + rpc - 1) / rpc);
+}
+
 // S: storage of the keys the scores read (original keys, or key latents);
 // SV: storage of the value latents. With FP8 latents S is BF16 (original
 // keys) or FP8 (key latents), SV is FP8, and the factors are bf16.
@@ -57,14 +76,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint8_t* __restrict__ keys, const uint8_t* __restrict__ v_lat,
     const float* __restrict__ qsrc, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_counts, float* __restrict__ partials,
-    uint32_t* __restrict__ counters, float* __restrict__ z_out, float* __restrict__ lse_out,
-    const uint8_t* __restrict__ B_v, float* __restrict__ o_out, int Dh, int Hq, int Hkv, int P,
-    int log2P, int max_pages, int k_max,
+    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_counts,
+    float* __restrict__ partials, int Hq, int Hkv, int P, int log2P, int max_pages, int k_max,
     float scale_log2e, int rows_per_chunk, int max_splits, int batch) {
   constexpr int CH = S::CH;
   static_assert(SV::CH == CH, "keys and value latents share the elements per chunk");
-  using SF = std::conditional_t<S::CB == 8, BF16, S>;  // factor storage
   constexpr int CKW = KW / CH;     // key chunks per token
   constexpr int CV = RV / CH;      // value-latent chunks per token
   constexpr int TPL = kWave / CV;  // token stride between a lane's P.V tokens
@@ -74,7 +90,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ float s_p[kWaves][kWave][G];
   __shared__ float s_ml[kWaves][G][2];
   __shared__ float s_z[kWaves][G][RV];
-  __shared__ int s_last;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
@@ -88,27 +103,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (!sel) return (seq_lens[b] + P - 1) >> log2P;
     return sel_counts ? min(max(sel_counts[b * Hkv + g], 0), k_max) : k_max;
   };
-  build_chunk_prefix(batch, s_base, [&](int b) {
-    int items = 0;
-    for (int g = 0; g < Hkv; ++g) items = max(items, items_of(b, g));
-    const int rows = (items + (1 << ipr_log2) - 1) >> ipr_log2;
-    return Hkv * max(1, (rows + rows_per_chunk - 1) / rows_per_chunk);
-  });
-  const int total = s_base[batch];
+  const bool uniform = sel && !sel_counts;  // every pair walks k_max rows in max_splits chunks
+  int total;
+  if (uniform) {
+    total = batch * Hkv * max_splits;
+  } else {
+    build_chunk_prefix(batch, s_base,
+                       [&](int b) { return Hkv * attn_splits(items_of, b, Hkv, ipr_log2, rows_per_chunk); });
+    total = s_base[batch];
+  }
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int b = find_sequence(s_base, batch, w);
+    int b, g, split, nsplit;
+    if (uniform) {
+      const int pr = w / max_splits;
+      split = w - pr * max_splits;
+      nsplit = max_splits;
+      b = pr / Hkv;
+      g = pr - b * Hkv;
+    } else {
+      b = find_sequence(s_base, batch, w);
+      nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
+      const int local = w - s_base[b];
+      g = local / nsplit;
+      split = local - g * nsplit;
+    }
     const int L = seq_lens[b];
     const int N = (L + P - 1) >> log2P;
-    const int nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
-    const int local = w - s_base[b];
-    const int g = local / nsplit;
-    const int split = local - g * nsplit;
     const int n_items = items_of(b, g);
     const int nrows = (n_items + (1 << ipr_log2) - 1) >> ipr_log2;
     const int pair = b * Hkv + g;
     const int32_t* __restrict__ pt = page_table + static_cast<size_t>(b) * max_pages;
     const int32_t* __restrict__ sl = sel ? sel + static_cast<size_t>(pair) * k_max : nullptr;
+    // physical pages of the selected ids (written by routing beside them), or
+    // the page table
+    const int32_t* __restrict__ sp = (sel && sel_phys) ? sel_phys + static_cast<size_t>(pair) * k_max : nullptr;
+    auto phys_of = [&](int row, int pg) -> size_t {
+      return static_cast<size_t>(sp ? sp[row] : pt[pg]);
+    };
     const float* __restrict__ qg = qsrc + static_cast<size_t>(b * Hq + g * G) * KW;
     const int row0 = split * rows_per_chunk;
     const int row1 = min(row0 + rows_per_chunk, nrows);
@@ -221,9 +253,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const uint8_t* vb;
         int on, nvalid;
       };
-      auto row_ref = [&](int pg) -> RowRef {
+      auto row_ref = [&](int row, int pg) -> RowRef {
         if (pg < 0) return RowRef{keys, v_lat, 0, 0};
-        const size_t ph = static_cast<size_t>(pt[pg]);
+        const size_t ph = phys_of(row, pg);
         return RowRef{keys + (ph * Hkv + g) * slab_k,
                       v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * SV::CB, 1,
                       min(L - pg * kWave, kWave)};
@@ -240,19 +272,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       int r = row0 + wave;
       typename S::Raw A[4][KS];
       typename SV::Raw vc[CV];
-      RowRef cur = row_ref(page_of(r));
+      RowRef cur = row_ref(r, page_of(r));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int st = 0; st < KS; ++st) A[j][st] = S::load_stream(a_addr(cur, j, st));
 #pragma unroll
       for (int k = 0; k < CV; ++k) vc[k] = SV::load_stream(v_addr(cur, k));
-      RowRef nxt = row_ref(page_of(r + kWaves));
+      RowRef nxt = row_ref(r + kWaves, page_of(r + kWaves));
       int pg2 = page_of(r + 2 * kWaves);
       float lcol = 0.f;  // sum of this lane's probabilities of head col
       for (; r < row1; r += kWaves) {
         // table lookups run ahead: physical page two rows on, page id three rows on
-        const RowRef nn = row_ref(pg2);
+        const RowRef nn = row_ref(r + 2 * kWaves, pg2);
         const int pg3 = page_of(r + 3 * kWaves);
         f32x4 acc[4];
 #pragma unroll
@@ -358,10 +390,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const uint8_t* vb;
         int kstride, vstride, nvalid;
       };
-      auto row_ref = [&](int pg) -> RowRef {
+      auto row_ref = [&](int row, int pg) -> RowRef {
         RowRef rr;
         if (pg >= 0) {
-          const size_t ph = static_cast<size_t>(pt[pg]);
+          const size_t ph = phys_of(row, pg);
           rr.kb = keys + (ph * Hkv + g) * slab_k + lane * 16;
           rr.vb = v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * 16;
           rr.kstride = kWave * 16;
@@ -378,16 +410,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       };
       int r = row0 + wave;
       uint4 kc[CKW], vc[CV];
-      RowRef cur = row_ref(page_of(r));
+      RowRef cur = row_ref(r, page_of(r));
 #pragma unroll
       for (int c = 0; c < CKW; ++c) kc[c] = load16_stream(cur.kb + c * cur.kstride);
 #pragma unroll
       for (int k = 0; k < CV; ++k) vc[k] = load16_stream(cur.vb + (lane / CV + k * TPL) * cur.vstride);
-      RowRef nxt = row_ref(page_of(r + kWaves));
+      RowRef nxt = row_ref(r + kWaves, page_of(r + kWaves));
       int pg2 = page_of(r + 2 * kWaves);
       for (; r < row1; r += kWaves) {
         // table lookups run ahead: physical page two rows on, page id three rows on
-        const RowRef nn = row_ref(pg2);
+        const RowRef nn = row_ref(r + 2 * kWaves, pg2);
         const int pg3 = page_of(r + 3 * kWaves);
         float s[G];
 #pragma unroll
@@ -428,7 +460,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         int page = -1;
         if (item < n_items) page = sl ? sl[item] : item;
         const bool valid = page >= 0 && page < N && (page << log2P) + slot < L;
-        const int phys = valid ? pt[page] : 0;
+        const int phys = valid ? static_cast<int>(phys_of(item, page)) : 0;
         uint4 kc[CKW];
         if (valid) {
           const uint8_t* kb = keys + (static_cast<size_t>(phys) * Hkv + g) * slab_k + slot * 16;
@@ -481,7 +513,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
 
-    // ---- chunk partial (max, sum, z) per head
+    // ---- chunk partial (max, sum, z) per head; merge_kernel combines them
     float* part = partials + (static_cast<size_t>(pair) * max_splits + split) * G * PW;
     for (int i = threadIdx.x; i < G * RV; i += kThreads) {
       const int h = i / RV, e = i - h * RV;
@@ -497,83 +529,88 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           Ls += f * s_ml[ww][h][1];
         }
       }
-      store_shared_f32(&part[h * PW + 2 + e], Z);
+      part[h * PW + 2 + e] = Z;
       if (e == 0) {
-        store_shared_f32(&part[h * PW], M);
-        store_shared_f32(&part[h * PW + 1], Ls);
+        part[h * PW] = M;
+        part[h * PW + 1] = Ls;
       }
     }
+    __syncthreads();
+  }
+}
 
-    // ---- ticket: the last chunk of the pair merges the splits
-    wait_stores_done();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t prev = take_ticket(&counters[pair]);
-      s_last = (prev == static_cast<uint32_t>(nsplit - 1));
-    }
-    __syncthreads();
-    if (s_last) {
-      const float* allp = partials + static_cast<size_t>(pair) * max_splits * G * PW;
-      for (int i = threadIdx.x; i < G * RV; i += kThreads) {
-        const int h = i / RV, e = i - h * RV;
-        // the splits' records are read eight at a time, every load in flight
-        // before the first is used (one at a time, each coherent load would
-        // wait out a full memory latency); indices past the last split
-        // re-read it: no effect on the max, skipped in the sums
-        float M = kNegInf;
-        for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
-          float mm[8];
+// Combines the chunk records of each (sequence, KV head) pair: with M the
+// largest chunk max (base-2 scaled scores), z = sum_c 2^(m_c - M) z_c /
+// sum_c 2^(m_c - M) l_c and lse = (M + log2 l) ln 2; no valid token gives
+// z = 0, lse = -inf. With B_v, o_h = z_h B_v[g] for the group's heads.
+// One workgroup per pair; the pair's chunk count follows the attention
+// launch's plan. Every load of a chunk record is issued before the first is
+// used; B_v is staged in LDS meanwhile.
+template <class SF, int G, int RV>
+__global__ __launch_bounds__(kThreads) void merge_kernel(
+    const float* __restrict__ partials, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_counts, int k_max,
+    int P, int log2P, int rows_per_chunk, int max_splits, int Hq, int Hkv, int Dh,
+    float* __restrict__ z_out, float* __restrict__ lse_out, const uint8_t* __restrict__ B_v,
+    float* __restrict__ o_out) {
+  constexpr int PW = RV + 2;
+  __shared__ float s_zz[G][RV];
+  __shared__ uint4 s_bv[RV * 128 * SF::ELEM_BYTES / 16];  // B_v[g] as stored, head_dim <= 128
+  const int pair = blockIdx.x;
+  const int b = pair / Hkv, g = pair - b * Hkv;
+  const int ipr_log2 = 6 - log2P;
+  auto items_of = [&](int bb, int gg) {
+    if (!sel) return (seq_lens[bb] + P - 1) >> log2P;
+    return sel_counts ? min(max(sel_counts[bb * Hkv + gg], 0), k_max) : k_max;
+  };
+  const int nsplit = (sel && !sel_counts) ? max_splits
+                                          : attn_splits(items_of, b, Hkv, ipr_log2, rows_per_chunk);
+  if (o_out) {
+    const uint8_t* Bg = B_v + static_cast<size_t>(g) * RV * Dh * SF::ELEM_BYTES;
+    for (int i = threadIdx.x; i < RV * Dh * SF::ELEM_BYTES / 16; i += kThreads) s_bv[i] = load16(Bg + i * 16);
+  }
+  const float* allp = partials + static_cast<size_t>(pair) * max_splits * G * PW;
+  for (int i = threadIdx.x; i < G * RV; i += kThreads) {
+    const int h = i / RV, e = i - h * RV;
+    float M = kNegInf, Z = 0.f, Ls = 0.f;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+      float mm[8], ll[8], zz[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            mm[u] = load_shared_f32(&allp[(min(sp0 + u, nsplit - 1) * G + h) * PW]);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) M = fmaxf(M, mm[u]);
-        }
-        float Z = 0.f, Ls = 0.f;
-        if (M != kNegInf) {
-          for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
-            float mm[8], ll[8], zz[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const float* r = allp + (min(sp0 + u, nsplit - 1) * G + h) * PW;
-              mm[u] = load_shared_f32(&r[0]);
-              ll[u] = load_shared_f32(&r[1]);
-              zz[u] = load_shared_f32(&r[2 + e]);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              if (sp0 + u < nsplit) {
-                const float f = fast_exp2(mm[u] - M);
-                Z += f * zz[u];
-                Ls += f * ll[u];
-              }
-            }
-          }
-        }
-        const int qh = g * G + h;
-        const float zv = (Ls > 0.f) ? Z / Ls : 0.f;
-        z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = zv;
-        s_z[0][h][e] = zv;
-        if (e == 0 && lse_out) {
-          lse_out[static_cast<size_t>(b) * Hq + qh] =
-              (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
-        }
+      for (int u = 0; u < 8; ++u) {  // past the last chunk: re-read it, skipped below
+        const float* r = allp + (min(sp0 + u, nsplit - 1) * G + h) * PW;
+        mm[u] = r[0];
+        ll[u] = r[1];
+        zz[u] = r[2 + e];
       }
-      if (o_out) {
-        // value compression tied to the output projection: o_h = z_h B_v, once per head
-        __syncthreads();
-        const uint8_t* Bg = B_v + static_cast<size_t>(g) * RV * Dh * SF::ELEM_BYTES;
-        for (int i = threadIdx.x; i < G * Dh; i += kThreads) {
-          const int h = i / Dh, d = i - h * Dh;
-          float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (sp0 + u >= nsplit || mm[u] == kNegInf) continue;
+        const float mn = fmaxf(M, mm[u]);
+        const float a = (M == kNegInf) ? 0.f : fast_exp2(M - mn);
+        const float f = fast_exp2(mm[u] - mn);
+        Z = Z * a + f * zz[u];
+        Ls = Ls * a + f * ll[u];
+        M = mn;
+      }
+    }
+    const int qh = g * G + h;
+    const float zv = (Ls > 0.f) ? Z / Ls : 0.f;
+    z_out[(static_cast<size_t>(b) * Hq + qh) * RV + e] = zv;
+    s_zz[h][e] = zv;
+    if (e == 0 && lse_out)
+      lse_out[static_cast<size_t>(b) * Hq + qh] =
+          (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
+  }
+  if (o_out) {
+    // value compression tied to the output projection: o_h = z_h B_v, once per head
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * Dh; i += kThreads) {
+      const int h = i / Dh, d = i - h * Dh;
+      float acc = 0.f;
 #pragma unroll 8
-          for (int e = 0; e < RV; ++e) acc = fmaf(s_z[0][h][e], SF::load1(Bg, static_cast<long>(e) * Dh + d), acc);
-          o_out[(static_cast<size_t>(b) * Hq + g * G + h) * Dh + d] = acc;
-        }
-      }
-      if (threadIdx.x == 0) reset_ticket(&counters[pair]);
+      for (int e = 0; e < RV; ++e) acc = fmaf(s_zz[h][e], SF::load1(s_bv, static_cast<long>(e) * Dh + d), acc);
+      o_out[(static_cast<size_t>(b) * Hq + g * G + h) * Dh + d] = acc;
     }
-    __syncthreads();
   }
 }
 
@@ -589,17 +626,22 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   if (a.dm.P == kWave)
     hipLaunchKernelGGL((attn_kernel<S, SV, G, KW, RV, true>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
-                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials,
-                       a.counters, a.z_out, a.lse_out, static_cast<const uint8_t*>(a.B_v), a.o_out,
-                       a.dm.D, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_phys, a.sel_counts,
+                       a.partials, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
                        a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
   else if constexpr (SV::CB == 16)
     hipLaunchKernelGGL((attn_kernel<S, SV, G, KW, RV, false>), grid, dim3(kThreads), lds, s,
                        static_cast<const uint8_t*>(a.keys), static_cast<const uint8_t*>(a.v_lat),
-                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.partials,
-                       a.counters, a.z_out, a.lse_out, static_cast<const uint8_t*>(a.B_v), a.o_out,
-                       a.dm.D, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
+                       a.qsrc, a.seq_lens, a.page_table, a.sel, a.sel_phys, a.sel_counts,
+                       a.partials, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.k_max,
                        a.scale_log2e, a.rows_per_chunk, a.max_splits, a.batch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  using SF = std::conditional_t<S::CB == 8, BF16, S>;  // factor storage
+  hipLaunchKernelGGL((merge_kernel<SF, G, RV>), dim3(a.batch * a.dm.Hkv), dim3(kThreads), 0, s,
+                     a.partials, a.seq_lens, a.sel, a.sel_counts, a.k_max, a.dm.P, log2P,
+                     a.rows_per_chunk, a.max_splits, a.dm.Hq, a.dm.Hkv, a.dm.D, a.z_out, a.lse_out,
+                     static_cast<const uint8_t*>(a.B_v), a.o_out);
   return hipGetLastError();
 }
 
@@ -621,8 +663,8 @@ hipError_t by_rv(const AttnArgs& a, hipStream_t s) {
     case 16: return by_kw<S, SV, G, 16>(a, s);
     case 32: return by_kw<S, SV, G, 32>(a, s);
     case 64: return by_kw<S, SV, G, 64>(a, s);
-    case 128:
-      if constexpr (SV::CB == 16) return by_kw<S, SV, G, 128>(a, s);
+    case 128:  // values at full width: bf16 only
+      if constexpr (std::is_same_v<S, BF16> && std::is_same_v<SV, BF16>) return by_kw<S, SV, G, 128>(a, s);
       break;
   }
   return hipErrorInvalidValue;

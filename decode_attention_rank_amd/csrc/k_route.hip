@@ -58,8 +58,10 @@ __device__ inline int block_excl_count(bool flag, int* total, int* lds4) {
 }
 
 // Top-k of scores[0..N) into sel[0..k_max): k largest, ties to the lower
-// index, ascending, -1 padding. Also writes -inf to scores[N..max_pages).
-__device__ void select_pages(float* scores, int N, int k, int k_max, int max_pages, int32_t* sel) {
+// index, ascending, -1 padding; with sel_phys, also each chosen page's
+// physical page pt[j] (-1 padding). Also writes -inf to scores[N..max_pages).
+__device__ void select_pages(float* scores, int N, int k, int k_max, int max_pages, int32_t* sel,
+                             const int32_t* pt, int32_t* sel_phys) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_digit;
   __shared__ int s_kk;
@@ -124,11 +126,17 @@ __device__ void select_pages(float* scores, int N, int k, int k_max, int max_pag
     const bool take = gt || (eq && eq_rank < kk);
     int take_total = 0;
     const int pos = taken + block_excl_count(take, &take_total, lds4);
-    if (take && pos < k_max) sel[pos] = j;
+    if (take && pos < k_max) {
+      sel[pos] = j;
+      if (sel_phys) sel_phys[pos] = pt[j];
+    }
     taken += take_total;
     eq_seen += eq_total;
   }
-  for (int i = k + tid; i < k_max; i += kThreads) sel[i] = -1;
+  for (int i = k + tid; i < k_max; i += kThreads) {
+    sel[i] = -1;
+    if (sel_phys) sel_phys[i] = -1;
+  }
   for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
 }
 
@@ -165,10 +173,13 @@ constexpr int kSelectLds = 4096;  // largest page count selected from LDS
 // the histogram itself and finds the same bin. The passes stop early once
 // the bin holding the k-th largest key is taken whole. The ascending
 // compaction gives thread t the contiguous pages t*per .. t*per+per-1, placed
-// by one block-wide scan of the packed (above, equal) counts.
+// by one block-wide scan of the packed (above, equal) counts. With sel_phys,
+// the sequence's page-table row is read into LDS together with the scores
+// (no extra wait), and each chosen page's physical page is written too.
 __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max_pages,
-                                 int32_t* sel) {
+                                 int32_t* sel, const int32_t* pt, int32_t* sel_phys) {
   __shared__ uint32_t s_keys[kSelectLds];
+  __shared__ int32_t s_pt[kSelectLds];
   __shared__ uint4 hist4[4][kWave];  // per pass: 256 bins, lane l owns bins 4l .. 4l+3
   __shared__ int lds4[kWaves];
   const int tid = threadIdx.x;
@@ -182,14 +193,20 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
   if (tid < 4 * kWave) (&hist4[0][0])[tid] = make_uint4(0, 0, 0, 0);
   for (int j0 = 0; j0 < N; j0 += 8 * kThreads) {
     float v[8];
+    int32_t ph[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = __hip_atomic_load(gs + min(j0 + u * kThreads + tid, N - 1), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u * kThreads + tid, N - 1);
+      v[u] = __hip_atomic_load(gs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sel_phys) ph[u] = pt[j];
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = j0 + u * kThreads + tid;
-      if (j < N) s_keys[j] = order_key(v[u]);
+      if (j < N) {
+        s_keys[j] = order_key(v[u]);
+        if (sel_phys) s_pt[j] = ph[u];
+      }
     }
   }
   __syncthreads();
@@ -259,20 +276,26 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
     const bool take = gt || (eq && eq_rank < kk);
     eq_rank += eq ? 1 : 0;
     if (take) {
-      if (pos < k_max) sel[pos] = j;
+      if (pos < k_max) {
+        sel[pos] = j;
+        if (sel_phys) sel_phys[pos] = s_pt[j];
+      }
       ++pos;
     }
   }
-  for (int i = k + tid; i < k_max; i += kThreads) sel[i] = -1;
+  for (int i = k + tid; i < k_max; i += kThreads) {
+    sel[i] = -1;
+    if (sel_phys) sel_phys[i] = -1;
+  }
   for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
 }
 
 __device__ inline void select_top_pages(float* scores, int N, int k, int k_max, int max_pages,
-                                        int32_t* sel) {
+                                        int32_t* sel, const int32_t* pt, int32_t* sel_phys) {
   if (N <= kSelectLds)
-    select_pages_lds(scores, N, k, k_max, max_pages, sel);
+    select_pages_lds(scores, N, k, k_max, max_pages, sel, pt, sel_phys);
   else
-    select_pages(scores, N, k, k_max, max_pages, sel);
+    select_pages(scores, N, k, k_max, max_pages, sel, pt, sel_phys);
 }
 
 // Scores of one 64-token row: acc[h] = q_hat_h . v + q_tilde_h . c per lane,
@@ -314,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     const float* __restrict__ q_proj, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, float* __restrict__ scores,
     uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int32_t* __restrict__ sel_counts,
-    int Hq, int Hkv, int P,
+    int32_t* __restrict__ sel_phys, const int32_t* __restrict__ k_pages, int Hq, int Hkv, int P,
     int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_chunk,
     int batch, KLayout kl) {
   constexpr int CH = S::CH;
@@ -609,13 +632,20 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     __syncthreads();
     if (s_last) {
       const int N = (L + P - 1) >> log2P;
+      // pages kept: the caller's per-sequence budget, else the fraction
+      // (at least one page of a non-empty sequence); at most k_max
       int k = 0;
       if (N > 0) {
-        const long long want = (static_cast<long long>(N) * topk_num + topk_den - 1) / topk_den;
-        k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
+        if (k_pages) {
+          k = min(N, max(k_pages[b], 0));
+        } else {
+          const long long want = (static_cast<long long>(N) * topk_num + topk_den - 1) / topk_den;
+          k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
+        }
         k = min(k, k_max);
       }
-      select_top_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max);
+      select_top_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max, pt,
+                       sel_phys ? sel_phys + static_cast<size_t>(pair) * k_max : nullptr);
       if (threadIdx.x == 0) {
         if (sel_counts) sel_counts[pair] = k;
         reset_ticket(&counters[pair]);
@@ -636,7 +666,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true, true>), grid, dim3(kThreads), lds, s,
                            static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                            a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel,
-                           a.sel_counts, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num,
+                           a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num,
                            a.topk_den, a.k_max, a.rows_per_chunk, a.batch, a.kl);
       else
         return hipErrorInvalidValue;
@@ -644,7 +674,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((route_kernel<S, G, RV, RK, true>), grid, dim3(kThreads), lds, s,
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
-                         a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
+                         a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
                          a.k_max, a.rows_per_chunk, a.batch, a.kl);
     }
   } else {
@@ -653,7 +683,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((route_kernel<S, G, RV, RK, false>), grid, dim3(kThreads), lds, s,
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
-                         a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
+                         a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
                          a.k_max, a.rows_per_chunk, a.batch, a.kl);
   }
   return hipGetLastError();

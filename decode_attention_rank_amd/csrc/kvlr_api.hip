@@ -75,9 +75,9 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int ceil_div(long long a, long long b) { return static_cast<int>((a + b - 1) / b); }
 
-// Workspace plan. Route: [counters | scores]; attention: [counters | partials].
+// Workspace plan. Route: [tickets | scores]; attention: [chunk partials].
 struct Plan {
-  size_t route_cnt, route_scores, attn_cnt, attn_part, total;
+  size_t route_cnt, route_scores, attn_part, total;
   int attn_max_splits;
 };
 
@@ -99,8 +99,6 @@ Plan plan_for(const Dims& dm, int batch, int max_pages) {
   }
   // partial slots per pair: enough for the smallest chunk size over every page
   p.attn_max_splits = max_chunks(attn_rows(max_pages, dm.P), kvlr::attn_rows_per_chunk(true));
-  p.attn_cnt = off;
-  off += round_up(pairs * sizeof(uint32_t));
   p.attn_part = off;
   off += round_up(pairs * p.attn_max_splits * dm.G * static_cast<size_t>(dm.RV + 2) * sizeof(float));
   p.total = off;
@@ -287,9 +285,9 @@ kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* fa
 kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
                              const int32_t* seq_lens, const int32_t* page_table,
                              int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
-                             int32_t k_max, int32_t* sel_pages, int32_t* sel_counts,
-                             float* page_scores, void* workspace, size_t ws_bytes,
-                             int32_t batch, void* stream) {
+                             const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
+                             int32_t* sel_counts, int32_t* sel_phys, float* page_scores,
+                             void* workspace, size_t ws_bytes, int32_t batch, void* stream) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
@@ -298,16 +296,22 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
   if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
-  if (topk_num < 0 || topk_den < 1) return KVLR_ERR_INVALID_ARGUMENT;
-  const long long bound = (static_cast<long long>(max_pages_per_seq) * topk_num + topk_den - 1) / topk_den;
-  const long long need_k = bound < 1 ? 1 : (bound > max_pages_per_seq ? max_pages_per_seq : bound);
-  if (k_max < need_k || k_max > max_pages_per_seq) return KVLR_ERR_INVALID_ARGUMENT;
+  if (k_pages) {
+    // per-sequence budgets: the caller keeps each within [0, k_max]
+    if (k_max < 1 || k_max > max_pages_per_seq || !aligned16(k_pages)) return KVLR_ERR_INVALID_ARGUMENT;
+  } else {
+    if (topk_num < 0 || topk_den < 1) return KVLR_ERR_INVALID_ARGUMENT;
+    const long long bound = (static_cast<long long>(max_pages_per_seq) * topk_num + topk_den - 1) / topk_den;
+    const long long need_k = bound < 1 ? 1 : (bound > max_pages_per_seq ? max_pages_per_seq : bound);
+    if (k_max < need_k || k_max > max_pages_per_seq) return KVLR_ERR_INVALID_ARGUMENT;
+  }
   if (batch == 0) return KVLR_OK;
   if (!ok_ptr(cache->v_lat) || !ok_ptr(cache->k_lat) || !ok_ptr(q_proj) || !ok_ptr(seq_lens) ||
       !ok_ptr(page_table) || !ok_ptr(sel_pages) || !ok_ptr(workspace))
     return KVLR_ERR_INVALID_ARGUMENT;
   if (page_scores && !aligned16(page_scores)) return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_counts && !aligned16(sel_counts)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_phys && !aligned16(sel_phys)) return KVLR_ERR_INVALID_ARGUMENT;
   const Plan plan = plan_for(dm, batch, max_pages_per_seq);
   if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -323,9 +327,11 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.max_pages = max_pages_per_seq;
   a.topk_num = topk_num;
   a.topk_den = topk_den;
+  a.k_pages = k_pages;
   a.k_max = k_max;
   a.sel = sel_pages;
   a.sel_counts = sel_counts;
+  a.sel_phys = sel_phys;
   a.scores = page_scores ? page_scores : reinterpret_cast<float*>(ws + plan.route_scores);
   a.counters = reinterpret_cast<uint32_t*>(ws + plan.route_cnt);
   a.batch = batch;
@@ -344,8 +350,9 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
                                     const kvlr_cache* cache, const float* q, const float* q_proj,
                                     const int32_t* seq_lens, const int32_t* page_table,
                                     int32_t max_pages_per_seq, const int32_t* sel_pages,
-                                    const int32_t* sel_counts, int32_t k_max, float softmax_scale,
-                                    float* z_out, float* lse_out, float* o_out, void* workspace,
+                                    const int32_t* sel_phys, const int32_t* sel_counts,
+                                    int32_t k_max, float softmax_scale, float* z_out,
+                                    float* lse_out, float* o_out, void* workspace,
                                     size_t ws_bytes, int32_t batch, void* stream) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
@@ -361,6 +368,7 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
     return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_pages && !aligned16(sel_pages)) return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_counts && (!sel_pages || !aligned16(sel_counts))) return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_phys && (!sel_pages || !aligned16(sel_phys))) return KVLR_ERR_INVALID_ARGUMENT;
   if (lse_out && !aligned16(lse_out)) return KVLR_ERR_INVALID_ARGUMENT;
   if (dm.exact && (!ok_ptr(cache->k_exact) || !ok_ptr(q))) return KVLR_ERR_INVALID_ARGUMENT;
   if (o_out && (!factors || !ok_ptr(factors->B_v) || !aligned16(o_out))) return KVLR_ERR_INVALID_ARGUMENT;
@@ -378,11 +386,11 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
   a.page_table = page_table;
   a.max_pages = max_pages_per_seq;
   a.sel = sel_pages;
+  a.sel_phys = sel_phys;
   a.sel_counts = sel_counts;
   a.k_max = sel_pages ? k_max : 0;
   a.scale_log2e = softmax_scale * 1.4426950408889634f;
   a.partials = reinterpret_cast<float*>(ws + plan.attn_part);
-  a.counters = reinterpret_cast<uint32_t*>(ws + plan.attn_cnt);
   a.z_out = z_out;
   a.lse_out = lse_out;
   a.B_v = o_out ? factors->B_v : nullptr;
@@ -400,26 +408,28 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
 kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
                              const float* q_proj, const int32_t* seq_lens,
                              const int32_t* page_table, int32_t max_pages_per_seq,
-                             const int32_t* sel_pages, const int32_t* sel_counts, int32_t k_max,
-                             float softmax_scale, float* z_out, float* lse_out, void* workspace,
-                             size_t ws_bytes, int32_t batch, void* stream) {
+                             const int32_t* sel_pages, const int32_t* sel_phys,
+                             const int32_t* sel_counts, int32_t k_max, float softmax_scale,
+                             float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
+                             int32_t batch, void* stream) {
   return decode_attn_impl(shape, nullptr, cache, q, q_proj, seq_lens, page_table, max_pages_per_seq,
-                          sel_pages, sel_counts, k_max, softmax_scale, z_out, lse_out, nullptr,
-                          workspace, ws_bytes, batch, stream);
+                          sel_pages, sel_phys, sel_counts, k_max, softmax_scale, z_out, lse_out,
+                          nullptr, workspace, ws_bytes, batch, stream);
 }
 
 kvlr_status kvlr_decode_attn_upproject(const kvlr_shape* shape, const kvlr_factors* factors,
                                        const kvlr_cache* cache, const float* q,
                                        const float* q_proj, const int32_t* seq_lens,
                                        const int32_t* page_table, int32_t max_pages_per_seq,
-                                       const int32_t* sel_pages, const int32_t* sel_counts,
-                                       int32_t k_max, float softmax_scale, float* z_out,
-                                       float* lse_out, float* o_out, void* workspace,
-                                       size_t ws_bytes, int32_t batch, void* stream) {
+                                       const int32_t* sel_pages, const int32_t* sel_phys,
+                                       const int32_t* sel_counts, int32_t k_max,
+                                       float softmax_scale, float* z_out, float* lse_out,
+                                       float* o_out, void* workspace, size_t ws_bytes,
+                                       int32_t batch, void* stream) {
   if (!o_out) return KVLR_ERR_INVALID_ARGUMENT;
   return decode_attn_impl(shape, factors, cache, q, q_proj, seq_lens, page_table,
-                          max_pages_per_seq, sel_pages, sel_counts, k_max, softmax_scale, z_out,
-                          lse_out, o_out, workspace, ws_bytes, batch, stream);
+                          max_pages_per_seq, sel_pages, sel_phys, sel_counts, k_max, softmax_scale,
+                          z_out, lse_out, o_out, workspace, ws_bytes, batch, stream);
 }
 
 kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors, const float* z,

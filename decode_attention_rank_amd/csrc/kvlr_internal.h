@@ -47,8 +47,10 @@ struct RouteArgs {
   const int32_t* page_table;
   int max_pages;
   int topk_num, topk_den, k_max;
+  const int32_t* k_pages;  // optional [B]: pages kept per sequence (else the fraction)
   int32_t* sel;
   int32_t* sel_counts;  // optional [B][Hkv]
+  int32_t* sel_phys;    // optional [B][Hkv][k_max]: physical pages of sel
   float* scores;        // [B][Hkv][max_pages]
   uint32_t* counters;   // [B * Hkv], zero between calls
   KLayout kl;
@@ -69,14 +71,14 @@ struct AttnArgs {
   const int32_t* page_table;
   int max_pages;
   const int32_t* sel;    // NULL = every page
+  const int32_t* sel_phys;    // optional physical pages of sel
   const int32_t* sel_counts;  // optional valid entries per (sequence, KV head)
   int k_max;
   float scale_log2e;
   float* partials;       // [B*Hkv][num_splits][G][RV + 2]
-  uint32_t* counters;    // [B * Hkv]
   float* z_out;
   float* lse_out;        // may be NULL
-  const void* B_v;       // with o_out: up-project z in the final merge
+  const void* B_v;       // with o_out: up-project z in the merge launch
   float* o_out;          // may be NULL
   int batch;
   int rows_per_chunk;    // 64-token rows per work chunk

@@ -31,7 +31,7 @@ def kvlr_dtype(wl: Workload) -> int:
 class DecodeSession:
     def __init__(self, wl: Workload, device="cuda", *, seq_lens=None, append_per_seq=None,
                  spare_pages: int = 0, tail_fill: float = 0.0, stage_prefix: bool = True,
-                 page_table=None, num_phys=None):
+                 page_table=None, num_phys=None, k_pages=None):
         self.wl = wl
         self.device = torch.device(device)
         self.tail_fill = tail_fill
@@ -91,19 +91,31 @@ class DecodeSession:
         self.cu_new = torch.tensor(cu, dtype=torch.int32, device=dev)
         self.total_new = cu[-1]
 
-        # routing bound and outputs
+        # routing bound and outputs; pages kept: the workload's fraction, or a
+        # per-sequence budget (k_pages, one int per sequence)
         B, Hq, d = wl.batch, wl.num_q_heads, wl.head_dim
-        if wl.routed:
+        self.k_pages_cpu = None if k_pages is None else [int(k) for k in k_pages]
+        self.k_pages = (None if k_pages is None else
+                        torch.tensor(self.k_pages_cpu, dtype=torch.int32, device=dev))
+        if wl.routed and k_pages is not None:
+            self.k_max = min(self.max_pages, max([1] + self.k_pages_cpu))
+        elif wl.routed:
             bound = -(-(self.max_pages * wl.topk_num) // wl.topk_den)
             self.k_max = min(self.max_pages, max(1, bound))
         else:
             self.k_max = 0
+        # attention walks k_max page ids per pair unless the pairs keep
+        # different numbers of pages (ragged lengths or budgets): then the
+        # per-pair counts bound the rows
+        self.use_counts = k_pages is not None or len(set(self.seq_lens)) > 1
         self.qp_width = K.kvlr_qproj_width(self.shape)
         self.q_proj = torch.empty(B, Hq, self.qp_width, dtype=torch.float32, device=dev)
         self.sel = (torch.empty(B, H, self.k_max, dtype=torch.int32, device=dev)
                     if wl.routed else None)
         self.sel_counts = (torch.empty(B, H, dtype=torch.int32, device=dev)
                            if wl.routed else None)
+        self.sel_phys = (torch.empty(B, H, self.k_max, dtype=torch.int32, device=dev)
+                         if wl.routed else None)
         self.page_scores = (torch.empty(B, H, self.max_pages, dtype=torch.float32, device=dev)
                             if wl.routed else None)
         self.z = torch.empty(B, Hq, wl.rank_v, dtype=torch.float32, device=dev)
@@ -190,15 +202,24 @@ class DecodeSession:
 
     def route(self, stream=None):
         K.kvlr_route_pages(self.shape, self.kcache, self.q_proj, self.seq_lens_dev, self.page_table,
-                           self.max_pages, self.wl.topk_num, self.wl.topk_den, self.k_max, self.sel,
-                           self.sel_counts, self.page_scores, self.workspace, self.ws_bytes,
-                           self.wl.batch, stream)
+                           self.max_pages, self.wl.topk_num, self.wl.topk_den, self.k_pages,
+                           self.k_max, self.sel, self.sel_counts, self.sel_phys, self.page_scores,
+                           self.workspace, self.ws_bytes, self.wl.batch, stream)
 
-    def attend(self, stream=None, sel=True, counts=True):
+    def _attn_sel(self, sel, counts, phys):
         use_sel = self.sel if (self.wl.routed and sel) else None
+        if counts is None:
+            counts = self.use_counts
         use_counts = self.sel_counts if (use_sel is not None and counts) else None
+        use_phys = self.sel_phys if (use_sel is not None and phys) else None
+        return use_sel, use_phys, use_counts
+
+    def attend(self, stream=None, sel=True, counts=None, phys=True):
+        """Attention over the selected pages (or every page), then the merge
+        of the chunk records into z and lse."""
+        use_sel, use_phys, use_counts = self._attn_sel(sel, counts, phys)
         K.kvlr_decode_attn(self.shape, self.kcache, self.q, self.q_proj, self.seq_lens_dev,
-                           self.page_table, self.max_pages, use_sel, use_counts,
+                           self.page_table, self.max_pages, use_sel, use_phys, use_counts,
                            self.k_max if use_sel is not None else 0, self.scale, self.z, self.lse,
                            self.workspace, self.ws_bytes, self.wl.batch, stream)
 
@@ -219,17 +240,17 @@ class DecodeSession:
         else:
             self.append(stream)
 
-    def attend_upproject(self, stream=None):
-        """Attention with the up-projection applied in the same launch."""
-        use_sel = self.sel if self.wl.routed else None
-        use_counts = self.sel_counts if use_sel is not None else None
+    def attend_upproject(self, stream=None, counts=None, phys=True):
+        """Attention with the up-projection applied in its merge launch."""
+        use_sel, use_phys, use_counts = self._attn_sel(True, counts, phys)
         K.kvlr_decode_attn_upproject(self.shape, self.kfactors, self.kcache, self.q, self.q_proj,
                                      self.seq_lens_dev, self.page_table, self.max_pages, use_sel,
-                                     use_counts, self.k_max if use_sel is not None else 0,
+                                     use_phys, use_counts,
+                                     self.k_max if use_sel is not None else 0,
                                      self.scale, self.z, self.lse, self.o, self.workspace,
                                      self.ws_bytes, self.wl.batch, stream)
 
-    def finish(self, stream=None, fused=False):
+    def finish(self, stream=None, fused=True):
         """Routing (routed caches), attention and up-projection."""
         if self.wl.routed:
             self.route(stream)
@@ -250,9 +271,26 @@ class DecodeSession:
             self.project_queries(stream)
         self.finish(stream)
 
-    def step(self, stream=None):
+    def step(self, stream=None, fused=True):
         self.prepare(stream)
-        self.finish(stream)
+        self.finish(stream, fused=fused)
+
+    def capture(self, fused=True) -> torch.cuda.CUDAGraph:
+        """The whole step recorded once as a HIP graph (its four launches,
+        no memset or copy nodes: the workspace was cleared by a kernel at
+        set-up). graph.replay() re-runs the step on the same buffers; the
+        launches' host overhead and the gaps between them go away."""
+        side = torch.cuda.Stream()  # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step(fused=fused)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            self.step(fused=fused)
+        torch.cuda.synchronize()
+        return graph
 
     # ------------------------------------------------------------ output side
     def prepare_output_projection(self):

@@ -203,21 +203,32 @@ kvlr_status kvlr_append_encode_project(const kvlr_shape* shape, const kvlr_facto
 /*
  * Page routing (KVLR_KEYS_EXACT only). BasisKV English abstract: the value
  * latent's key prediction plus the key-specific residual rank the key pages,
- * and only the chosen pages are read exactly.
+ * and only the chosen pages are read exactly; the abstract leaves the number
+ * of pages kept to the caller.
  * For each sequence b and KV head g, with L = seq_lens[b], N = ceil(L / P):
  *   s[h, t] = q_hat_h . v_t + q_tilde_h . c_t    (t < L, h in the group)
  *   S[j]    = max over the group's heads and the valid tokens of page j
- *   k_b     = min(N, max(1, ceil(N * topk_num / topk_den))), 0 if N = 0
+ *   k_b     = min(N, k_pages[b]) with a per-sequence budget, else
+ *             min(N, max(1, ceil(N * topk_num / topk_den))); 0 if N = 0
  *   sel     = the k_b pages of largest S, equal scores to the lower index,
  *             written in ascending order, then -1 up to k_max
- *   q_proj       from kvlr_project_queries
+ *   q_proj       from kvlr_project_queries (the routing query images are
+ *                made once per step, where the append launch can carry them)
  *   seq_lens     [batch]
  *   page_table   [batch][max_pages_per_seq]
- *   k_max        host; must be >= min(max_pages_per_seq,
+ *   topk_num, topk_den  host; the fraction of pages kept when k_pages is
+ *                NULL (ignored otherwise)
+ *   k_pages      optional [batch] device budgets, each in [0, k_max]
+ *                (values above k_max keep k_max pages, negative ones none)
+ *   k_max        host; with k_pages: 1 <= k_max <= max_pages_per_seq; else
+ *                at least min(max_pages_per_seq,
  *                ceil(max_pages_per_seq * topk_num / topk_den))
  *   sel_pages    out [batch][H_kv][k_max] logical page ids
  *   sel_counts   optional out [batch][H_kv]: k_b, the number of valid
  *                entries at the front of each sel_pages row
+ *   sel_phys     optional out [batch][H_kv][k_max]: page_table entry of each
+ *                selected page, -1 beside the -1 padding (lets attention
+ *                address the pages without a second lookup)
  *   page_scores  optional out [batch][H_kv][max_pages_per_seq] float32
  *                (S, then -inf past N); NULL keeps them in the workspace
  *   workspace    >= kvlr_workspace_bytes(...) bytes, zero-filled once
@@ -230,9 +241,9 @@ kvlr_status kvlr_append_encode_project(const kvlr_shape* shape, const kvlr_facto
 kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
                              const int32_t* seq_lens, const int32_t* page_table,
                              int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
-                             int32_t k_max, int32_t* sel_pages, int32_t* sel_counts,
-                             float* page_scores, void* workspace, size_t ws_bytes,
-                             int32_t batch, void* stream);
+                             const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
+                             int32_t* sel_counts, int32_t* sel_phys, float* page_scores,
+                             void* workspace, size_t ws_bytes, int32_t batch, void* stream);
 
 /*
  * Decode attention over the compressed cache. BasisKV English abstract:
@@ -247,26 +258,34 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
  * Attended pages: sel_pages[b][g][0 .. n) with -1 entries skipped, where
  * n = sel_counts[b][g] when sel_counts is given (entries past it are not
  * read) and n = k_max otherwise; or every page 0 .. N-1 when sel_pages is
- * NULL. An empty set gives z = 0 and lse = -inf.
+ * NULL. An empty set gives z = 0 and lse = -inf. Without sel_counts every
+ * pair walks k_max entries, which suits batches whose pairs keep about the
+ * same number of pages; with it, ragged batches skip their empty rows.
  *   q        [batch][num_q_heads][head_dim] float32 (EXACT; may be NULL in LATENT)
  *   q_proj   from kvlr_project_queries (LATENT; may be NULL in EXACT)
+ *   sel_phys optional [batch][H_kv][k_max]: the physical page of each
+ *            sel_pages entry (kvlr_route_pages writes it); NULL reads the
+ *            page table
  *   z_out    out [batch][num_q_heads][rank_v] float32
  *   lse_out  optional out [batch][num_q_heads] float32 (natural log)
  *   workspace, ws_bytes: as for kvlr_route_pages
+ * Two launches: the attention over page chunks, then the merge of each
+ * pair's chunk records into z and lse.
  */
 kvlr_status kvlr_decode_attn(const kvlr_shape* shape, const kvlr_cache* cache, const float* q,
                              const float* q_proj, const int32_t* seq_lens,
                              const int32_t* page_table, int32_t max_pages_per_seq,
-                             const int32_t* sel_pages, const int32_t* sel_counts, int32_t k_max,
-                             float softmax_scale,
+                             const int32_t* sel_pages, const int32_t* sel_phys,
+                             const int32_t* sel_counts, int32_t k_max, float softmax_scale,
                              float* z_out, float* lse_out, void* workspace, size_t ws_bytes,
                              int32_t batch, void* stream);
 
 /*
- * kvlr_decode_attn followed by the up-projection, in one launch. BasisKV
- * English abstract and method details (key innovation): the value latent is
- * tied to the output projection, so o_h = z_h . B_v[g] is applied once per
- * query head, here by the workgroup that merges the head group's partials.
+ * kvlr_decode_attn with the up-projection applied in its merge launch.
+ * BasisKV English abstract and method details (key innovation): the value
+ * latent is tied to the output projection, so o_h = z_h . B_v[g] is applied
+ * once per query head, here by the workgroup that merges the head group's
+ * chunk records (float32 FMA over rank_v terms).
  * Arguments as for kvlr_decode_attn, plus:
  *   factors  B_v is read ([H_kv][rank_v][head_dim], storage type)
  *   o_out    out [batch][num_q_heads][head_dim] float32 (required)
@@ -277,10 +296,11 @@ kvlr_status kvlr_decode_attn_upproject(const kvlr_shape* shape, const kvlr_facto
                                        const kvlr_cache* cache, const float* q,
                                        const float* q_proj, const int32_t* seq_lens,
                                        const int32_t* page_table, int32_t max_pages_per_seq,
-                                       const int32_t* sel_pages, const int32_t* sel_counts,
-                                       int32_t k_max, float softmax_scale, float* z_out,
-                                       float* lse_out, float* o_out, void* workspace,
-                                       size_t ws_bytes, int32_t batch, void* stream);
+                                       const int32_t* sel_pages, const int32_t* sel_phys,
+                                       const int32_t* sel_counts, int32_t k_max,
+                                       float softmax_scale, float* z_out, float* lse_out,
+                                       float* o_out, void* workspace, size_t ws_bytes,
+                                       int32_t batch, void* stream);
 
 /*
  * Up-projection, once per query head. BasisKV English abstract and method

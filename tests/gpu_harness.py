@@ -62,6 +62,54 @@ def oracle_state(sess, b: int, g: int) -> dict:
     return st
 
 
+def oracle_states(sess, b: int) -> list:
+    """oracle_state of every KV head of sequence b (one draw of the prefix)."""
+    wl = sess.wl
+    L0, n = sess.lens_before[b], sess.n_new[b]
+    rows = sess.prefix_rows(b)
+    out = []
+    for g in range(wl.num_kv_heads):
+        st = {k: f64(v[g]) for k, v in rows.items()}
+        st["k_lat"] = k_cols(sess, g, st["k_lat"])
+        if n:
+            off = sum(sess.n_new[:b])
+            Kn = f64(sess.k_new[off:off + n, g])
+            Vn = f64(sess.v_new[off:off + n, g])
+            f = factors_np(sess, g)
+            st = O.append_tokens(st, L0, Kn, Vn, f["A_v"], f["A_k"], f["W_pred"],
+                                 key_mode=wl.key_mode, storage=wl.lat_storage)
+        out.append(st)
+    return out
+
+
+def pages_kept(sess, b: int, N: int) -> int:
+    """k_b of sequence b: its budget when the session routes with per-sequence
+    budgets (capped by the page count), else the workload's fraction."""
+    if getattr(sess, "k_pages_cpu", None) is not None:
+        return min(N, max(sess.k_pages_cpu[b], 0)) if N > 0 else 0
+    return O.pages_to_keep(N, sess.wl.topk_num, sess.wl.topk_den)
+
+
+def check_selection(sess, b: int, g: int, st: dict, slack: float = 0.0,
+                    gpu_sel=None, gpu_scores=None) -> int:
+    """The GPU's page set and page scores of (b, g) against the oracle's
+    scores of the same cache; returns the number of pages in the tie band."""
+    wl = sess.wl
+    P, L = wl.page_size, sess.seq_lens[b]
+    f = factors_np(sess, g)
+    N = -(-L // P)
+    S = O.page_scores(q_group(sess, b, g), st["v"], st["k_lat"], f["W_pred"], f["B_k"], L, P)
+    k = pages_kept(sess, b, N)
+    gsel = sess.sel[b, g].cpu().numpy() if gpu_sel is None else gpu_sel
+    ok, band = accepted_selection(S, k, gsel, slack)
+    assert ok, f"pair ({b},{g}): GPU pages {sorted(gsel[gsel >= 0].tolist())[:16]}... not accepted"
+    if N:
+        gs = f64(sess.page_scores[b, g, :N]) if gpu_scores is None else gpu_scores[:N]
+        tol = TIE_REL * np.maximum(1.0, np.abs(S)) + slack
+        assert np.all(np.abs(gs - S) <= tol), f"pair ({b},{g}): page scores off by {np.abs(gs - S).max()}"
+    return band
+
+
 def q_group(sess, b: int, g: int) -> np.ndarray:
     G = sess.wl.group
     return f64(sess.q[b, g * G:(g + 1) * G])
@@ -144,12 +192,18 @@ def check_pair(sess, b: int, g: int, *, state=None, check_scores=True, slack=0.0
     if wl.routed:
         N = -(-L // P)
         S = O.page_scores(q, st["v"], st["k_lat"], f["W_pred"], f["B_k"], L, P)
-        k = O.pages_to_keep(N, wl.topk_num, wl.topk_den)
+        k = pages_kept(sess, b, N)
         gsel = sess.sel[b, g].cpu().numpy()
         ok, band = accepted_selection(S, k, gsel, slack)
         assert ok, f"pair ({b},{g}): GPU pages {sorted(gsel[gsel >= 0].tolist())[:16]}... not accepted"
         info["tie_band"] = band
         pages = [int(j) for j in gsel if j >= 0]
+        if getattr(sess, "sel_phys", None) is not None:
+            # the physical pages written beside the ids: page-table entries, -1 padding
+            gphys = sess.sel_phys[b, g].cpu().numpy()
+            want = np.full(len(gsel), -1, np.int64)
+            want[:len(pages)] = sess.page_table_cpu[b][pages].numpy()
+            assert np.array_equal(gphys, want), f"pair ({b},{g}): physical pages differ from the table"
         if check_scores and N:
             gs = f64(sess.page_scores[b, g, :N])
             tol = TIE_REL * np.maximum(1.0, np.abs(S)) + slack

@@ -90,9 +90,9 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     f = K.make_factors()
     E = K.KVLR_ERR_INVALID_ARGUMENT
     # null pointers
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c), None, None, None, 512, 1, 8, 64,
-                                None, None, None, None, 0, 16, None) == E
-    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c), None, None, None, None, 512, None,
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c), None, None, None, 512, 1, 8, None, 64,
+                                None, None, None, None, None, 0, 16, None) == E
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c), None, None, None, None, 512, None, None,
                                 None, 0, 0.1, None, None, None, 0, 16, None) == E
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), None, None,
                                   None, None, None, 512, 16, 16, None) == E
@@ -103,48 +103,61 @@ def test_bad_arguments_are_rejected_before_launch(lib):
     # k_max below the routing bound, or above max pages
     fake = 1 << 20  # aligned non-null placeholder; never dereferenced on these paths
     c2 = K.make_cache(fake, fake, fake)
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 63,
-                                fake, None, None, fake, 1 << 30, 16, None) == E
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 513,
-                                fake, None, None, fake, 1 << 30, 16, None) == E
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, None, 63,
+                                fake, None, None, None, fake, 1 << 30, 16, None) == E
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, None, 513,
+                                fake, None, None, None, fake, 1 << 30, 16, None) == E
     # topk fraction with a zero denominator
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 0, 64,
-                                fake, None, None, fake, 1 << 30, 16, None) == E
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 0, None, 64,
+                                fake, None, None, None, fake, 1 << 30, 16, None) == E
     # misaligned pointer
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake + 4, fake, fake, 512, 1, 8,
-                                64, fake, None, None, fake, 1 << 30, 16, None) == E
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake + 4, fake, fake, 512, 1, 8, None,
+                                64, fake, None, None, None, fake, 1 << 30, 16, None) == E
     # workspace too small
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
-                                fake, None, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
-    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, fake,
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, None, 64,
+                                fake, None, None, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, fake, None,
                                 None, 64, 0.1, fake, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
     # counts without a page list
-    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, None,
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, None, None,
                                 fake, 64, 0.1, fake, None, fake, 1 << 30, 16, None) == E
     # batch above the supported maximum
-    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
-                                fake, None, None, fake, 1 << 40, 5000, None) == K.KVLR_ERR_UNSUPPORTED
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, None, 64,
+                                fake, None, None, None, fake, 1 << 40, 5000, None) == K.KVLR_ERR_UNSUPPORTED
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
                                   fake, fake, fake, 512, 5000, 16, None) == K.KVLR_ERR_UNSUPPORTED
     # the fused up-projection needs its output and the factors
     assert lib.kvlr_decode_attn_upproject(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
-                                          fake, fake, 512, fake, None, 64, 0.1, fake, None, None, fake,
+                                          fake, fake, 512, fake, None, None, 64, 0.1, fake, None, None, fake,
                                           1 << 30, 16, None) == E
     assert lib.kvlr_decode_attn_upproject(ctypes.byref(s), None, ctypes.byref(c2), fake, fake, fake,
-                                          fake, 512, fake, None, 64, 0.1, fake, None, fake, fake,
+                                          fake, 512, fake, None, None, 64, 0.1, fake, None, fake, fake,
                                           1 << 30, 16, None) == E
     # non-positive or non-finite softmax scale
     for sc in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512,
-                                    fake, None, 64, sc, fake, None, fake, 1 << 30, 16, None) == E
+                                    fake, None, None, 64, sc, fake, None, fake, 1 << 30, 16, None) == E
     # routing reads compressed value latents
     assert lib.kvlr_route_pages(ctypes.byref(_shape(rank_v=128)), ctypes.byref(c2), fake, fake, fake,
-                                512, 1, 8, 64, fake, None, None, fake, 1 << 30, 16,
+                                512, 1, 8, None, 64, fake, None, None, None, fake, 1 << 30, 16,
                                 None) == K.KVLR_ERR_UNSUPPORTED
     # routing needs the routed (exact-key) cache
     sl = _shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)
-    assert lib.kvlr_route_pages(ctypes.byref(sl), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, 64,
-                                fake, None, None, fake, 1 << 30, 16, None) == K.KVLR_ERR_UNSUPPORTED
+    assert lib.kvlr_route_pages(ctypes.byref(sl), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, None, 64,
+                                fake, None, None, None, fake, 1 << 30, 16, None) == K.KVLR_ERR_UNSUPPORTED
+    # per-sequence page budgets: k_max must be positive, arrays aligned
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, fake, 0,
+                                fake, None, None, None, fake, 1 << 30, 16, None) == E
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, fake + 4,
+                                64, fake, None, None, None, fake, 1 << 30, 16, None) == E
+    # with budgets the fraction is not read (a zero denominator is accepted)
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 0, fake, 64,
+                                fake, None, None, None, fake, 16, 16, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    assert lib.kvlr_route_pages(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, 512, 1, 8, None, 64,
+                                fake, None, fake + 4, None, fake, 1 << 30, 16, None) == E
+    # physical page ids need the page ids beside them
+    assert lib.kvlr_decode_attn(ctypes.byref(s), ctypes.byref(c2), fake, fake, fake, fake, 512, None,
+                                fake, None, 64, 0.1, fake, None, fake, 1 << 30, 16, None) == E
     # negative batch / sizes
     assert lib.kvlr_upproject(ctypes.byref(s), ctypes.byref(f), fake, fake, -1, None) == E
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(f), ctypes.byref(c2), fake, fake,
@@ -243,8 +256,8 @@ def test_per_head_residual_rank_arguments(lib):
 
     def route(shape, ranks):
         c = K.make_cache(fake, fake, fake, ranks)
-        return lib.kvlr_route_pages(ctypes.byref(shape), ctypes.byref(c), fake, fake, fake, 512, 1, 8,
-                                    64, fake, None, None, fake, ws, 4, None)
+        return lib.kvlr_route_pages(ctypes.byref(shape), ctypes.byref(c), fake, fake, fake, 512, 1, 8, None,
+                                    64, fake, None, None, None, fake, ws, 4, None)
 
     def encode(shape, ranks):
         c = K.make_cache(fake, fake, fake, ranks)

@@ -341,10 +341,10 @@ def test_binding_reports_bad_launch_arguments():
     s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=1)
     with pytest.raises(K.KvlrError):
         K.kvlr_route_pages(s.shape, s.kcache, s.q_proj, s.seq_lens_dev, s.page_table, s.max_pages,
-                           1, 8, s.k_max - 1, s.sel, None, None, s.workspace, s.ws_bytes, wl.batch)
+                           1, 8, None, s.k_max - 1, s.sel, None, None, None, s.workspace, s.ws_bytes, wl.batch)
     with pytest.raises(K.KvlrError):
         K.kvlr_decode_attn(s.shape, s.kcache, s.q, s.q_proj, s.seq_lens_dev, s.page_table,
-                           s.max_pages, s.sel, None, s.k_max, 0.1, s.z, s.lse, s.workspace, 64, wl.batch)
+                           s.max_pages, s.sel, None, None, s.k_max, 0.1, s.z, s.lse, s.workspace, 64, wl.batch)
 
 
 def test_long_sequence_selects_from_global_scores():
@@ -456,3 +456,83 @@ def test_output_projection_fold(cfg):
         o = np.stack([O.upproject(z[h], Bv[h]) for h in range(Hq)])
         ref = O.output_projection(o, Wo)
         assert H.rel_err(H.f64(s.out[b]), ref) <= H.OUT_TOL
+
+
+GRAPH_CASES = [
+    dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True),
+    dict(G=8, d=128, rv=32, rk=32, P=64, storage="bf16", routed=True, latent="fp8"),
+    dict(G=4, d=128, rv=64, rk=64, P=64, storage="bf16", routed=False),
+    dict(G=2, d=64, rv=32, rk=16, P=16, storage="f32", routed=True),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate-upproject", "fused-upproject"])
+@pytest.mark.parametrize("kw", GRAPH_CASES, ids=["bf16-routed", "fp8-G8", "dense", "f32-P16"])
+def test_graph_replay_matches_eager(kw, fused):
+    """The step captured as a HIP graph: every replay, with the program's own
+    eager work (output buffers overwritten, other kernels) and
+    synchronisations between replays, gives exactly the eager step's outputs
+    and cache pages."""
+    wl = make_wl(**kw)
+    _say("case graph", wl.name, "fused" if fused else "separate")
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37)
+    s.step(fused=fused)
+    torch.cuda.synchronize()
+    names = [n for n in ("sel", "sel_counts", "page_scores", "z", "lse", "o", "q_proj", "v_lat",
+                         "k_lat", "k_exact") if getattr(s, n, None) is not None]
+    ref = {n: getattr(s, n).clone() for n in names}
+    g = s.capture(fused=fused)
+    for rep in range(4):
+        for n in ("z", "lse", "o", "q_proj") + (("sel", "page_scores") if wl.routed else ()):
+            getattr(s, n).fill_(-7)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for n in names:
+            assert torch.equal(getattr(s, n), ref[n]), f"replay {rep}: {n} differs from the eager step"
+    del g
+
+
+@pytest.mark.parametrize("kw", [dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16"),
+                                dict(G=8, d=128, rv=32, rk=32, P=64, storage="bf16", latent="fp8"),
+                                dict(G=2, d=64, rv=32, rk=16, P=16, storage="f32")],
+                         ids=["bf16", "fp8-G8", "f32-P16"])
+def test_per_sequence_page_budgets(kw):
+    """Routing with a caller-given number of pages per sequence (k_pages):
+    each pair keeps min(N_b, k_b) pages, checked against the oracle's scores
+    and brute-force top-k rule; zero budgets attend nothing; budgets above
+    the page count keep every page."""
+    wl = make_wl(routed=True, **kw)
+    _say("case k_pages", wl.name)
+    sess = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37, k_pages=[1, 0, 3, 200])
+    run_and_check(sess)
+    counts = sess.sel_counts.cpu().numpy()
+    N = [-(-L // wl.page_size) for L in LENS]
+    for b in range(wl.batch):
+        assert (counts[b] == min(N[b], [1, 0, 3, 200][b])).all()
+    assert torch.all(torch.isneginf(sess.lse[1])) and torch.all(sess.z[1] == 0)
+
+
+@pytest.mark.parametrize("kw", [dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16"),
+                                dict(G=1, d=64, rv=16, rk=16, P=16, storage="bf16")],
+                         ids=["P64", "P16"])
+def test_attention_walks_agree(kw):
+    """Attention over routed pages gives bit-identical z, lse and o whether
+    it walks every pair's k_max page ids (skipping -1 padding) or only the
+    counted ones, and whether it addresses pages through the physical ids
+    routing wrote or through the page table."""
+    wl = make_wl(routed=True, **kw)
+    _say("case walks", wl.name)
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=37, k_pages=[1, 0, 3, 7])
+    s.prepare()
+    s.route()
+    outs = []
+    for counts, phys in ((True, True), (False, True), (True, False), (False, False)):
+        s.attend_upproject(counts=counts, phys=phys)
+        torch.cuda.synchronize()
+        outs.append({n: getattr(s, n).clone() for n in ("z", "lse", "o")})
+    for o in outs[1:]:
+        for n in ("z", "lse", "o"):
+            assert torch.equal(o[n], outs[0][n]), n

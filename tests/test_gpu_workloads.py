@@ -1,9 +1,14 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (the same five library calls on the same buffers).
+benchmark times (the same library calls on the same buffers, replayed as one
+HIP graph).
 
-The GPU runs the whole step for every (sequence, KV head); the oracle checks a
-sample of pairs one by one: the first and last pairs, a middle one, and for
-ragged contexts the longest and shortest sequences.
+The GPU runs the whole step for every (sequence, KV head). For routed
+workloads the page set and the page scores of EVERY pair are checked against
+the oracle's scores of the same cache (bit-exact outside the tie band: a
+dropped page in a long context would hide inside the output tolerance, so the
+page set is the guard); the outputs z, o and lse are checked on a sample of
+pairs: the first and last pairs, a middle one, and for ragged contexts the
+longest and shortest sequences.
 """
 
 import numpy as np
@@ -42,8 +47,21 @@ def test_full_size_workload(name):
     wl = WORKLOADS[name]
     print("case", name, flush=True)
     sess = DecodeSession(wl, "cuda")
-    sess.step()
+    graph = sess.capture()
+    graph.replay()
     torch.cuda.synchronize()
+    if wl.routed:
+        # every pair's page set, end to end (GPU encode of the new tokens)
+        sel = sess.sel.cpu().numpy()
+        scores = sess.page_scores.cpu().numpy().astype(np.float64)
+        bands = 0
+        for b in range(wl.batch):
+            for g, st in enumerate(H.oracle_states(sess, b)):
+                slack = H.new_token_slack(sess, b, g, st)
+                bands += H.check_selection(sess, b, g, st, slack, gpu_sel=sel[b, g],
+                                           gpu_scores=scores[b, g])
+        print(f"  all {wl.batch * wl.num_kv_heads} page sets accepted; "
+              f"{bands} pages in tie bands", flush=True)
     pairs = _sample(sess)
     states = {}
     for b, g in pairs:
