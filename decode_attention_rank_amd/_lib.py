@@ -36,6 +36,7 @@ EXPORTED = (
     "kvlr_workspace_init", "kvlr_fold_output_weights", "kvlr_output_projection",
     "kvlr_status_string", "kvlr_version", "kvlr_fit_workspace_bytes", "kvlr_fit_moments",
     "kvlr_fit_solve", "kvlr_fit_factors", "kvlr_choose_residual_ranks",
+    "kvlr_decode_attn_upproject_noalloc", "kvlr_noalloc_scratch_bytes",
 )
 
 
@@ -83,6 +84,10 @@ _SIG = {
     "kvlr_decode_attn_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
                                     ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _P, _I,
                                     ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
+    "kvlr_decode_attn_upproject_noalloc": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
+                                            ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _P,
+                                            _I, ctypes.c_float, _P, _P, _P, _I, _P], _I),
+    "kvlr_noalloc_scratch_bytes": ([], ctypes.c_size_t),
     "kvlr_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I, _I], ctypes.c_size_t),
     "kvlr_fold_output_weights": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _I,
@@ -243,6 +248,20 @@ def kvlr_decode_attn_upproject(shape, factors, cache, q, q_proj, seq_lens, page_
         _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_phys),
         _ptr(sel_counts), k_max, float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(o_out),
         _ptr(workspace), ws_bytes, batch, _stream(stream)))
+
+
+def kvlr_decode_attn_upproject_noalloc(shape, factors, cache, q, q_proj, seq_lens, page_table,
+                                       max_pages_per_seq, sel_pages, sel_phys, sel_counts, k_max,
+                                       softmax_scale, z_out, lse_out, o_out, batch, stream=None):
+    _check("kvlr_decode_attn_upproject_noalloc", lib().kvlr_decode_attn_upproject_noalloc(
+        ctypes.byref(shape), ctypes.byref(factors), ctypes.byref(cache), _ptr(q), _ptr(q_proj),
+        _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, _ptr(sel_pages), _ptr(sel_phys),
+        _ptr(sel_counts), k_max, float(softmax_scale), _ptr(z_out), _ptr(lse_out), _ptr(o_out),
+        batch, _stream(stream)))
+
+
+def kvlr_noalloc_scratch_bytes() -> int:
+    return int(lib().kvlr_noalloc_scratch_bytes())
 
 
 def kvlr_upproject(shape, factors, z, o_out, batch, stream=None):

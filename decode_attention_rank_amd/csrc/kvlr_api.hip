@@ -6,12 +6,24 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "kvlr.h"
 #include "kvlr_internal.h"
 
+// Chunk-record scratch of kvlr_decode_attn_upproject_noalloc: one copy per
+// GPU, held until the process ends. Host code never passes this name to a
+// kernel (on the host it only stands for the symbol); it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+static constexpr size_t kStaticScratchBytes = static_cast<size_t>(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};  // device address of `scratch`, per device
 
 using kvlr::Dims;
 
@@ -58,6 +70,25 @@ kvlr_status check_shape(const kvlr_shape* s, Dims* dm) {
   dm->dtype = s->dtype == KVLR_DTYPE_F32 ? 1 : 0;   // factors, original keys, new tokens
   dm->lat = s->dtype == KVLR_DTYPE_BF16_FP8 ? 2 : dm->dtype;
   dm->exact = s->key_mode == KVLR_KEYS_EXACT ? 1 : 0;
+  return KVLR_OK;
+}
+
+// The current device's address of the static scratch, looked up once per
+// device (with that device current) and kept.
+kvlr_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return KVLR_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return KVLR_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
   return KVLR_OK;
 }
 
@@ -353,7 +384,8 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
                                     const int32_t* sel_phys, const int32_t* sel_counts,
                                     int32_t k_max, float softmax_scale, float* z_out,
                                     float* lse_out, float* o_out, void* workspace,
-                                    size_t ws_bytes, int32_t batch, void* stream) {
+                                    size_t ws_bytes, int32_t batch, void* stream,
+                                    bool use_static = false) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
@@ -364,7 +396,7 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
   if (sel_pages && (k_max < 1 || k_max > max_pages_per_seq)) return KVLR_ERR_INVALID_ARGUMENT;
   if (batch == 0) return KVLR_OK;
   if (!ok_ptr(cache->v_lat) || !ok_ptr(seq_lens) || !ok_ptr(page_table) || !ok_ptr(z_out) ||
-      !ok_ptr(workspace))
+      (!use_static && !ok_ptr(workspace)))
     return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_pages && !aligned16(sel_pages)) return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_counts && (!sel_pages || !aligned16(sel_counts))) return KVLR_ERR_INVALID_ARGUMENT;
@@ -374,8 +406,7 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
   if (o_out && (!factors || !ok_ptr(factors->B_v) || !aligned16(o_out))) return KVLR_ERR_INVALID_ARGUMENT;
   if (!dm.exact && (!ok_ptr(cache->k_lat) || !ok_ptr(q_proj))) return KVLR_ERR_INVALID_ARGUMENT;
   const Plan plan = plan_for(dm, batch, max_pages_per_seq);
-  if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (!use_static && ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
   kvlr::AttnArgs a{};
   a.dm = dm;
   a.keys = dm.exact ? cache->k_exact : cache->k_lat;
@@ -390,7 +421,6 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
   a.sel_counts = sel_counts;
   a.k_max = sel_pages ? k_max : 0;
   a.scale_log2e = softmax_scale * 1.4426950408889634f;
-  a.partials = reinterpret_cast<float*>(ws + plan.attn_part);
   a.z_out = z_out;
   a.lse_out = lse_out;
   a.B_v = o_out ? factors->B_v : nullptr;
@@ -400,6 +430,18 @@ static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors*
   a.rows_per_chunk = kvlr::attn_rows_per_chunk(sel_pages != nullptr);
   a.max_splits = max_chunks(rows, a.rows_per_chunk);
   if (a.max_splits > plan.attn_max_splits) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  if (use_static) {
+    // this call's chunk records: pairs x chunks x (m, l, z) per query head
+    const size_t need = static_cast<size_t>(batch) * dm.Hkv * a.max_splits * dm.G *
+                        static_cast<size_t>(dm.RV + 2) * sizeof(float);
+    if (need > kStaticScratchBytes) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+    void* p = nullptr;
+    const kvlr_status sst = static_scratch(&p);
+    if (sst != KVLR_OK) return sst;
+    a.partials = static_cast<float*>(p);
+  } else {
+    a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + plan.attn_part);
+  }
   const long long chunks = static_cast<long long>(batch) * dm.Hkv * a.max_splits;
   a.grid = static_cast<int>(chunks < kAttnGrid ? chunks : kAttnGrid);
   return hip_status(kvlr::launch_attn(a, as_stream(stream)));
@@ -431,6 +473,22 @@ kvlr_status kvlr_decode_attn_upproject(const kvlr_shape* shape, const kvlr_facto
                           max_pages_per_seq, sel_pages, sel_phys, sel_counts, k_max, softmax_scale,
                           z_out, lse_out, o_out, workspace, ws_bytes, batch, stream);
 }
+
+kvlr_status kvlr_decode_attn_upproject_noalloc(const kvlr_shape* shape, const kvlr_factors* factors,
+                                               const kvlr_cache* cache, const float* q,
+                                               const float* q_proj, const int32_t* seq_lens,
+                                               const int32_t* page_table, int32_t max_pages_per_seq,
+                                               const int32_t* sel_pages, const int32_t* sel_phys,
+                                               const int32_t* sel_counts, int32_t k_max,
+                                               float softmax_scale, float* z_out, float* lse_out,
+                                               float* o_out, int32_t batch, void* stream) {
+  if (!o_out) return KVLR_ERR_INVALID_ARGUMENT;
+  return decode_attn_impl(shape, factors, cache, q, q_proj, seq_lens, page_table,
+                          max_pages_per_seq, sel_pages, sel_phys, sel_counts, k_max, softmax_scale,
+                          z_out, lse_out, o_out, nullptr, 0, batch, stream, true);
+}
+
+size_t kvlr_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
 
 kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors, const float* z,
                            float* o_out, int32_t batch, void* stream) {

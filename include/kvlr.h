@@ -14,7 +14,9 @@
  *   - Every pointer argument is a device pointer unless marked "host".
  *     The caller owns every buffer; the library allocates no device memory
  *     and keeps no mutable global state (only the text of each calling
- *     thread's last HIP error, kept per thread). Calls are thread-safe.
+ *     thread's last HIP error, kept per thread), except the static scratch
+ *     array of kvlr_decode_attn_upproject_noalloc. Calls are thread-safe;
+ *     calls of that entry point must not overlap on one GPU.
  *   - Each call validates its arguments on the host, then enqueues its
  *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
  *     returns without synchronising. Outputs are valid once the stream has
@@ -301,6 +303,37 @@ kvlr_status kvlr_decode_attn_upproject(const kvlr_shape* shape, const kvlr_facto
                                        float softmax_scale, float* z_out, float* lse_out,
                                        float* o_out, void* workspace, size_t ws_bytes,
                                        int32_t batch, void* stream);
+
+/*
+ * kvlr_decode_attn_upproject without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Arguments, outputs and results
+ * are those of kvlr_decode_attn_upproject (the same kernels), without
+ * workspace and ws_bytes: the chunk records live in a static device array of
+ * kvlr_noalloc_scratch_bytes() bytes (32 MiB) that each GPU the library runs
+ * on holds until the process ends. A call needing more, i.e. batch * H_kv *
+ * chunks * G * (rank_v + 2) * 4 bytes with chunks = ceil(rows / 16) for
+ * selected pages (rows = k_max * page_size / 64) or ceil(rows / 128) for
+ * every page (rows = max_pages_per_seq * page_size / 64), returns
+ * KVLR_ERR_WORKSPACE_TOO_SMALL and enqueues nothing. The call allocates
+ * nothing (no hipMalloc, no allocating library routine); its first use on a
+ * device looks up that device's address of the array once. Every call on
+ * one GPU shares the array: calls that overlap on one GPU (on different
+ * streams, or from different threads) race and must be ordered by the
+ * caller. Nothing in the array needs clearing: each chunk writes its record
+ * before the merge launch reads it.
+ */
+kvlr_status kvlr_decode_attn_upproject_noalloc(const kvlr_shape* shape, const kvlr_factors* factors,
+                                               const kvlr_cache* cache, const float* q,
+                                               const float* q_proj, const int32_t* seq_lens,
+                                               const int32_t* page_table, int32_t max_pages_per_seq,
+                                               const int32_t* sel_pages, const int32_t* sel_phys,
+                                               const int32_t* sel_counts, int32_t k_max,
+                                               float softmax_scale, float* z_out, float* lse_out,
+                                               float* o_out, int32_t batch, void* stream);
+
+/* Bytes of the static scratch kvlr_decode_attn_upproject_noalloc uses. */
+size_t kvlr_noalloc_scratch_bytes(void);
 
 /*
  * Up-projection, once per query head. BasisKV English abstract and method

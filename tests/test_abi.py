@@ -273,3 +273,27 @@ def test_per_head_residual_rank_arguments(lib):
         assert call(_shape(rank_k=64, dtype=K.KVLR_DTYPE_F32), [16] * 8) == U
         assert call(_shape(rank_k=64, num_q_heads=68, num_kv_heads=17), [16] * 17) == U  # > 16 heads
     assert encode(_shape(rank_k=64, key_mode=K.KVLR_KEYS_LATENT), [16] * 8) == U   # routed keys only
+
+
+def test_noalloc_attention_arguments(lib):
+    """The allocation-free attention call checks its arguments like the
+    workspace one and rejects, before any launch, a call whose chunk records
+    would not fit the static scratch."""
+    fake = 1 << 20
+    s = _shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)
+    c = K.make_cache(fake, fake, fake)
+    f = K.make_factors(fake, fake, fake, fake, fake)
+    assert K.kvlr_noalloc_scratch_bytes() == 32 << 20
+    # dense attention over 2048 sequences of 65536 pages: 2048 * 8 pairs x 512
+    # chunks x 4 heads x 66 floats of chunk records, far above 32 MiB
+    assert lib.kvlr_decode_attn_upproject_noalloc(
+        ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), fake, fake, fake, fake, 65536, None,
+        None, None, 0, 0.1, fake, None, fake, 2048, None) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    # the output is required, as for kvlr_decode_attn_upproject
+    assert lib.kvlr_decode_attn_upproject_noalloc(
+        ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), fake, fake, fake, fake, 512, None,
+        None, None, 0, 0.1, fake, None, None, 16, None) == K.KVLR_ERR_INVALID_ARGUMENT
+    # non-finite scale
+    assert lib.kvlr_decode_attn_upproject_noalloc(
+        ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), fake, fake, fake, fake, 512, None,
+        None, None, 0, float("nan"), fake, None, fake, 16, None) == K.KVLR_ERR_INVALID_ARGUMENT
