@@ -40,6 +40,13 @@ Recipe (per KV head g; all draws seeded by (workload seed, role, sequence)):
     V = (C * scale) Q_v^T; K = [C[:, :ns] * scale[:ns], E * FIT_KEY_SCALE *
     scale[ns:]] Q_k^T with E ~ N(0,1) (ns = shared_rank: the key part the
     value carries). No further noise. Rounded to the storage type.
+  * Attention-output samples for the joint decoder fit (make_output_samples):
+    per sample n a hidden vector s_n ~ N(0, diag(OUT_DECAY^i)) of width
+    OUT_HIDDEN shared by every query head, and per head
+    x_h = (s_n + OUT_OWN u_{n,h}) M_h + OUT_NOISE e, with u, e ~ N(0, I) and
+    M_h ~ N(0, 1/OUT_HIDDEN) [OUT_HIDDEN, d] seeded per head: heads of
+    different KV heads (different GPUs' partitions) are correlated through
+    s_n, as outputs of heads reading one residual stream are. float32.
   * Ragged contexts: L ~ round(lognormal(mu, sigma)) clipped to
     [ctx_min, ctx_max], mu = mean of the log bounds, sigma = quarter of the
     log range.
@@ -55,9 +62,13 @@ import torch
 from .workloads import Workload
 
 _ROLE = {"bases": 1, "q": 2, "coef": 3, "noise": 4, "lens": 5, "planted": 6,
-         "pages": 7, "raw": 8, "oproj": 9, "fit": 10}
+         "pages": 7, "raw": 8, "oproj": 9, "fit": 10, "outputs": 11}
 
 FIT_DECAY = 0.97      # per-coordinate scale ratio of the calibration samples
+OUT_HIDDEN = 64       # width of the hidden part the attention-output samples share
+OUT_DECAY = 0.97      # its per-coordinate scale ratio
+OUT_OWN = 0.5         # head-specific part, relative
+OUT_NOISE = 0.05      # isotropic noise
 FIT_KEY_SCALE = 0.8   # key-only coordinates relative to the shared ones
 
 TORCH_STORAGE = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}
@@ -305,3 +316,22 @@ def make_fit_samples(wl: Workload, n: int, device="cpu"):
         K[:, g] = (kc @ bk.T.contiguous()).to(dt)
         del C, E, kc
     return K, V
+
+
+def make_output_samples(wl: Workload, n: int, device="cpu", chunk: int = 4096) -> torch.Tensor:
+    """Attention-output samples X [n, H_q, d] float32 for the joint decoder fit."""
+    Hq, d, m = wl.num_q_heads, wl.head_dim, OUT_HIDDEN
+    gm = _gen("cpu", wl.seed, "outputs", 0)
+    M = (torch.randn(Hq, m, d, generator=gm, dtype=torch.float64) / math.sqrt(m)).to(torch.float32)
+    M = M.to(device)
+    scale = (OUT_DECAY ** torch.arange(m, dtype=torch.float64)).to(torch.float32).to(device)
+    X = torch.empty(n, Hq, d, dtype=torch.float32, device=device)
+    for c0 in range(0, n, chunk):
+        c = min(chunk, n - c0)
+        gen = _gen(device, wl.seed, "outputs", 1, c0)
+        s = torch.randn(c, m, generator=gen, device=device) * scale
+        for h in range(Hq):
+            u = torch.randn(c, m, generator=gen, device=device)
+            e = torch.randn(c, d, generator=gen, device=device)
+            X[c0:c0 + c, h] = (s + OUT_OWN * u) @ M[h] + OUT_NOISE * e
+    return X

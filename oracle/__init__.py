@@ -29,4 +29,10 @@ from .kvlr_oracle import (  # noqa: F401
     latent_output_projection,
     fit_factors,
     choose_residual_ranks,
+    latent_outputs,
+    staged_decoder,
+    fit_joint_decoder,
+    fit_partition_decoders,
+    fold_decoder,
+    complete_output_error,
 )

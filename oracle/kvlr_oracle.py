@@ -447,3 +447,96 @@ def choose_residual_ranks(lam_k, energy_frac: float, allowed=(16, 32, 64)):
                 break
         out.append(pick)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Joint fit of the value decoders across per-GPU attention partitions
+# (BasisKV English abstract: the low-rank factors are optimised jointly across
+# the per-GPU attention partitions against the complete attention output,
+# not partition by partition; method details, key design: the loss couples
+# every GPU's attention partition; key innovation: value compression is tied
+# to the output projection). Reading taken here: the value encoders A_g stay
+# as fitted (the cache's latents v = V A_g exist before any query), and the
+# decoders that map latent outputs back to attention outputs are what the
+# joint loss chooses. Head h's latent output is z_h = x_h A_g (x_h its exact
+# attention output, sum_t p_t V_t, since z_h = sum_t p_t v_t); the complete
+# output of a layer is y = W_o concat_h(x_h), reproduced as F concat_h(z_h)
+# with the folded decoder F = W_o D^T.
+#   staged:    D = blockdiag_h(A_g^T)          (B_v = A_v^T, head by head)
+#   isolated:  partition p fits its own heads' outputs from its own latents
+#   joint:     D = argmin sum_n |x_n - z_n D|^2 over all partitions at once
+# For any W_o, argmin_F sum_n |W_o x_n - F z_n|^2 = W_o D_joint^T: the
+# least-squares residual of D_joint is orthogonal to every latent, so one
+# decoder serves every output projection.
+# ----------------------------------------------------------------------------
+
+def latent_outputs(X, A_heads, group: int):
+    """z_h = x_h A_{h // group} for every query head h of every sample.
+
+    X: [n, H_q, d] exact attention outputs; A_heads: [H_kv, d, r].
+    Returns Z [n, H_q * r] (head h's latents at columns h r .. h r + r - 1).
+    """
+    X = np.asarray(X, np.float64)
+    A = np.asarray(A_heads, np.float64)
+    n, Hq, d = X.shape
+    r = A.shape[2]
+    Z = np.empty((n, Hq * r))
+    for h in range(Hq):
+        Z[:, h * r:(h + 1) * r] = X[:, h, :] @ A[h // group]
+    return Z
+
+
+def staged_decoder(A_heads, num_q_heads: int):
+    """D = blockdiag_h(A_{g(h)}^T), [H_q r, H_q d]: each head decoded by its own
+    up-projection B_v = A_v^T."""
+    A = np.asarray(A_heads, np.float64)
+    H_kv, d, r = A.shape
+    group = num_q_heads // H_kv
+    D = np.zeros((num_q_heads * r, num_q_heads * d))
+    for h in range(num_q_heads):
+        D[h * r:(h + 1) * r, h * d:(h + 1) * d] = A[h // group].T
+    return D
+
+
+def fit_joint_decoder(X, A_heads, group: int):
+    """Decoder of the complete attention output from the latents of every
+    partition: D = argmin_D |X - Z D|_F^2 (numpy least squares on the
+    samples), X flattened to [n, H_q d]. Returns D [H_q r, H_q d]."""
+    X = np.asarray(X, np.float64)
+    n = X.shape[0]
+    Z = latent_outputs(X, A_heads, group)
+    D, *_ = np.linalg.lstsq(Z, X.reshape(n, -1), rcond=None)
+    return D
+
+
+def fit_partition_decoders(X, A_heads, group: int, partitions):
+    """Each partition fitted in isolation: partition p (a list of KV heads)
+    decodes its own query heads' outputs from its own latents only, by least
+    squares; D is block diagonal over the partitions."""
+    X = np.asarray(X, np.float64)
+    n, Hq, d = X.shape
+    Z = latent_outputs(X, A_heads, group)
+    r = Z.shape[1] // Hq
+    D = np.zeros((Hq * r, Hq * d))
+    for part in partitions:
+        heads = [h for g in part for h in range(g * group, (g + 1) * group)]
+        zc = np.concatenate([np.arange(h * r, (h + 1) * r) for h in heads])
+        xc = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
+        Dp, *_ = np.linalg.lstsq(Z[:, zc], X.reshape(n, -1)[:, xc], rcond=None)
+        D[np.ix_(zc, xc)] = Dp
+    return D
+
+
+def fold_decoder(W_o, D):
+    """F = W_o D^T: the output projection seen from the latents of all heads,
+    [hidden, H_q r] (with the staged D this is fold_output_weights)."""
+    return np.asarray(W_o, np.float64) @ np.asarray(D, np.float64).T
+
+
+def complete_output_error(X, A_heads, group: int, D, W_o):
+    """sum_n |W_o x_n - W_o D^T z_n|^2: the loss on the complete output."""
+    X = np.asarray(X, np.float64)
+    n = X.shape[0]
+    Z = latent_outputs(X, A_heads, group)
+    R = (X.reshape(n, -1) - Z @ np.asarray(D, np.float64)) @ np.asarray(W_o, np.float64).T
+    return float(np.sum(R * R))

@@ -131,3 +131,37 @@ def test_fit_smallest_directions_is_caught(monkeypatch):
         return w[:r], U[:, :r]
     monkeypatch.setattr(K, "_top_eigvecs", bad_top)
     _fails(pins.test_fit_value_basis_is_the_top_right_singular_subspace)
+
+
+def test_latents_from_the_wrong_kv_head_are_caught(monkeypatch):
+    def wrong(X, A_heads, group):
+        X = np.asarray(X, float)
+        A = np.asarray(A_heads, float)
+        n, Hq, d = X.shape
+        r = A.shape[2]
+        return np.concatenate([X[:, h] @ A[h % A.shape[0]] for h in range(Hq)], axis=1)
+    _patch(monkeypatch, "latent_outputs", wrong)
+    _fails(pins.test_latent_outputs_use_each_heads_kv_encoder)
+
+
+def test_joint_fit_done_head_by_head_is_caught(monkeypatch):
+    # a "joint" fit that ignores the other heads' latents (per-head decoders)
+    def wrong(X, A_heads, group):
+        X = np.asarray(X, float)
+        n, Hq, d = X.shape
+        return K.fit_partition_decoders(X, A_heads, group,
+                                        [[g] for g in range(np.asarray(A_heads).shape[0])])
+    _patch(monkeypatch, "fit_joint_decoder", wrong)
+    _fails(pins.test_joint_fit_never_loses_to_isolated_or_staged_decoders, 35)
+
+
+def test_decoder_fitted_against_the_latents_transposed_is_caught(monkeypatch):
+    def wrong(X, A_heads, group):
+        X = np.asarray(X, float)
+        n = X.shape[0]
+        Z = K.latent_outputs(X, A_heads, group)
+        # the encoder-side map (x -> z) instead of the decoder (z -> x)
+        E, *_ = np.linalg.lstsq(X.reshape(n, -1), Z, rcond=None)
+        return E.T
+    _patch(monkeypatch, "fit_joint_decoder", wrong)
+    _fails(pins.test_joint_decoder_satisfies_the_normal_equations)

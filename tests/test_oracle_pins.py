@@ -552,3 +552,114 @@ def test_fit_latent_mode_uses_key_principal_directions():
     assert f["W_pred"] is None
     _, _, Vt = np.linalg.svd(K, full_matrices=False)
     np.testing.assert_allclose(f["A_k"] @ f["A_k"].T, Vt[:5].T @ Vt[:5], atol=1e-9)
+
+
+# ----------------------------------------------------------------------------
+# Joint fit of the decoders across partitions (BasisKV English abstract:
+# factors optimised jointly across per-GPU partitions against the complete
+# attention output)
+# ----------------------------------------------------------------------------
+
+def _correlated_outputs(rng, n, Hq, d, m=8, shared=1.0, own=0.5, noise=0.05):
+    """Attention-output-like samples whose heads share a hidden component:
+    x_h = (shared s_n + own u_{n,h}) M_h + noise."""
+    s = rng.standard_normal((n, m))
+    X = np.empty((n, Hq, d))
+    for h in range(Hq):
+        M = rng.standard_normal((m, d)) / math.sqrt(m)
+        X[:, h] = (shared * s + own * rng.standard_normal((n, m))) @ M
+    return X + noise * rng.standard_normal(X.shape)
+
+
+def _encoders(rng, H_kv, d, r):
+    return np.stack([_orth(rng, d)[:, :r] for _ in range(H_kv)])
+
+
+def test_joint_decoder_at_full_rank_is_the_staged_decoder():
+    # r = d with orthonormal encoders: z A^T = x exactly, so the unique least-
+    # squares decoder is blockdiag(A^T) and the complete output is exact
+    rng = np.random.default_rng(31)
+    Hq, H_kv, d = 4, 2, 8
+    X = _correlated_outputs(rng, 200, Hq, d)
+    A = _encoders(rng, H_kv, d, d)
+    D = O.fit_joint_decoder(X, A, Hq // H_kv)
+    assert np.allclose(D, O.staged_decoder(A, Hq), atol=1e-10)
+    W = rng.standard_normal((12, Hq * d))
+    assert O.complete_output_error(X, A, Hq // H_kv, D, W) < 1e-18 * np.sum(X * X)
+
+
+def test_joint_decoder_of_outputs_in_the_latent_span_is_the_staged_decoder():
+    # x_h = c_h A_g^T (outputs inside each head's encoder span): Z = C and
+    # X = Z blockdiag(A^T) exactly, a unique fit when Z has full column rank
+    rng = np.random.default_rng(32)
+    Hq, H_kv, d, r, n = 6, 3, 16, 4, 100
+    A = _encoders(rng, H_kv, d, r)
+    C = rng.standard_normal((n, Hq, r))
+    X = np.stack([C[:, h] @ A[h // 2].T for h in range(Hq)], axis=1)
+    D = O.fit_joint_decoder(X, A, Hq // H_kv)
+    assert np.allclose(D, O.staged_decoder(A, Hq), atol=1e-10)
+
+
+def test_joint_decoder_satisfies_the_normal_equations():
+    # the residual of a least-squares fit is orthogonal to every regressor
+    rng = np.random.default_rng(33)
+    Hq, H_kv, d, r = 8, 2, 16, 4
+    X = _correlated_outputs(rng, 300, Hq, d)
+    A = _encoders(rng, H_kv, d, r)
+    Z = O.latent_outputs(X, A, Hq // H_kv)
+    R = X.reshape(300, -1) - Z @ O.fit_joint_decoder(X, A, Hq // H_kv)
+    assert np.abs(Z.T @ R).max() < 1e-9 * np.abs(Z).max() * np.abs(X).max() * 300
+
+
+def test_latent_outputs_use_each_heads_kv_encoder():
+    rng = np.random.default_rng(34)
+    Hq, H_kv, d, r = 4, 2, 8, 3
+    X = rng.standard_normal((5, Hq, d))
+    A = _encoders(rng, H_kv, d, r)
+    Z = O.latent_outputs(X, A, 2)
+    for n in range(5):
+        for h in range(Hq):
+            for j in range(r):
+                assert abs(Z[n, h * r + j] - sum(X[n, h, i] * A[h // 2, i, j] for i in range(d))) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [35, 36])
+def test_joint_fit_never_loses_to_isolated_or_staged_decoders(seed):
+    # joint, isolated and staged decoders are all feasible for the joint
+    # problem; isolated decoders contain the staged ones. On heads sharing a
+    # hidden component the joint one is strictly better, for any W_o.
+    rng = np.random.default_rng(seed)
+    Hq, H_kv, d, r = 8, 4, 16, 4
+    X = _correlated_outputs(rng, 400, Hq, d)
+    A = _encoders(rng, H_kv, d, r)
+    parts = [[0, 1], [2, 3]]
+    W = rng.standard_normal((24, Hq * d))
+    e_joint = O.complete_output_error(X, A, 2, O.fit_joint_decoder(X, A, 2), W)
+    e_iso = O.complete_output_error(X, A, 2, O.fit_partition_decoders(X, A, 2, parts), W)
+    e_staged = O.complete_output_error(X, A, 2, O.staged_decoder(A, Hq), W)
+    assert e_joint < 0.95 * e_iso
+    assert e_iso <= e_staged * (1 + 1e-12)
+
+
+def test_joint_fit_equals_isolated_fits_when_partitions_never_co_occur():
+    # each sample has output in one partition only: the cross-partition
+    # moments vanish and the joint problem splits into the isolated ones
+    rng = np.random.default_rng(37)
+    Hq, H_kv, d, r, n = 4, 2, 12, 3, 240
+    X = _correlated_outputs(rng, n, Hq, d)
+    X[: n // 2, 2:] = 0.0   # partition 1 (KV head 1: heads 2, 3) silent
+    X[n // 2:, :2] = 0.0    # partition 0 silent
+    A = _encoders(rng, H_kv, d, r)
+    Dj = O.fit_joint_decoder(X, A, 2)
+    Di = O.fit_partition_decoders(X, A, 2, [[0], [1]])
+    assert np.allclose(Dj, Di, atol=1e-9)
+
+
+def test_folded_staged_decoder_is_the_output_projection_fold():
+    rng = np.random.default_rng(38)
+    Hq, H_kv, d, r = 4, 2, 8, 4
+    A = _encoders(rng, H_kv, d, r)
+    W = rng.standard_normal((16, Hq * d))
+    B_v_heads = np.stack([A[h // 2].T for h in range(Hq)])
+    assert np.allclose(O.fold_decoder(W, O.staged_decoder(A, Hq)),
+                       O.fold_output_weights(B_v_heads, W), atol=1e-12)

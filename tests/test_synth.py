@@ -103,3 +103,20 @@ def test_planted_pages_are_recalled_by_routing():
         assert len(res["sel"]) == math.ceil(N / 16)
         recalls.append(len(planted & set(res["sel"])) / len(planted))
     assert min(recalls) >= 0.8
+
+
+def test_output_samples_are_seeded_and_share_a_hidden_part():
+    from decode_attention_rank_amd.workloads import FIT_WORKLOADS
+    wl = FIT_WORKLOADS["llama3-8b-fit-512k"].scaled(num_q_heads=8, num_kv_heads=2)
+    X = synth.make_output_samples(wl, 3000)
+    assert X.shape == (3000, 8, wl.head_dim) and X.dtype == torch.float32
+    assert torch.equal(X, synth.make_output_samples(wl, 3000))
+    # heads of different KV heads are correlated through the shared hidden part:
+    # the leading canonical correlation between two heads is far from zero
+    a = X[:, 0].double()
+    b = X[:, 7].double()
+    a = a - a.mean(0)
+    b = b - b.mean(0)
+    qa, _ = torch.linalg.qr(a)
+    qb, _ = torch.linalg.qr(b)
+    assert torch.linalg.svdvals(qa.T @ qb)[0] > 0.5
