@@ -48,6 +48,7 @@ METRIC = "decode-attn KV-tokens/s over compressed cache + % of HBM peak GB/s (1 
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30   # written between steps of the cold pass (> the 256 MB Infinity Cache)
 CPU_CACHE_BYTES = 6 << 30  # host memory for oracle inputs repeated after the first pass
+JOINT_SAMPLES = 8192       # calibration samples of the joint decoder fit
 CSRC = os.path.join(ROOT, "decode_attention_rank_amd", "csrc")
 KERNEL_SOURCES = {
     "route_kernel": os.path.join(CSRC, "k_route.hip"),
@@ -485,6 +486,50 @@ def time_factor_fit(reps: int = 10):
             "fit_factors_call_ms": round(fit_ms, 2)}
 
 
+def time_joint_fit(reps: int = 5):
+    """The joint decoder fit on calibration samples at the 8B layer's shapes
+    (32 query heads of 8 KV heads, every partition's latents at once):
+    kvlr_fit_joint_moments timed with HIP events, and the whole synchronous
+    kvlr_fit_joint call (moments, copy to host, float64 Cholesky solve over
+    the 4096 output columns, fold into F = W_o D^T) by wall clock."""
+    from decode_attention_rank_amd.fit import JointFit
+    from decode_attention_rank_amd.workloads import DEFAULT_FIT_WORKLOAD, FIT_WORKLOADS
+
+    wl = FIT_WORKLOADS[DEFAULT_FIT_WORKLOAD]
+    n = JOINT_SAMPLES
+    Hq, d, r = wl.num_q_heads, wl.head_dim, wl.rank_v
+    x = synth.make_output_samples(wl, n, device="cuda")
+    factors = synth.make_factors(wl, "cuda")
+    from decode_attention_rank_amd import _lib as K
+    kf = K.make_factors(**factors)
+    hidden = synth.output_width(wl)
+    W_o = synth.make_output_weight(wl, "cuda")
+    jf = JointFit(wl, n, hidden)
+    stream = torch.cuda.current_stream()
+    jf.fit(kf, x, W_o)
+    for _ in range(2):
+        jf.moments(kf, x, n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        jf.moments(kf, x, n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    t0 = time.perf_counter()
+    for _ in range(2):
+        jf.fit(kf, x, W_o)
+    call_ms = (time.perf_counter() - t0) * 1e3 / 2
+    nl, nx = Hq * r, Hq * d
+    flops = 2.0 * n * (Hq * d * r + nl * nl + nl * nx)   # Z = X A, Z^T Z, Z^T X
+    del x
+    return {"workload": wl.name, "samples": n, "num_q_heads": Hq, "latents": nl, "outputs": nx,
+            "hidden": hidden,
+            "timed": "kvlr_fit_joint_moments: latent outputs and the moments Z^T Z, Z^T X",
+            "moments_call_us": round(us, 1), "mfma_f32_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "fit_joint_call_ms": round(call_ms, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -571,6 +616,8 @@ def main():
     if not args.no_fit:
         log("[bench] timing the factor fit")
         out["factor_fit"] = time_factor_fit()
+        log("[bench] timing the joint decoder fit")
+        out["joint_fit"] = time_joint_fit()
     print(json.dumps(out), flush=True)
 
 

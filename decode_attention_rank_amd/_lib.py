@@ -37,6 +37,8 @@ EXPORTED = (
     "kvlr_status_string", "kvlr_version", "kvlr_fit_workspace_bytes", "kvlr_fit_moments",
     "kvlr_fit_solve", "kvlr_fit_factors", "kvlr_choose_residual_ranks",
     "kvlr_decode_attn_upproject_noalloc", "kvlr_noalloc_scratch_bytes",
+    "kvlr_fit_joint_workspace_bytes", "kvlr_fit_joint_moments", "kvlr_fit_joint_solve",
+    "kvlr_fold_joint_decoder", "kvlr_fit_joint",
 )
 
 
@@ -88,6 +90,13 @@ _SIG = {
                                             ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _P,
                                             _I, ctypes.c_float, _P, _P, _P, _I, _P], _I),
     "kvlr_noalloc_scratch_bytes": ([], ctypes.c_size_t),
+    "kvlr_fit_joint_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I], ctypes.c_size_t),
+    "kvlr_fit_joint_moments": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _I, _P,
+                                _P, _I, _P, ctypes.c_size_t, _P], _I),
+    "kvlr_fit_joint_solve": ([ctypes.POINTER(kvlr_shape), _P, _P, _P], _I),
+    "kvlr_fold_joint_decoder": ([ctypes.POINTER(kvlr_shape), _P, _I, _P, _P, _P], _I),
+    "kvlr_fit_joint": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _I, _P, _I, _P,
+                        _P, _P, ctypes.c_size_t, _P], _I),
     "kvlr_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _P, _I, _P], _I),
     "kvlr_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I, _I], ctypes.c_size_t),
     "kvlr_fold_output_weights": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _I,
@@ -316,3 +325,47 @@ def kvlr_choose_residual_ranks(shape, lam_k, energy_frac) -> list:
     _check("kvlr_choose_residual_ranks", lib().kvlr_choose_residual_ranks(
         ctypes.byref(shape), _ptr(lam_k), float(energy_frac), ctypes.cast(out, ctypes.c_void_p)))
     return list(out)
+
+
+def kvlr_fit_joint_workspace_bytes(shape, n) -> int:
+    return int(lib().kvlr_fit_joint_workspace_bytes(ctypes.byref(shape), n))
+
+
+def kvlr_fit_joint_moments(shape, factors, x, n, zz, zx, accumulate, workspace, ws_bytes,
+                           stream=None):
+    _check("kvlr_fit_joint_moments", lib().kvlr_fit_joint_moments(
+        ctypes.byref(shape), ctypes.byref(factors), _ptr(x), n, _ptr(zz), _ptr(zx), accumulate,
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvlr_fit_joint_solve(shape, zz, zx):
+    """Host solve; zz, zx host float64 arrays. Returns D (float64 numpy)."""
+    zz = _host_f64(zz, "zz")
+    zx = _host_f64(zx, "zx")
+    zz = zz.numpy() if isinstance(zz, torch.Tensor) else zz
+    zx = zx.numpy() if isinstance(zx, torch.Tensor) else zx
+    D = np.empty(zx.shape, dtype=np.float64)
+    _check("kvlr_fit_joint_solve", lib().kvlr_fit_joint_solve(
+        ctypes.byref(shape), zz.ctypes.data_as(ctypes.c_void_p), zx.ctypes.data_as(ctypes.c_void_p),
+        D.ctypes.data_as(ctypes.c_void_p)))
+    return D
+
+
+def kvlr_fold_joint_decoder(shape, W_o, hidden, D, F_out, stream=None):
+    _check("kvlr_fold_joint_decoder", lib().kvlr_fold_joint_decoder(
+        ctypes.byref(shape), _ptr(W_o), hidden, _ptr(D), _ptr(F_out), _stream(stream)))
+
+
+def kvlr_fit_joint(shape, factors, x, n, W_o, hidden, F_out, workspace, ws_bytes, want_D=False,
+                   stream=None):
+    """The synchronous joint fit; returns the float64 decoder when asked."""
+    D = None
+    if want_D:
+        nl = shape.num_q_heads * shape.rank_v
+        nx = shape.num_q_heads * shape.head_dim
+        D = np.empty((nl, nx), dtype=np.float64)
+    _check("kvlr_fit_joint", lib().kvlr_fit_joint(
+        ctypes.byref(shape), ctypes.byref(factors), _ptr(x), n, _ptr(W_o), hidden, _ptr(F_out),
+        None if D is None else D.ctypes.data_as(ctypes.c_void_p), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return D

@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvlr.so")
 
 SOURCES = ["kvlr_api.hip", "k_route.hip", "k_attn.hip", "k_encode.hip", "k_small.hip", "k_oproj.hip",
-           "k_fit.hip"]
+           "k_fit.hip", "k_outfit.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -574,6 +574,89 @@ kvlr_status kvlr_fit_moments(const kvlr_shape* shape, const void* k, const void*
   return hip_status(kvlr::launch_fit_moments(a, as_stream(stream)));
 }
 
+// Joint decoder fit: sizes and buffers. nl = H_q rank_v latents per sample,
+// nx = H_q head_dim outputs per sample.
+static bool joint_dims(const Dims& dm, long* nl, long* nx) {
+  *nl = static_cast<long>(dm.Hq) * dm.RV;
+  *nx = static_cast<long>(dm.Hq) * dm.D;
+  return *nl <= 4096 && *nx <= 16384;
+}
+
+size_t kvlr_fit_joint_workspace_bytes(const kvlr_shape* shape, int32_t n) {
+  Dims dm;
+  long nl = 0, nx = 0;
+  if (check_shape(shape, &dm) != KVLR_OK || n < 0 || dm.lat == 2 || !joint_dims(dm, &nl, &nx)) return 0;
+  return round_up(static_cast<size_t>(n) * nl * sizeof(float)) +        // latent outputs Z
+         round_up(static_cast<size_t>(nl) * nl * sizeof(double)) +      // Z^T Z
+         round_up(static_cast<size_t>(nl) * nx * sizeof(double)) +      // Z^T X
+         round_up(static_cast<size_t>(nl) * nx * sizeof(float));        // decoder for the fold
+}
+
+kvlr_status kvlr_fit_joint_moments(const kvlr_shape* shape, const kvlr_factors* factors,
+                                   const float* x, int32_t n, double* zz, double* zx,
+                                   int32_t accumulate, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  long nl = 0, nx = 0;
+  if (dm.lat == 2 || !joint_dims(dm, &nl, &nx)) return KVLR_ERR_UNSUPPORTED;
+  if (!factors || n < 0 || (accumulate != 0 && accumulate != 1) || !ok_ptr(zz) || !ok_ptr(zx))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (!ok_ptr(factors->A_v) || !ok_ptr(x) || !ok_ptr(workspace)))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (n > 0 && ws_bytes < round_up(static_cast<size_t>(n) * nl * sizeof(float)))
+    return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  kvlr::JointArgs a{};
+  a.dm = dm;
+  a.A_v = factors->A_v;
+  a.x = x;
+  a.n = n;
+  a.z = static_cast<float*>(workspace);
+  a.zz = zz;
+  a.zx = zx;
+  a.accumulate = accumulate;
+  if (n == 0) {
+    if (accumulate) return KVLR_OK;
+    hipError_t e = kvlr::launch_zero_fill(zz, static_cast<size_t>(nl) * nl * sizeof(double), as_stream(stream));
+    if (e == hipSuccess)
+      e = kvlr::launch_zero_fill(zx, static_cast<size_t>(nl) * nx * sizeof(double), as_stream(stream));
+    return hip_status(e);
+  }
+  return hip_status(kvlr::launch_joint_moments(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_fit_joint_solve(const kvlr_shape* shape, const double* zz, const double* zx,
+                                 double* D_out) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  long nl = 0, nx = 0;
+  if (dm.lat == 2 || !joint_dims(dm, &nl, &nx)) return KVLR_ERR_UNSUPPORTED;
+  if (!zz || !zx || !D_out) return KVLR_ERR_INVALID_ARGUMENT;
+  return kvlr::joint_solve(static_cast<int>(nl), static_cast<int>(nx), zz, zx, D_out) == kvlr::FitStatus::kOk
+             ? KVLR_OK
+             : KVLR_ERR_NUMERICAL;
+}
+
+kvlr_status kvlr_fold_joint_decoder(const kvlr_shape* shape, const void* W_o, int32_t hidden,
+                                    const float* D, void* F_out, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  long nl = 0, nx = 0;
+  if (dm.dtype != KVLR_DTYPE_BF16 || dm.lat == 2 || !joint_dims(dm, &nl, &nx)) return KVLR_ERR_UNSUPPORTED;
+  if (hidden < 1 || hidden > (1 << 20) || !ok_ptr(W_o) || !ok_ptr(D) || !ok_ptr(F_out))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::JointFoldArgs a{};
+  a.dm = dm;
+  a.W_o = W_o;
+  a.Dm = D;
+  a.F = F_out;
+  a.hidden = hidden;
+  return hip_status(kvlr::launch_joint_fold(a, as_stream(stream)));
+}
+
 kvlr_status kvlr_choose_residual_ranks(const kvlr_shape* shape, const double* lam_k,
                                        double energy_frac, int32_t* ranks_out) {
   Dims dm;
@@ -688,6 +771,47 @@ kvlr_status kvlr_fit_factors(const kvlr_shape* shape, const void* k, const void*
     if (e != hipSuccess) return hip_status(e);
   }
   return hip_status(hipStreamSynchronize(s));  // the host images must outlive the copies
+}
+
+kvlr_status kvlr_fit_joint(const kvlr_shape* shape, const kvlr_factors* factors, const float* x,
+                           int32_t n, const void* W_o, int32_t hidden, void* F_out, double* D_out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  long nl = 0, nx = 0;
+  if (dm.dtype != KVLR_DTYPE_BF16 || dm.lat == 2 || !joint_dims(dm, &nl, &nx)) return KVLR_ERR_UNSUPPORTED;
+  if (n < 1 || hidden < 1 || hidden > (1 << 20) || !factors || !ok_ptr(factors->A_v) || !ok_ptr(x) ||
+      !ok_ptr(W_o) || !ok_ptr(F_out) || !ok_ptr(workspace))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < kvlr_fit_joint_workspace_bytes(shape, n)) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t oz = round_up(static_cast<size_t>(n) * nl * sizeof(float));
+  const size_t ozz = oz + round_up(static_cast<size_t>(nl) * nl * sizeof(double));
+  const size_t ozx = ozz + round_up(static_cast<size_t>(nl) * nx * sizeof(double));
+  double* zz = reinterpret_cast<double*>(ws + oz);
+  double* zx = reinterpret_cast<double*>(ws + ozz);
+  float* Dm = reinterpret_cast<float*>(ws + ozx);
+  st = kvlr_fit_joint_moments(shape, factors, x, n, zz, zx, 0, workspace, ws_bytes, stream);
+  if (st != KVLR_OK) return st;
+  const hipStream_t s = as_stream(stream);
+  std::vector<double> hzz(static_cast<size_t>(nl) * nl), hzx(static_cast<size_t>(nl) * nx),
+      hD(static_cast<size_t>(nl) * nx);
+  hipError_t e = hipMemcpyAsync(hzz.data(), zz, hzz.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(hzx.data(), zx, hzx.size() * sizeof(double), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  if (kvlr::joint_solve(static_cast<int>(nl), static_cast<int>(nx), hzz.data(), hzx.data(), hD.data()) !=
+      kvlr::FitStatus::kOk)
+    return KVLR_ERR_NUMERICAL;
+  if (D_out) memcpy(D_out, hD.data(), hD.size() * sizeof(double));
+  std::vector<float> hDf(hD.size());
+  for (size_t i = 0; i < hD.size(); ++i) hDf[i] = static_cast<float>(hD[i]);
+  e = hipMemcpyAsync(Dm, hDf.data(), hDf.size() * sizeof(float), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_status(e);
+  st = kvlr_fold_joint_decoder(shape, W_o, hidden, Dm, F_out, stream);
+  if (st != KVLR_OK) return st;
+  return hip_status(hipStreamSynchronize(s));  // the host copy of D must outlive the upload
 }
 
 }  // extern "C"

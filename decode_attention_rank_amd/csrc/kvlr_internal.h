@@ -166,4 +166,28 @@ enum class FitStatus { kOk, kSingular, kNoConvergence };
 FitStatus fit_solve(const Dims& dm, const double* moments, double* A_v, double* A_k, double* W,
                     double* lam_v, double* lam_k);
 
+// Joint decoder fit: latent outputs Z = X A per head and the moments Z^T Z,
+// Z^T X (float64), then the fold F = W_o D^T of a decoder D.
+struct JointArgs {
+  Dims dm;
+  const void* A_v;  // [Hkv][D][RV] storage type
+  const float* x;   // [n][Hq][D] attention outputs
+  int n;
+  float* z;         // [n][Hq RV] workspace
+  double* zz;       // [Hq RV][Hq RV]
+  double* zx;       // [Hq RV][Hq D]
+  int accumulate;   // add onto zz, zx
+};
+hipError_t launch_joint_moments(const JointArgs& a, hipStream_t s);
+struct JointFoldArgs {
+  Dims dm;
+  const void* W_o;  // [hidden][Hq D] bf16
+  const float* Dm;  // [Hq RV][Hq D] decoder
+  void* F;          // [hidden][Hq RV] bf16
+  int hidden;
+};
+hipError_t launch_joint_fold(const JointFoldArgs& a, hipStream_t s);
+// Host: D = zz^-1 zx (row-major [nl][nx]); kSingular for a non-positive pivot.
+FitStatus joint_solve(int nl, int nx, const double* zz, const double* zx, double* D);
+
 }  // namespace kvlr

@@ -58,3 +58,34 @@ class FactorFit:
     def factors(self) -> dict:
         return {"A_v": self.A_v, "B_v": self.B_v, "A_k": self.A_k, "B_k": self.B_k,
                 "W_pred": self.W_pred}
+
+
+class JointFit:
+    """Device buffers for the joint decoder fit of one shape: the workspace
+    (latent outputs, float64 moments, the float32 decoder) and the folded
+    output weight F [hidden][H_q r_v] (storage type)."""
+
+    def __init__(self, wl: Workload, n: int, hidden: int, device="cuda"):
+        self.wl, self.n, self.hidden = wl, n, hidden
+        self.shape = fit_shape(wl)
+        nl, nx = wl.num_q_heads * wl.rank_v, wl.num_q_heads * wl.head_dim
+        self.ws_bytes = K.kvlr_fit_joint_workspace_bytes(self.shape, n)
+        if self.ws_bytes == 0:
+            raise ValueError("shape rejected by kvlr_fit_joint_workspace_bytes")
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.zz = torch.empty(nl, nl, dtype=torch.float64, device=device)
+        self.zx = torch.empty(nl, nx, dtype=torch.float64, device=device)
+        self.F = torch.empty(hidden, nl, dtype=torch.bfloat16, device=device)
+
+    def moments(self, factors, x, n, accumulate=0, stream=None):
+        K.kvlr_fit_joint_moments(self.shape, factors, x, n, self.zz, self.zx, accumulate,
+                                 self.workspace, self.ws_bytes, stream)
+
+    def solve(self):
+        """Host solve of the moments on the device (copied back first)."""
+        return K.kvlr_fit_joint_solve(self.shape, self.zz.cpu().numpy(), self.zx.cpu().numpy())
+
+    def fit(self, factors, x, W_o, want_D=False, stream=None):
+        """kvlr_fit_joint: moments, solve and fold into self.F (synchronous)."""
+        return K.kvlr_fit_joint(self.shape, factors, x, self.n, W_o, self.hidden, self.F,
+                                self.workspace, self.ws_bytes, want_D=want_D, stream=stream)

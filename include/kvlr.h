@@ -481,6 +481,70 @@ kvlr_status kvlr_fit_factors(const kvlr_shape* shape, const void* k, const void*
                              const kvlr_factor_buffers* out, double* lam_v, double* lam_k,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Joint fit of the value decoders across attention partitions (calibration,
+ * not decode). BasisKV English abstract: the low-rank factors are optimised
+ * jointly across the per-GPU attention partitions against the complete
+ * attention output, rather than fitting each partition on its own; method
+ * details (key design: the loss couples every GPU's attention partition;
+ * key innovation: value compression is tied to the output projection).
+ * The pages give no procedure; the reading implemented here keeps the value
+ * encoders A_v as fitted (the cache's latents exist before any query) and
+ * chooses the decoder of the complete attention output from the latents of
+ * every partition by least squares over calibration samples:
+ *   z_h = x_h . A_v[h / G]           latent output of query head h
+ *   D   = argmin sum_n |x_n - z_n D|^2 = (Z^T Z)^-1 Z^T X
+ *   F   = W_o . D^T                   the output projection seen from the
+ *                                     latents (as kvlr_fold_output_weights,
+ *                                     whose F is this with D = blockdiag(B_v))
+ * x_n = concat_h(x_h) [H_q * head_dim] is one sample's exact attention output
+ * (all query heads of all partitions), z_n [H_q * rank_v] its latents. For
+ * any W_o, F minimises sum_n |W_o x_n - F z_n|^2. Sizes: H_q * rank_v <=
+ * 4096 and H_q * head_dim <= 16384; bf16 or f32 storage (not FP8 latents);
+ * n should well exceed H_q * rank_v.
+ *   x        [n][num_q_heads][head_dim] float32 samples (device)
+ *   factors  A_v is read ([H_kv][head_dim][rank_v], storage type)
+ */
+size_t kvlr_fit_joint_workspace_bytes(const kvlr_shape* shape, int32_t n);
+
+/* The moments of n samples, accumulated on the GPU (stream-ordered):
+ *   zz  device [H_q rank_v][H_q rank_v] float64: Z^T Z
+ *   zx  device [H_q rank_v][H_q head_dim] float64: Z^T X
+ * accumulate = 1 adds onto zz, zx (streamed calibration), 0 overwrites.
+ * Z is formed in float32 on the matrix cores; the moments take float32 sums
+ * over runs of 256 samples and float64 sums of the runs. */
+kvlr_status kvlr_fit_joint_moments(const kvlr_shape* shape, const kvlr_factors* factors,
+                                   const float* x, int32_t n, double* zz, double* zx,
+                                   int32_t accumulate, void* workspace, size_t ws_bytes,
+                                   void* stream);
+
+/* Host only: D = zz^-1 zx in float64 (Cholesky, then the triangular solves
+ * for each of the H_q head_dim columns on up to 16 host threads).
+ *   zz, zx  host, as kvlr_fit_joint_moments writes them
+ *   D_out   host out [H_q rank_v][H_q head_dim] float64
+ * KVLR_ERR_NUMERICAL when a Cholesky pivot falls to 1e-12 of the largest
+ * diagonal entry (latents the samples do not determine). */
+kvlr_status kvlr_fit_joint_solve(const kvlr_shape* shape, const double* zz, const double* zx,
+                                 double* D_out);
+
+/* F = W_o . D^T on the GPU (bf16 storage only):
+ *   W_o    [hidden][H_q head_dim] bf16, rows are output features
+ *   D      [H_q rank_v][H_q head_dim] float32 (device)
+ *   F_out  out [hidden][H_q rank_v] bf16 (RNE of float32 sums of float32
+ *          products, summed in float64 over runs of 256)
+ * F_out is what kvlr_output_projection applies. */
+kvlr_status kvlr_fold_joint_decoder(const kvlr_shape* shape, const void* W_o, int32_t hidden,
+                                    const float* D, void* F_out, void* stream);
+
+/* The whole joint fit in one synchronous call: the moments into the
+ * workspace, a copy to the host, the solve, D rounded to float32 and folded
+ * into F_out. D_out (host, may be NULL) receives the float64 decoder. Uses
+ * host memory (about 3 (H_q rank_v)^2 + 3 H_q rank_v H_q head_dim doubles)
+ * and synchronises `stream`: for calibration, not the decode loop. */
+kvlr_status kvlr_fit_joint(const kvlr_shape* shape, const kvlr_factors* factors, const float* x,
+                           int32_t n, const void* W_o, int32_t hidden, void* F_out, double* D_out,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

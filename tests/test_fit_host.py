@@ -19,6 +19,7 @@ from decode_attention_rank_amd import _lib as K
 from decode_attention_rank_amd import synth
 from decode_attention_rank_amd.fit import fit_shape
 from decode_attention_rank_amd.workloads import DEFAULT_FIT_WORKLOAD, FIT_WORKLOADS
+import oracle as O
 from oracle import fit_factors
 
 
@@ -159,3 +160,46 @@ def test_choose_residual_ranks_cases_and_library(lib):
         lam = -np.sort(-rng.exponential(size=(4, 64)) * rng.uniform(0.05, 1, (4, 1)) ** 8, axis=1)
         assert K.kvlr_choose_residual_ranks(s, np.ascontiguousarray(lam), frac) == \
             choose_residual_ranks(lam, frac)
+
+
+# ----------------------------------------------------------------------------
+# Joint decoder fit: the library's host solve against the oracle's
+# least-squares fit on the samples (CPU only)
+# ----------------------------------------------------------------------------
+
+def _joint_case(seed, Hq, H_kv, d, r, n):
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((n, 8))
+    X = np.empty((n, Hq, d))
+    for h in range(Hq):
+        M = rng.standard_normal((8, d)) / np.sqrt(8)
+        X[:, h] = (s + 0.5 * rng.standard_normal((n, 8))) @ M
+    X += 0.05 * rng.standard_normal(X.shape)
+    A = np.stack([np.linalg.qr(rng.standard_normal((d, d)))[0][:, :r] for _ in range(H_kv)])
+    return X, A
+
+
+@pytest.mark.parametrize("Hq,H_kv,d,r,n", [(4, 2, 64, 16, 300), (8, 1, 128, 32, 700), (8, 8, 64, 16, 500)])
+def test_joint_solve_matches_the_oracle_least_squares(Hq, H_kv, d, r, n):
+    X, A = _joint_case(41, Hq, H_kv, d, r, n)
+    Z = O.latent_outputs(X, A, Hq // H_kv)
+    zz = Z.T @ Z
+    zx = Z.T @ X.reshape(n, -1)
+    shape = K.make_shape(num_q_heads=Hq, num_kv_heads=H_kv, head_dim=d, page_size=64, rank_v=r,
+                         rank_k=16, dtype=K.KVLR_DTYPE_BF16, key_mode=K.KVLR_KEYS_EXACT,
+                         num_phys_pages=1)
+    D = K.kvlr_fit_joint_solve(shape, zz, zx)
+    ref = O.fit_joint_decoder(X, A, Hq // H_kv)
+    cond = np.linalg.cond(zz)
+    assert np.abs(D - ref).max() <= 1e-13 * cond * np.abs(ref).max() + 1e-12
+
+
+def test_joint_solve_rejects_undetermined_latents():
+    X, A = _joint_case(42, 4, 2, 64, 16, 40)   # 40 samples, 64 latents
+    Z = O.latent_outputs(X, A, 2)
+    shape = K.make_shape(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=64, rank_v=16,
+                         rank_k=16, dtype=K.KVLR_DTYPE_BF16, key_mode=K.KVLR_KEYS_EXACT,
+                         num_phys_pages=1)
+    with pytest.raises(K.KvlrError) as e:
+        K.kvlr_fit_joint_solve(shape, Z.T @ Z, Z.T @ X.reshape(40, -1))
+    assert e.value.status == K.KVLR_ERR_NUMERICAL
