@@ -78,6 +78,18 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def measured_counters(kernel: str, workload: str):
+    """MFMA and VALU busy shares from a committed counter summary, if current."""
+    p = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return {"mfma_busy_pct": rec.get("mfma_busy_pct"), "valu_busy_pct": rec.get("valu_busy_pct")}
+
+
 def pct(xs, q):
     """q-th percentile (0..100) of xs by linear interpolation."""
     s = sorted(xs)
@@ -180,6 +192,8 @@ def measure(sess, steps: int, warmup: int, graph: bool, fused: bool, flush) -> d
             gbps = kb[n] / (us * 1e-6) / 1e9
             rec.update(algo_bytes=kb[n], achieved_gbps=round(gbps, 1),
                        frac=round(gbps / HBM_PEAK_GBPS, 4))
+        cnt = measured_counters(n, wl.name)
+        rec.update(cnt if cnt else {"mfma_busy_pct": None, "valu_busy_pct": None})
         kernels[n] = rec
     if g is not None:
         # leave the buffers as a replay of the step leaves them

@@ -38,7 +38,7 @@ EXPORTED = (
     "kvlr_fit_solve", "kvlr_fit_factors", "kvlr_choose_residual_ranks",
     "kvlr_decode_attn_upproject_noalloc", "kvlr_noalloc_scratch_bytes",
     "kvlr_fit_joint_workspace_bytes", "kvlr_fit_joint_moments", "kvlr_fit_joint_solve",
-    "kvlr_fold_joint_decoder", "kvlr_fit_joint",
+    "kvlr_fold_joint_decoder", "kvlr_fit_joint", "kvlr_residual_prep_bytes", "kvlr_prepare_residual",
 )
 
 
@@ -60,7 +60,7 @@ class kvlr_cache(ctypes.Structure):
 
 
 class kvlr_factors(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("A_v", "B_v", "A_k", "B_k", "W_pred")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("A_v", "B_v", "A_k", "B_k", "W_pred", "residual_prep")]
 
 
 class kvlr_factor_buffers(ctypes.Structure):
@@ -90,6 +90,9 @@ _SIG = {
                                             ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I, _P, _P, _P,
                                             _I, ctypes.c_float, _P, _P, _P, _I, _P], _I),
     "kvlr_noalloc_scratch_bytes": ([], ctypes.c_size_t),
+    "kvlr_residual_prep_bytes": ([ctypes.POINTER(kvlr_shape)], ctypes.c_size_t),
+    "kvlr_prepare_residual": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P,
+                               ctypes.c_size_t, _P], _I),
     "kvlr_fit_joint_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I], ctypes.c_size_t),
     "kvlr_fit_joint_moments": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P, _I, _P,
                                 _P, _I, _P, ctypes.c_size_t, _P], _I),
@@ -182,8 +185,18 @@ def make_cache(v_lat=None, k_lat=None, k_exact=None, k_lat_ranks=None) -> kvlr_c
     return c
 
 
-def make_factors(A_v=None, B_v=None, A_k=None, B_k=None, W_pred=None) -> kvlr_factors:
-    return kvlr_factors(_ptr(A_v), _ptr(B_v), _ptr(A_k), _ptr(B_k), _ptr(W_pred))
+def make_factors(A_v=None, B_v=None, A_k=None, B_k=None, W_pred=None,
+                 residual_prep=None) -> kvlr_factors:
+    return kvlr_factors(_ptr(A_v), _ptr(B_v), _ptr(A_k), _ptr(B_k), _ptr(W_pred), _ptr(residual_prep))
+
+
+def kvlr_residual_prep_bytes(shape: kvlr_shape) -> int:
+    return lib().kvlr_residual_prep_bytes(ctypes.byref(shape))
+
+
+def kvlr_prepare_residual(shape, factors, prep, prep_bytes, stream=None):
+    _check("kvlr_prepare_residual", lib().kvlr_prepare_residual(
+        ctypes.byref(shape), ctypes.byref(factors), _ptr(prep), prep_bytes, _stream(stream)))
 
 
 def kvlr_version() -> int:

@@ -1,15 +1,21 @@
 """Build libkvlr.so for gfx950 with hipcc, in-tree.
 
     python -m decode_attention_rank_amd.build [--jobs N]
+    # a variant with compile-time switches, e.g. vector-ALU scoring:
+    python -m decode_attention_rank_amd.build -D KVLR_ROUTE_MFMA=0 -D KVLR_ATTN_MFMA=0 \
+        --out /tmp/libkvlr_valu.so
 
 Each kernel source compiles to an object under _build/ in parallel; the
-objects link into decode_attention_rank_amd/libkvlr.so.
+objects link into decode_attention_rank_amd/libkvlr.so. A variant's objects go
+to a folder of their own under _build/ and its library to --out; the binding
+loads it when KVLR_LIBRARY names it.
 """
 
 from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -43,9 +49,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the kvlr library needs ROCm's hipcc")
 
 
-def _compile(src: str) -> tuple[str, float, str]:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> tuple[str, float, str]:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
@@ -56,34 +62,46 @@ def _compile(src: str) -> tuple[str, float, str]:
     return obj, time.time() - t0, warn
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = True, defines: tuple = (),
+          out: str | None = None) -> str:
+    defines = tuple(defines)
+    build_dir = BUILD
+    if defines:
+        tag = hashlib.sha256(" ".join(defines).encode()).hexdigest()[:10]
+        build_dir = os.path.join(BUILD, f"variant_{tag}")
+    lib_path = out or LIB
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     objs = []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        for obj, dt, warn in ex.map(_compile, SOURCES):
+        for obj, dt, warn in ex.map(lambda s: _compile(s, build_dir, defines), SOURCES):
             objs.append(obj)
             if verbose:
                 print(f"  compiled {os.path.basename(obj)} in {dt:.1f}s", flush=True)
                 if warn.strip():
                     print(warn, flush=True)
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{p.stdout}\n{p.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"  linked {LIB}", flush=True)
-    return LIB
+        print(f"  linked {lib_path}" + (f" with {' '.join(defines)}" if defines else ""), flush=True)
+    return lib_path
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="compile-time switch NAME=VALUE for every source (a variant build)")
+    ap.add_argument("--out", default=None, help="library path (default: the package's libkvlr.so)")
     args = ap.parse_args()
+    if args.defines and not args.out:
+        ap.error("a variant build (-D) needs --out, so the package's library stays the default one")
     try:
-        build(args.jobs)
+        build(args.jobs, defines=args.defines, out=args.out)
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

@@ -12,9 +12,12 @@
 // accumulation. The routed residual is evaluated as
 //   c = K A_k + v (-(W_pred A_k)),
 // an exact reassociation of the definition: the r_v x r_k matrix
-// W_pred A_k is formed once per workgroup on the matrix cores, negated and,
-// for bf16, split into a high and a low bf16 part so the product with the
-// stored (bf16) latent v keeps about 16 significant bits of the matrix.
+// W_pred A_k is formed on the matrix cores, negated and, for bf16, split
+// into a high and a low bf16 part so the product with the stored (bf16)
+// latent v keeps about 16 significant bits of the matrix. It depends on the
+// factors only: a preparation launch (one workgroup per KV head, the same
+// code) can write it once in the B-operand layout the encode reads, and the
+// encode then copies it instead of forming it in every workgroup.
 //
 // Work split: grid (KV head, token-tile groups). A workgroup stages the
 // factor fragments of its head in LDS once, then loops over 64-token tiles,
@@ -161,6 +164,22 @@ struct QTiles {
   int batch, Hq, G, row_tiles, col_tiles, qy;
 };
 
+// The prepared residual operand -(W_pred A_k): per KV head its high parts,
+// then (bf16) its low parts, each [k-step][n-tile][lane][KPL] as in EncSmem.
+// out set: form it and write it (no tokens); in set: copy it, do not form it.
+struct MPrep {
+  const uint8_t* in;
+  uint8_t* out;
+};
+
+template <class S, int RV, int RK>
+constexpr size_t mprep_head_bytes() {
+  using MM = Mma<S>;
+  constexpr int KSV = (RV + MM::KSTEP - 1) / MM::KSTEP;
+  return static_cast<size_t>(KSV) * (RK / 16) * kWave * MM::KPL * sizeof(typename MM::E) *
+         (MM::KPL > 1 ? 2 : 1);
+}
+
 template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 __global__ __launch_bounds__(kThreads) void encode_kernel(
     const uint8_t* __restrict__ A_v, const uint8_t* __restrict__ A_k,
@@ -168,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     const uint8_t* __restrict__ v_new, const int32_t* __restrict__ cu_new,
     const int32_t* __restrict__ lens_before, const int32_t* __restrict__ page_table,
     uint8_t* __restrict__ v_lat, uint8_t* __restrict__ k_lat, uint8_t* __restrict__ k_exact,
-    int Hkv, int P, int log2P, int max_pages, int batch, int total_new, KLayout kl, QTiles qt) {
+    int Hkv, int P, int log2P, int max_pages, int batch, int total_new, KLayout kl, QTiles qt,
+    MPrep mp) {
   using MM = Mma<S>;
   using SM = EncSmem<S, LS, D, RV, RK, ROUTED>;
   using LT = Lat<S, LS>;
@@ -183,14 +203,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   extern __shared__ int s_seq[];  // cu_new[0..batch], then lens_before[0..batch)
 
   if (static_cast<int>(blockIdx.y) < qt.qy) {  // a workgroup of query-projection tiles
-    const int t = (static_cast<int>(blockIdx.y) * static_cast<int>(gridDim.x) +
-                   static_cast<int>(blockIdx.x)) * kWaves + static_cast<int>(threadIdx.x) / kWave;
-    const int per_head = qt.row_tiles * qt.col_tiles;
-    if (t < per_head * Hkv) {
-      const int hg = t / per_head, rem = t - hg * per_head;
-      const int ct = rem / qt.row_tiles;
+    // grid column x holds KV head x's tiles, as it holds that head's encode
+    // workgroups: workgroups go to the XCDs round robin by linear id, so with
+    // H_kv = 8 columns every workgroup of a head shares one XCD's L2, and the
+    // head's query rows and factor columns are fetched from memory once
+    const int hg = blockIdx.x;
+    const int t = static_cast<int>(blockIdx.y) * kWaves + static_cast<int>(threadIdx.x) / kWave;
+    if (t < qt.row_tiles * qt.col_tiles) {
+      const int ct = t / qt.row_tiles;
       qproj_tile<S, D>(W_pred, qt.B_k, qt.q, qt.q_proj, qt.batch, qt.Hq, qt.G, RV, RK, ROUTED ? 1 : 0,
-                       rem - ct * qt.row_tiles, ct, hg);
+                       t - ct * qt.row_tiles, ct, hg);
     }
     return;
   }
@@ -223,13 +245,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) kf[ks] = MM::gmem(k_new + row_off + (ks * KSTEP + KPL * kq) * EB);
   };
-  // this workgroup's first tile, and the W_pred rows of M = W_pred A_k, are
-  // requested before the set-up below
-  frag_t vf[KSD], kf[KSD];
-  load_tile(tile0, vf, kf);
   constexpr int MT = ROUTED ? (NTV * NTK + kWaves - 1) / kWaves : 0;  // M tiles per wave
   frag_t wa[MT > 0 ? MT : 1][KSD];
-  if constexpr (ROUTED) {
+  // the W_pred rows of this wave's tiles of M = W_pred A_k
+  auto load_w = [&] {
     const uint8_t* Wg = W_pred + static_cast<size_t>(g) * RV * D * EB;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -240,7 +259,37 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       for (int ks = 0; ks < KSD; ++ks)
         wa[m][ks] = MM::gmem(Wg + (static_cast<size_t>(row) * D + ks * KSTEP + KPL * (lane >> 4)) * EB);
     }
-  }
+  };
+  // M's tiles on the matrix cores (A_k's fragments staged in LDS), then
+  // -M split into the high and low B-operand fragments of the residual
+  // products; ends with the workgroup synchronised
+  auto form_m = [&] {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int ti = wave + m * kWaves;
+      if (ti >= NTV * NTK) continue;
+      const int mt = ti / NTK, nt = ti - mt * NTK;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) acc = MM::mma(wa[m][ks], MM::lds(&sm.ak[ks][nt][lane][0]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.u.mstage[mt * 16 + 4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[i];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < KSV * NTK * kWave * KPL; idx += kThreads) {
+      const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTK;
+      const int ks = idx / (KPL * kWave * NTK);
+      const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
+      const float mv = (k < RV) ? -sm.u.mstage[k][n] : 0.f;
+      const E hi = MM::store(mv);
+      sm.mhi[ks][nt][l][e] = hi;
+      if constexpr (KPL > 1) sm.mlo[ks][nt][l][e] = MM::store(mv - MM::value(hi));
+    }
+    __syncthreads();
+  };
+  constexpr size_t kMHalf = static_cast<size_t>(KSV) * NTK * kWave * KPL * sizeof(E);
+  constexpr size_t kMHead = mprep_head_bytes<S, RV, RK>();
+  static_assert(kMHead == kMHalf * (KPL > 1 ? 2 : 1), "prepared operand size");
 
   // ---- stage B fragments: element (k, n) with k = ks*KSTEP + KPL*(l/16) + e,
   // n = nt*16 + l%16; each thread reads CH consecutive n of one row k
@@ -273,8 +322,42 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       }
     }
   };
+  if constexpr (ROUTED) {
+    if (mp.out) {  // preparation launch: form -M once and write it out
+      load_w();
+      stage(Ak, &sm.ak[0][0][0][0], std::integral_constant<int, RK>{});
+      __syncthreads();
+      form_m();
+      uint8_t* dst = mp.out + static_cast<size_t>(g) * kMHead;
+      for (size_t o = static_cast<size_t>(tid) * 16; o < kMHalf; o += kThreads * 16) {
+        store16(dst + o, *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(&sm.mhi[0][0][0][0]) + o));
+        if constexpr (KPL > 1)
+          store16(dst + kMHalf + o,
+                  *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(&sm.mlo[0][0][0][0]) + o));
+      }
+      return;
+    }
+  }
+  // this workgroup's first tile, and the W_pred rows of M (unless it comes
+  // prepared), are requested before the set-up below
+  frag_t vf[KSD], kf[KSD];
+  load_tile(tile0, vf, kf);
+  if constexpr (ROUTED) {
+    if (!mp.in) load_w();
+  }
   stage(Av, &sm.av[0][0][0][0], std::integral_constant<int, RV>{});
   stage(Ak, &sm.ak[0][0][0][0], std::integral_constant<int, RK>{});
+  if constexpr (ROUTED) {
+    if (mp.in) {  // the prepared -M, copied into its LDS fragments
+      const uint8_t* src = mp.in + static_cast<size_t>(g) * kMHead;
+      for (size_t o = static_cast<size_t>(tid) * 16; o < kMHalf; o += kThreads * 16) {
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&sm.mhi[0][0][0][0]) + o) = load16(src + o);
+        if constexpr (KPL > 1)
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&sm.mlo[0][0][0][0]) + o) =
+              load16(src + kMHalf + o);
+      }
+    }
+  }
   for (int b = tid; b <= batch; b += kThreads) s_seq[b] = cu_new[b];
   for (int b = tid; b < batch; b += kThreads) s_seq[batch + 1 + b] = lens_before[b];
   __syncthreads();
@@ -300,29 +383,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   const int phys0 = *locate(tile0, slot0);
 
   if constexpr (ROUTED) {
-    // M = W_pred A_k  [RV x RK], 16x16 tiles spread over the waves
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int ti = wave + m * kWaves;
-      if (ti >= NTV * NTK) continue;
-      const int mt = ti / NTK, nt = ti - mt * NTK;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KSD; ++ks) acc = MM::mma(wa[m][ks], MM::lds(&sm.ak[ks][nt][lane][0]), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.u.mstage[mt * 16 + 4 * (lane >> 4) + i][nt * 16 + (lane & 15)] = acc[i];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < KSV * NTK * kWave * KPL; idx += kThreads) {
-      const int e = idx % KPL, l = (idx / KPL) % kWave, nt = (idx / (KPL * kWave)) % NTK;
-      const int ks = idx / (KPL * kWave * NTK);
-      const int k = ks * KSTEP + KPL * (l >> 4) + e, n = nt * 16 + (l & 15);
-      const float mv = (k < RV) ? -sm.u.mstage[k][n] : 0.f;
-      const E hi = MM::store(mv);
-      sm.mhi[ks][nt][l][e] = hi;
-      if constexpr (KPL > 1) sm.mlo[ks][nt][l][e] = MM::store(mv - MM::value(hi));
-    }
-    __syncthreads();
+    if (!mp.in) form_m();  // M = W_pred A_k [RV x RK], 16x16 tiles spread over the waves
   }
 
   // v = V A_v and the residual (routed) or key latent (dense), rounded into
@@ -504,8 +565,7 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
     qt.G = a.dm.G;
     qt.row_tiles = (a.batch * a.dm.G + 15) / 16;
     qt.col_tiles = ((ROUTED ? RV : 0) + RK) / 16;
-    const int tiles = qt.row_tiles * qt.col_tiles * a.dm.Hkv;
-    qt.qy = (tiles + kWaves * a.dm.Hkv - 1) / (kWaves * a.dm.Hkv);
+    qt.qy = (qt.row_tiles * qt.col_tiles + kWaves - 1) / kWaves;  // rows of tiles per head
   }
   if (per_head + qt.qy == 0) return hipSuccess;
   dim3 grid(a.dm.Hkv, per_head + qt.qy);
@@ -515,55 +575,102 @@ hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
                      static_cast<const uint8_t*>(a.v_new), a.cu_new, a.lens_before, a.page_table,
                      static_cast<uint8_t*>(a.v_lat), static_cast<uint8_t*>(a.k_lat),
                      static_cast<uint8_t*>(a.k_exact), a.dm.Hkv, a.dm.P, log2P, a.max_pages,
-                     a.batch, a.total_new, a.kl, qt);
+                     a.batch, a.total_new, a.kl, qt,
+                     MPrep{ROUTED ? static_cast<const uint8_t*>(a.m_prep) : nullptr, nullptr});
   return hipGetLastError();
 }
 
+// The preparation launch: one workgroup per KV head writes its -M.
+template <class S, class LS, int D, int RV, int RK, bool ROUTED>
+hipError_t launch_prep_t(const EncodeArgs& a, void* out, hipStream_t s) {
+  if constexpr (!ROUTED) {
+    return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((encode_kernel<S, LS, D, RV, RK, ROUTED>), dim3(a.dm.Hkv, 1), dim3(kThreads),
+                       sizeof(int), s, static_cast<const uint8_t*>(a.A_v),
+                       static_cast<const uint8_t*>(a.A_k), static_cast<const uint8_t*>(a.W_pred),
+                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       a.dm.Hkv, a.dm.P, 0, 1, 0, 0, a.kl, QTiles{},
+                       MPrep{nullptr, static_cast<uint8_t*>(out)});
+    return hipGetLastError();
+  }
+}
+
+// What the dispatch below does per instance: launch the encode, launch the
+// preparation, or report the prepared operand's bytes.
+struct EncodeOp {
+  enum Kind { kEncode, kPrep, kBytes } kind;
+  void* out;
+  size_t* bytes;
+};
+
 template <class S, class LS, int D, int RV, int RK>
-hipError_t by_mode(const EncodeArgs& a, hipStream_t s) {
+hipError_t by_mode(const EncodeArgs& a, const EncodeOp& op, hipStream_t s) {
+  if (op.kind == EncodeOp::kBytes) {
+    *op.bytes = a.dm.exact ? mprep_head_bytes<S, RV, RK>() * a.dm.Hkv : 0;
+    return hipSuccess;
+  }
+  if (op.kind == EncodeOp::kPrep)
+    return a.dm.exact ? launch_prep_t<S, LS, D, RV, RK, true>(a, op.out, s) : hipErrorInvalidValue;
   return a.dm.exact ? launch_t<S, LS, D, RV, RK, true>(a, s) : launch_t<S, LS, D, RV, RK, false>(a, s);
 }
 
 template <class S, class LS, int D, int RV>
-hipError_t by_rk(const EncodeArgs& a, hipStream_t s) {
+hipError_t by_rk(const EncodeArgs& a, const EncodeOp& op, hipStream_t s) {
   switch (a.dm.RK) {
-    case 16: return by_mode<S, LS, D, RV, 16>(a, s);
-    case 32: return by_mode<S, LS, D, RV, 32>(a, s);
-    case 64: return by_mode<S, LS, D, RV, 64>(a, s);
+    case 16: return by_mode<S, LS, D, RV, 16>(a, op, s);
+    case 32: return by_mode<S, LS, D, RV, 32>(a, op, s);
+    case 64: return by_mode<S, LS, D, RV, 64>(a, op, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <class S, class LS, int D>
-hipError_t by_rv(const EncodeArgs& a, hipStream_t s) {
+hipError_t by_rv(const EncodeArgs& a, const EncodeOp& op, hipStream_t s) {
   switch (a.dm.RV) {
-    case 16: return by_rk<S, LS, D, 16>(a, s);
-    case 32: return by_rk<S, LS, D, 32>(a, s);
-    case 64: return by_rk<S, LS, D, 64>(a, s);
+    case 16: return by_rk<S, LS, D, 16>(a, op, s);
+    case 32: return by_rk<S, LS, D, 32>(a, op, s);
+    case 64: return by_rk<S, LS, D, 64>(a, op, s);
     case 128:
       // full-width values: bf16 storage only (the f32 tiles would not fit in LDS)
-      if constexpr (D == 128 && S::CH == 8 && LS::CB == 16) return by_rk<S, LS, D, 128>(a, s);
+      if constexpr (D == 128 && S::CH == 8 && LS::CB == 16) return by_rk<S, LS, D, 128>(a, op, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
 template <class S, class LS>
-hipError_t by_d(const EncodeArgs& a, hipStream_t s) {
+hipError_t by_d(const EncodeArgs& a, const EncodeOp& op, hipStream_t s) {
   switch (a.dm.D) {
-    case 64: return by_rv<S, LS, 64>(a, s);
-    case 128: return by_rv<S, LS, 128>(a, s);
+    case 64: return by_rv<S, LS, 64>(a, op, s);
+    case 128: return by_rv<S, LS, 128>(a, op, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(const EncodeArgs& a, const EncodeOp& op, hipStream_t s) {
+  if (a.dm.lat == 2) return by_d<BF16, FP8>(a, op, s);
+  if (a.dm.dtype == 0) return by_d<BF16, BF16>(a, op, s);
+  return by_d<F32, F32>(a, op, s);
 }
 
 }  // namespace
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
   if (a.batch == 0 || (a.total_new == 0 && !a.q)) return hipSuccess;
-  if (a.dm.lat == 2) return by_d<BF16, FP8>(a, s);
-  if (a.dm.dtype == 0) return by_d<BF16, BF16>(a, s);
-  return by_d<F32, F32>(a, s);
+  return dispatch(a, EncodeOp{EncodeOp::kEncode, nullptr, nullptr}, s);
+}
+
+hipError_t launch_encode_prep(const EncodeArgs& a, void* out, hipStream_t s) {
+  return dispatch(a, EncodeOp{EncodeOp::kPrep, out, nullptr}, s);
+}
+
+size_t encode_prep_bytes(const Dims& dm) {
+  EncodeArgs a{};
+  a.dm = dm;
+  size_t bytes = 0;
+  if (dispatch(a, EncodeOp{EncodeOp::kBytes, nullptr, &bytes}, nullptr) != hipSuccess) return 0;
+  return bytes;
 }
 
 }  // namespace kvlr

@@ -224,12 +224,15 @@ static kvlr_status encode_args(const Dims& dm, const kvlr_factors* factors, cons
       !ok_ptr(seq_lens_before) || !ok_ptr(page_table))
     return KVLR_ERR_INVALID_ARGUMENT;
   if (dm.exact && (!ok_ptr(factors->W_pred) || !ok_ptr(cache->k_exact))) return KVLR_ERR_INVALID_ARGUMENT;
+  if (dm.exact && factors->residual_prep && !aligned16(factors->residual_prep))
+    return KVLR_ERR_INVALID_ARGUMENT;
   const kvlr_status st = residual_layout(dm, cache, &a->kl);
   if (st != KVLR_OK) return st;
   a->dm = dm;
   a->A_v = factors->A_v;
   a->A_k = factors->A_k;
   a->W_pred = factors->W_pred;
+  a->m_prep = dm.exact ? factors->residual_prep : nullptr;
   a->k_new = k_new;
   a->v_new = v_new;
   a->cu_new = cu_new;
@@ -292,6 +295,30 @@ kvlr_status kvlr_append_encode_project(const kvlr_shape* shape, const kvlr_facto
   a.q = q;
   a.q_proj = q_proj;
   return hip_status(kvlr::launch_encode(a, as_stream(stream)));
+}
+
+size_t kvlr_residual_prep_bytes(const kvlr_shape* shape) {
+  Dims dm;
+  if (check_shape(shape, &dm) != KVLR_OK || !dm.exact) return 0;
+  return kvlr::encode_prep_bytes(dm);
+}
+
+kvlr_status kvlr_prepare_residual(const kvlr_shape* shape, const kvlr_factors* factors, void* prep,
+                                  size_t prep_bytes, void* stream) {
+  Dims dm;
+  const kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (!factors || !dm.exact || !ok_ptr(factors->A_k) || !ok_ptr(factors->W_pred) || !ok_ptr(prep))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  const size_t need = kvlr::encode_prep_bytes(dm);
+  if (need == 0) return KVLR_ERR_UNSUPPORTED;
+  if (prep_bytes < need) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  kvlr::EncodeArgs a{};
+  a.dm = dm;
+  a.A_v = factors->A_v;
+  a.A_k = factors->A_k;
+  a.W_pred = factors->W_pred;
+  return hip_status(kvlr::launch_encode_prep(a, prep, as_stream(stream)));
 }
 
 kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* factors,

@@ -137,8 +137,15 @@ struct EncodeArgs {
   const void* B_k;      // [Hkv][RK][D]
   const float* q;       // [B][Hq][D]
   float* q_proj;        // [B][Hq][width]
+  // optional (exact keys): -W_pred A_k prepared by launch_encode_prep
+  const void* m_prep;
 };
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+// Writes -W_pred A_k per KV head in the encode's operand layout (exact keys;
+// reads a.dm, a.A_k, a.W_pred, a.kl); encode_prep_bytes: its size, 0 if the
+// shape has none or is not supported.
+hipError_t launch_encode_prep(const EncodeArgs& a, void* out, hipStream_t s);
+size_t encode_prep_bytes(const Dims& dm);
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 

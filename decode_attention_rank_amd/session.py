@@ -31,7 +31,7 @@ def kvlr_dtype(wl: Workload) -> int:
 class DecodeSession:
     def __init__(self, wl: Workload, device="cuda", *, seq_lens=None, append_per_seq=None,
                  spare_pages: int = 0, tail_fill: float = 0.0, stage_prefix: bool = True,
-                 page_table=None, num_phys=None, k_pages=None):
+                 page_table=None, num_phys=None, k_pages=None, residual_prep: bool = True):
         self.wl = wl
         self.device = torch.device(device)
         self.tail_fill = tail_fill
@@ -61,7 +61,14 @@ class DecodeSession:
 
         # factors, queries
         self.factors = synth.make_factors(wl, dev)
-        self.kfactors = K.make_factors(**self.factors)
+        self.shape_prep_bytes = K.kvlr_residual_prep_bytes(self.shape)
+        self.residual_prep = None
+        if residual_prep and self.shape_prep_bytes:
+            # the encode's -(W_pred A_k), formed once for these factors
+            self.residual_prep = torch.empty(self.shape_prep_bytes, dtype=torch.uint8, device=dev)
+            K.kvlr_prepare_residual(self.shape, K.make_factors(**self.factors), self.residual_prep,
+                                    self.shape_prep_bytes)
+        self.kfactors = K.make_factors(**self.factors, residual_prep=self.residual_prep)
         self.q = synth.make_queries(wl, dev)
         self.Qv, self.Qk = synth.bases(wl)
 
@@ -328,17 +335,33 @@ class DecodeSession:
             return sum(self.seq_lens) * wl.num_kv_heads * (key + wl.rank_v * lb)
         tot = 0
         P = wl.page_size
-        for L in self.seq_lens:
+        for b, L in enumerate(self.seq_lens):
             N = -(-L // P)
-            k = 0 if N == 0 else min(N, max(1, -(-(N * wl.topk_num) // wl.topk_den)))
+            if self.k_pages_cpu is not None:
+                k = min(N, max(self.k_pages_cpu[b], 0))
+            else:
+                k = 0 if N == 0 else min(N, max(1, -(-(N * wl.topk_num) // wl.topk_den)))
             tot += k * P  # upper bound for a ragged last page; exact when pages are full
         return tot * wl.num_kv_heads * (wl.head_dim * eb + wl.rank_v * lb)
 
-    def append_bytes(self) -> int:
+    def append_bytes(self, project: bool = True) -> int:
+        """Algorithmic bytes of the append launch: the new keys and values
+        read, their latents (and original keys) written, the factors read
+        once (A_v, A_k and, with a residual, W_pred A_k); with the query
+        projection in the same launch also the queries and [W_pred; B_k]
+        read and the query images written."""
         wl = self.wl
         eb = torch.empty(0, dtype=self.dtype).element_size()
         lb = torch.empty(0, dtype=self.lat_dtype).element_size()
-        read = self.total_new * wl.num_kv_heads * 2 * wl.head_dim * eb
-        lat = sum(wl.rank_v + wl.k_rank(g) for g in range(wl.num_kv_heads)) * lb
-        write = self.total_new * (lat + wl.num_kv_heads * (wl.head_dim * eb if wl.exact else 0))
-        return read + write
+        H, d, rv, rk = wl.num_kv_heads, wl.head_dim, wl.rank_v, wl.rank_k
+        read = self.total_new * H * 2 * d * eb
+        lat = sum(rv + wl.k_rank(g) for g in range(H)) * lb
+        write = self.total_new * (lat + H * (d * eb if wl.exact else 0))
+        weights = H * (d * rv + d * rk + (rv * rk if wl.exact else 0)) * eb
+        total = read + write + weights
+        if project:
+            width = self.qp_width
+            total += wl.batch * wl.num_q_heads * d * 4           # queries
+            total += H * width * d * eb                          # [W_pred; B_k]
+            total += wl.batch * wl.num_q_heads * width * 4       # query images
+        return total

@@ -1,4 +1,5 @@
-"""Measured HBM traffic of one kernel from rocprofv3 counter runs.
+"""Measured HBM traffic and instruction counters of one kernel from rocprofv3
+counter runs.
 
     # a copy-shaped kernel of known size, to scale the counters
     python -m decode_attention_rank_amd.traffic copy --mib 1024 --reps 4
@@ -6,6 +7,10 @@
     python -m decode_attention_rank_amd.traffic summarize --kernel route_kernel \
         --workload llama3-8b-routed-32k --fetch DIR --write DIR \
         --copy-fetch DIR --copy-write DIR --copy-mib 1024 --algo-bytes N --out FILE
+
+    # after one run with the shader-sequencer counters below (SQ_COUNTERS):
+    python -m decode_attention_rank_amd.traffic counters --kernel route_kernel \
+        --workload llama3-8b-routed-32k --dir DIR [--build-tag valu] --out FILE
 
 FETCH_SIZE and WRITE_SIZE are the L2's reads from and writes to memory, in
 KiB per dispatch. The copy (y = -x over float32, each byte read once and
@@ -32,7 +37,16 @@ SOURCES = {
     "encode_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_encode.hip"),
     "moments_mfma_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_fit.hip"),
 }
+SOURCES["merge_kernel"] = SOURCES["attn_kernel"]
 COPY_KERNEL_HINT = "neg_kernel"
+
+# one rocprofv3 pass: eight shader-sequencer counters and the GPU-active clock
+SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+               "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+# MI355X: 256 compute units of 4 SIMDs each, in 8 XCDs (one GRBM_GUI_ACTIVE
+# instance per XCD; rocprofv3's per-dispatch value is their sum)
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 
 def source_hash(path: str) -> str:
@@ -113,6 +127,30 @@ def summarize(a) -> dict:
     return rec
 
 
+def counters(a) -> dict:
+    """Median per dispatch of each SQ_COUNTERS value, and the derived shares
+    rocprofv3 defines: MfmaUtil = MFMA busy cycles over (GPU-active cycles x
+    SIMDs), VALUBusy = VALU-active wave cycles over (GPU-active cycles x CUs)."""
+    med = {c: statistics.median(per_dispatch(a.dir, c, a.kernel)) for c in SQ_COUNTERS}
+    n = len(per_dispatch(a.dir, "SQ_WAVES", a.kernel))
+    gui = med["GRBM_GUI_ACTIVE"] / XCD_NUM  # cycles of one XCD
+    rec = {
+        "kernel": a.kernel, "workload": a.workload, "build": a.build_tag, "dispatches": n,
+        "median_per_dispatch": {c: med[c] for c in SQ_COUNTERS},
+        "gpu_active_cycles": round(gui, 1),
+        "mfma_busy_pct": round(100.0 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM), 3)
+        if gui else None,
+        "valu_busy_pct": round(100.0 * med["SQ_ACTIVE_INST_VALU"] / CU_NUM / gui, 3) if gui else None,
+        "mfma_flop": med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 + med["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512,
+        "valu_insts_per_wave": round(med["SQ_INSTS_VALU"] / med["SQ_WAVES"], 1)
+        if med["SQ_WAVES"] else None,
+        "mfma_insts_per_wave": round(med["SQ_INSTS_MFMA"] / med["SQ_WAVES"], 1)
+        if med["SQ_WAVES"] else None,
+        "source_sha256_16": source_hash(SOURCES[a.kernel]),
+    }
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -129,6 +167,12 @@ def main(argv=None):
     s.add_argument("--copy-mib", type=int, default=1024)
     s.add_argument("--algo-bytes", type=int, required=True)
     s.add_argument("--out", required=True)
+    q = sub.add_parser("counters")
+    q.add_argument("--kernel", required=True, choices=sorted(SOURCES))
+    q.add_argument("--workload", required=True)
+    q.add_argument("--dir", required=True)
+    q.add_argument("--build-tag", default="default")
+    q.add_argument("--out", required=True)
     t = sub.add_parser("table")
     t.add_argument("--dir", required=True)
     t.add_argument("--counter", required=True)
@@ -141,7 +185,7 @@ def main(argv=None):
         for k, n, v in table(a.dir, a.counter, a.name):
             print(f"{a.counter}\t{n}\t{v:.1f}\t{k}")
         return
-    rec = summarize(a)
+    rec = summarize(a) if a.cmd == "summarize" else counters(a)
     with open(a.out, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")

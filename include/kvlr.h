@@ -140,6 +140,12 @@ typedef struct kvlr_factors {
   const void* A_k;
   const void* B_k;
   const void* W_pred;     /* KVLR_KEYS_EXACT only, else NULL */
+  /* Optional, KVLR_KEYS_EXACT only: the encode's residual operand written by
+   * kvlr_prepare_residual from THESE A_k and W_pred (device, 16-byte
+   * aligned), or NULL to have every encode workgroup form it. A stale one
+   * (factors changed since) gives wrong residual latents: the caller keeps
+   * the two in step. Ignored with KVLR_KEYS_LATENT. */
+  const void* residual_prep;
 } kvlr_factors;
 
 /*
@@ -346,6 +352,26 @@ size_t kvlr_noalloc_scratch_bytes(void);
  */
 kvlr_status kvlr_upproject(const kvlr_shape* shape, const kvlr_factors* factors, const float* z,
                            float* o_out, int32_t batch, void* stream);
+
+/*
+ * Encode weight preparation. BasisKV English abstract (low-rank K/V
+ * projections; the residual is what the value latent cannot predict of the
+ * key): since (K - v W_pred) A_k = K A_k - v (W_pred A_k), the encode needs
+ * W_pred and A_k only through their r_v x r_k product. kvlr_prepare_residual
+ * forms -(W_pred A_k) once per factor set (float32 sums of exact products on
+ * the matrix cores, then, for bf16, split into high and low bf16 parts) in
+ * the operand layout the encode kernels read; pass it as
+ * kvlr_factors.residual_prep. The encode's outputs are bit-identical with or
+ * without it (the same arithmetic, done once instead of per workgroup).
+ *   prep        out, device, 16-byte aligned, prep_bytes >= the size below
+ * kvlr_residual_prep_bytes: its size for this shape (host); 0 when the shape
+ * has no residual (KVLR_KEYS_LATENT) or is rejected.
+ * Needs A_k and W_pred in factors; KVLR_KEYS_LATENT returns
+ * KVLR_ERR_INVALID_ARGUMENT, a too small buffer KVLR_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t kvlr_residual_prep_bytes(const kvlr_shape* shape);
+kvlr_status kvlr_prepare_residual(const kvlr_shape* shape, const kvlr_factors* factors,
+                                  void* prep, size_t prep_bytes, void* stream);
 
 /* Workspace bytes that route and attention need for this shape (host). */
 size_t kvlr_workspace_bytes(const kvlr_shape* shape, int32_t batch, int32_t max_pages_per_seq);

@@ -297,3 +297,38 @@ def test_noalloc_attention_arguments(lib):
     assert lib.kvlr_decode_attn_upproject_noalloc(
         ctypes.byref(s), ctypes.byref(f), ctypes.byref(c), fake, fake, fake, fake, 512, None,
         None, None, 0, float("nan"), fake, None, fake, 16, None) == K.KVLR_ERR_INVALID_ARGUMENT
+
+
+def test_residual_prep_arguments(lib):
+    """Sizes of the prepared residual operand, and the host-side rejections of
+    kvlr_prepare_residual and of a misaligned operand handed to the encode."""
+    # bf16: ceil(r_v/32) k-steps x r_k/16 tiles x 64 lanes x 8 elements x 2 B, high and low parts
+    assert K.kvlr_residual_prep_bytes(_shape()) == 8 * (2 * 2 * 64 * 8 * 2 * 2)
+    assert K.kvlr_residual_prep_bytes(_shape(dtype=K.KVLR_DTYPE_BF16_FP8)) == 8 * 8192
+    assert K.kvlr_residual_prep_bytes(_shape(head_dim=64, rank_v=32, rank_k=16, num_q_heads=16,
+                                             num_kv_heads=2)) == 2 * (1 * 1 * 64 * 8 * 2 * 2)
+    # f32: r_v/4 k-steps x r_k/16 tiles x 64 lanes x 4 B, one part
+    assert K.kvlr_residual_prep_bytes(_shape(dtype=K.KVLR_DTYPE_F32)) == 8 * (16 * 2 * 64 * 4)
+    assert K.kvlr_residual_prep_bytes(_shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64)) == 0
+    assert K.kvlr_residual_prep_bytes(_shape(head_dim=96)) == 0
+    fake = 1 << 20
+    f = K.make_factors(fake, fake, fake, fake, fake)
+    s = _shape()
+    need = K.kvlr_residual_prep_bytes(s)
+
+    def prep(shape, factors, ptr, nbytes):
+        return lib.kvlr_prepare_residual(ctypes.byref(shape), ctypes.byref(factors), ptr, nbytes, None)
+
+    assert prep(s, f, fake, need - 16) == K.KVLR_ERR_WORKSPACE_TOO_SMALL
+    assert prep(s, f, fake + 8, need) == K.KVLR_ERR_INVALID_ARGUMENT
+    assert prep(s, f, None, need) == K.KVLR_ERR_INVALID_ARGUMENT
+    assert prep(s, K.make_factors(fake, fake, fake, fake, None), fake, need) == K.KVLR_ERR_INVALID_ARGUMENT
+    assert prep(_shape(key_mode=K.KVLR_KEYS_LATENT, rank_k=64), f, fake, need) == \
+        K.KVLR_ERR_INVALID_ARGUMENT
+    with pytest.raises(K.KvlrError):
+        K.kvlr_prepare_residual(s, f, None, need)
+    # a misaligned operand is rejected by the encode before its launch
+    c = K.make_cache(fake, fake, fake)
+    fm = K.make_factors(fake, fake, fake, fake, fake, fake + 8)
+    assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(fm), ctypes.byref(c), fake, fake,
+                                  fake, fake, fake, 512, 4, 4, None) == K.KVLR_ERR_INVALID_ARGUMENT

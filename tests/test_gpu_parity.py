@@ -280,6 +280,44 @@ def test_append_and_projection_in_one_launch(kw):
     assert torch.equal(one.q_proj, two.q_proj)
 
 
+PREP_CASES = [
+    dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True),
+    dict(G=8, d=128, rv=32, rk=32, P=64, storage="bf16", routed=True, latent="fp8"),
+    dict(G=2, d=64, rv=32, rk=16, P=16, storage="f32", routed=True),
+    dict(G=4, d=128, rv=64, rk=64, P=64, storage="bf16", routed=True, ranks=(16, 64)),
+    dict(G=4, d=128, rv=128, rk=16, P=64, storage="bf16", routed=False, exact=True,
+         value_basis="identity"),
+]
+
+
+@pytest.mark.parametrize("kw", PREP_CASES, ids=["bf16", "fp8-G8", "f32-P16", "adaptive", "rv128"])
+def test_prepared_residual_equals_per_workgroup(kw):
+    """kvlr_prepare_residual's operand gives exactly the cache pages that the
+    encode writes when each workgroup forms -(W_pred A_k) itself, through both
+    append entry points."""
+    wl = make_wl(**kw)
+    _say("case prepared residual", wl.name)
+    lens = [300, 1000, 77, 129]
+    own = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=70, residual_prep=False)
+    pre = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=70)
+    assert own.residual_prep is None and pre.residual_prep is not None
+    assert pre.residual_prep.numel() == K.kvlr_residual_prep_bytes(pre.shape)
+    own.append()
+    pre.append()
+    torch.cuda.synchronize()
+    for n in ("v_lat", "k_lat", "k_exact"):
+        assert torch.equal(getattr(own, n), getattr(pre, n)), n
+    own.append_and_project()
+    pre.append_and_project()
+    torch.cuda.synchronize()
+    for n in ("v_lat", "k_lat", "k_exact", "q_proj"):
+        assert torch.equal(getattr(own, n), getattr(pre, n)), n
+    # and the pages still match the oracle's encode
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            H.check_encode(pre, b, g)
+
+
 @pytest.mark.parametrize("routed", [True, False])
 def test_chunked_append_equals_one_shot(routed):
     wl = make_wl(G=4, d=128, rv=64, rk=32 if routed else 64, P=64, storage="bf16", routed=routed)
