@@ -602,15 +602,33 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           (Ls > 0.f) ? (M + fast_log2(Ls)) * 0.69314718055994530942f : kNegInf;
   }
   if (o_out) {
-    // value compression tied to the output projection: o_h = z_h B_v, once per head
+    // value compression tied to the output projection: o_h = z_h B_v, once
+    // per head. A thread takes 4 consecutive outputs of one head over a
+    // contiguous 1/ES of the latent index; the ES partial sums sit in
+    // adjacent lanes and are added with two-lane exchanges.
     __syncthreads();
-    for (int i = threadIdx.x; i < G * Dh; i += kThreads) {
-      const int h = i / Dh, d = i - h * Dh;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < RV; ++e) acc = fmaf(s_zz[h][e], SF::load1(s_bv, static_cast<long>(e) * Dh + d), acc);
-      o_out[(static_cast<size_t>(b) * Hq + g * G + h) * Dh + d] = acc;
+    const int nq = Dh >> 2;                 // 4-output groups per head
+    int es = kThreads / (G * nq);           // latent splits per group: 1 .. 8
+    es = es >= 8 ? 8 : es >= 4 ? 4 : es >= 2 ? 2 : 1;
+    const int item = threadIdx.x / es, part = threadIdx.x - item * es;
+    const bool on = item < G * nq;
+    const int h = on ? item / nq : 0, d0 = on ? (item - (item / nq) * nq) * 4 : 0;
+    const int e0 = part * (RV / es), e1 = e0 + RV / es;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int e = e0; e < e1; ++e) {
+      const float zv = s_zz[h][e];
+      float bv[4];
+      SF::load4(s_bv, static_cast<long>(e) * Dh + d0, bv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(zv, bv[j], acc[j]);
     }
+    for (int m = 1; m < es; m <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], m);
+    if (on && part == 0)
+      *reinterpret_cast<float4*>(o_out + (static_cast<size_t>(b) * Hq + g * G + h) * Dh + d0) =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
 }
 

@@ -16,7 +16,8 @@
 //    workgroup covers 16 or 32 output features; its 8 waves split the
 //    reduction and request several k-steps of loads at a time. Each wave reads F rows as 16-byte
 //    B fragments and the float32 latents as bf16 high and low halves (two
-//    products per step); the partial tiles are summed through LDS.
+//    products per step); the partial tiles are summed through LDS in a
+//    fixed order with two barriers.
 
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kOThreads) void oproj_kernel(const uint8_t* __restr
                                                           const float* __restrict__ z,
                                                           float* __restrict__ out, int K,
                                                           int hidden, int batch) {
-  __shared__ float s_red[MG][kNT][4][kWave];
+  __shared__ float s_red[kOWaves / 2][MG][kNT][4][kWave];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int kq = lane >> 4, col = lane & 15;
@@ -137,26 +138,37 @@ __global__ __launch_bounds__(kOThreads) void oproj_kernel(const uint8_t* __restr
         }
       }
     }
-    // the waves' partial tiles are summed through LDS in wave order (the same
-    // order every run); lane holds batch rows 4*kq + v of output column col
-    for (int w = 0; w < kOWaves; ++w) {
-      if (wave == w) {
+    // the waves' partial tiles are summed through LDS in a fixed order (the
+    // same every run): waves w and w + 4 pair up, then the four pair sums are
+    // added in order; lane holds batch rows 4*kq + v of output column col
+    constexpr int kHalf = kOWaves / 2;
+    if (wave >= kHalf) {
 #pragma unroll
-        for (int m = 0; m < MG; ++m)
+      for (int m = 0; m < MG; ++m)
 #pragma unroll
-          for (int t = 0; t < kNT; ++t)
+        for (int t = 0; t < kNT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              s_red[m][t][v][lane] = (w == 0 ? 0.f : s_red[m][t][v][lane]) + acc[m][t][v];
-      }
-      __syncthreads();
+          for (int v = 0; v < 4; ++v) s_red[wave - kHalf][m][t][v][lane] = acc[m][t][v];
     }
+    __syncthreads();
+    if (wave < kHalf) {
+#pragma unroll
+      for (int m = 0; m < MG; ++m)
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s_red[wave][m][t][v][lane] += acc[m][t][v];
+    }
+    __syncthreads();
     for (int i = threadIdx.x; i < MG * kNT * 4 * kWave; i += kOThreads) {
       const int m = i / (kNT * 4 * kWave), t = (i / (4 * kWave)) % kNT, v = (i / kWave) % 4;
       const int l = i % kWave;
       const int row = (mg + m) * 16 + 4 * (l >> 4) + v;
       if (m >= mcount || row >= batch || t0 + t >= ntiles) continue;
-      out[static_cast<size_t>(row) * hidden + (t0 + t) * 16 + (l & 15)] = s_red[m][t][v][l];
+      float sum = s_red[0][m][t][v][l];
+#pragma unroll
+      for (int w = 1; w < kHalf; ++w) sum += s_red[w][m][t][v][l];
+      out[static_cast<size_t>(row) * hidden + (t0 + t) * 16 + (l & 15)] = sum;
     }
     __syncthreads();
   }

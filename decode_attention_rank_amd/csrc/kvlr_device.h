@@ -49,6 +49,14 @@ struct BF16 {
     const uint16_t u = reinterpret_cast<const uint16_t*>(base)[idx];
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
   }
+  // elements idx .. idx+3 (idx a multiple of 4) in one 8-byte read
+  __device__ static inline void load4(const void* base, long idx, float (&x)[4]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+  }
 };
 
 struct F32 {
@@ -65,6 +73,13 @@ struct F32 {
   }
   __device__ static inline float load1(const void* base, long idx) {
     return reinterpret_cast<const float*>(base)[idx];
+  }
+  __device__ static inline void load4(const void* base, long idx, float (&x)[4]) {
+    const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    x[0] = w.x;
+    x[1] = w.y;
+    x[2] = w.z;
+    x[3] = w.w;
   }
 };
 
