@@ -5,8 +5,9 @@
     python -m decode_attention_rank_amd.build -D KVLR_ROUTE_MFMA=0 -D KVLR_ATTN_MFMA=0 \
         --out /tmp/libkvlr_valu.so
 
-Each kernel source compiles to an object under _build/ in parallel; the
-objects link into decode_attention_rank_amd/libkvlr.so. A variant's objects go
+Each kernel source compiles to an object under _build/ in parallel (the
+plain C++ host source with the host compiler only); the objects link into
+decode_attention_rank_amd/libkvlr.so. A variant's objects go
 to a folder of their own under _build/ and its library to --out; the binding
 loads it when KVLR_LIBRARY names it.
 """
@@ -30,7 +31,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvlr.so")
 
 SOURCES = ["kvlr_api.hip", "k_route.hip", "k_attn.hip", "k_encode.hip", "k_small.hip", "k_oproj.hip",
-           "k_fit.hip", "k_outfit.hip"]
+           "k_fit.hip", "k_outfit.hip", "kvlr_host_solve.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -49,9 +50,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the kvlr library needs ROCm's hipcc")
 
 
+# plain C++ host sources (no device code): the host compiler alone
+HOST_FLAGS = ["-x", "c++", "-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{CSRC}"]
+
+
 def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> tuple[str, float, str]:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    flags = HOST_FLAGS if src.endswith(".cpp") else FLAGS
+    cmd = [hipcc(), *flags, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:

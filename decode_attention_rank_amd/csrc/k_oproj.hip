@@ -208,15 +208,30 @@ hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// (MG, kNT, kUnroll) for a batch of up to 16 and above
+#ifndef KVLR_OPROJ_S_UNROLL
+#define KVLR_OPROJ_S_UNROLL 4
+#endif
+#ifndef KVLR_OPROJ_L_MG
+#define KVLR_OPROJ_L_MG 4
+#endif
+#ifndef KVLR_OPROJ_L_NT
+#define KVLR_OPROJ_L_NT 2
+#endif
+#ifndef KVLR_OPROJ_L_UNROLL
+#define KVLR_OPROJ_L_UNROLL 2
+#endif
+
 hipError_t launch_oproj(const OprojArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const int K = a.dm.Hq * a.dm.RV;
   const int ntiles = a.hidden / 16;
   if (a.batch <= 16)
-    hipLaunchKernelGGL((oproj_kernel<1, 1, 4>), dim3(ntiles), dim3(kOThreads), 0, s,
+    hipLaunchKernelGGL((oproj_kernel<1, 1, KVLR_OPROJ_S_UNROLL>), dim3(ntiles), dim3(kOThreads), 0, s,
                        static_cast<const uint8_t*>(a.F), a.z, a.out, K, a.hidden, a.batch);
   else
-    hipLaunchKernelGGL((oproj_kernel<4, 2, 2>), dim3((ntiles + 1) / 2), dim3(kOThreads), 0, s,
+    hipLaunchKernelGGL((oproj_kernel<KVLR_OPROJ_L_MG, KVLR_OPROJ_L_NT, KVLR_OPROJ_L_UNROLL>),
+                       dim3((ntiles + KVLR_OPROJ_L_NT - 1) / KVLR_OPROJ_L_NT), dim3(kOThreads), 0, s,
                        static_cast<const uint8_t*>(a.F), a.z, a.out, K, a.hidden, a.batch);
   return hipGetLastError();
 }

@@ -19,9 +19,8 @@
 // GPU work (all dense contractions on the float32 matrix cores,
 // v_mfma_f32_16x16x4_f32, with float32 sums over runs of 256 and float64
 // sums of the runs): Z = X A per head; the moments Z^T Z and Z^T X; the fold
-// F = W_o D^T. The host solves the normal equations in float64 (Cholesky,
-// then the triangular solves over the H_q d right-hand sides on up to 16
-// threads).
+// F = W_o D^T. The host solves the normal equations in float64
+// (kvlr_host_solve.cpp).
 
 #include <math.h>
 
@@ -274,54 +273,4 @@ hipError_t launch_joint_fold(const JointFoldArgs& a, hipStream_t s) {
 // forward and back substitutions for every right-hand side column, columns
 // spread over threads. Fails when a pivot falls to 1e-12 of the largest
 // diagonal entry (latents that the samples do not determine).
-FitStatus joint_solve(int nl, int nx, const double* zz, const double* zx, double* D) {
-  std::vector<double> L(static_cast<size_t>(nl) * nl, 0.0);
-  double dmax = 0.0;
-  for (int i = 0; i < nl; ++i) dmax = std::max(dmax, zz[static_cast<size_t>(i) * nl + i]);
-  if (!(dmax > 0.0)) return FitStatus::kSingular;
-  for (int j = 0; j < nl; ++j) {
-    double* Lj = &L[static_cast<size_t>(j) * nl];
-    double s = zz[static_cast<size_t>(j) * nl + j];
-    for (int k = 0; k < j; ++k) s -= Lj[k] * Lj[k];
-    if (!(s > 1e-12 * dmax)) return FitStatus::kSingular;
-    const double djj = sqrt(s);
-    Lj[j] = djj;
-    const double inv = 1.0 / djj;
-    for (int i = j + 1; i < nl; ++i) {
-      double* Li = &L[static_cast<size_t>(i) * nl];
-      double t = zz[static_cast<size_t>(i) * nl + j];
-      for (int k = 0; k < j; ++k) t -= Li[k] * Lj[k];
-      Li[j] = t * inv;
-    }
-  }
-  // U = L^T, so the back substitution reads rows too
-  std::vector<double> U(static_cast<size_t>(nl) * nl, 0.0);
-  for (int i = 0; i < nl; ++i)
-    for (int j = 0; j <= i; ++j) U[static_cast<size_t>(j) * nl + i] = L[static_cast<size_t>(i) * nl + j];
-  const int nthreads = std::max(1, std::min<int>(16, static_cast<int>(std::thread::hardware_concurrency())));
-  auto work = [&](int t) {
-    std::vector<double> y(nl);
-    for (int c = t; c < nx; c += nthreads) {
-      for (int i = 0; i < nl; ++i) {
-        const double* Li = &L[static_cast<size_t>(i) * nl];
-        double s = zx[static_cast<size_t>(i) * nx + c];
-        for (int k = 0; k < i; ++k) s -= Li[k] * y[k];
-        y[i] = s / Li[i];
-      }
-      for (int i = nl - 1; i >= 0; --i) {
-        const double* Ui = &U[static_cast<size_t>(i) * nl];
-        double s = y[i];
-        for (int k = i + 1; k < nl; ++k) s -= Ui[k] * y[k];
-        y[i] = s / Ui[i];
-      }
-      for (int i = 0; i < nl; ++i) D[static_cast<size_t>(i) * nx + c] = y[i];
-    }
-  };
-  std::vector<std::thread> pool;
-  for (int t = 1; t < nthreads; ++t) pool.emplace_back(work, t);
-  work(0);
-  for (auto& th : pool) th.join();
-  return FitStatus::kOk;
-}
-
 }  // namespace kvlr

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvlr_host.h"
+
 namespace kvlr {
 
 // Shape facts every launcher needs, already validated by the API layer.
@@ -166,7 +168,6 @@ struct FitRuns {
 FitRuns fit_runs(int Hkv, int n);
 hipError_t launch_fit_moments(const FitArgs& a, hipStream_t s);
 
-enum class FitStatus { kOk, kSingular, kNoConvergence };
 // Host: factors from float64 moments. A_v [Hkv][D][RV], A_k [Hkv][D][RK],
 // W [Hkv][RV][D] (exact keys only), lam_v [Hkv][RV], lam_k [Hkv][RK] (may
 // be null).
@@ -194,7 +195,6 @@ struct JointFoldArgs {
   int hidden;
 };
 hipError_t launch_joint_fold(const JointFoldArgs& a, hipStream_t s);
-// Host: D = zz^-1 zx (row-major [nl][nx]); kSingular for a non-positive pivot.
-FitStatus joint_solve(int nl, int nx, const double* zz, const double* zx, double* D);
+
 
 }  // namespace kvlr
