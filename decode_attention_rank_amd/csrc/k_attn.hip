@@ -219,31 +219,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       constexpr int KS = (CKW + 3) / 4;  // k-steps of 32 key elements
       const int kq = lane >> 4, col = lane & 15;
       // the query halves, one 16-byte fragment per (k-step, half, lane), live
-      // in the wave's LDS slice and are read once per k-step of a row
+      // in the wave's LDS slice and are read once per k-step of a row. The
+      // query is requested first, the first rows' page ids next and their
+      // key and value chunks after those arrive; the halves are formed and
+      // stored only then, so the chunk's start waits for two memory round
+      // trips (query with page ids, then the first rows) instead of three.
       __shared__ uint4 s_qf[kWaves][KS][2][kWave];
+      float4 qx[KS][2];
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
         const int ci = 4 * st + kq;
-        float x[8];
         if (col < G && ci < CKW) {
           const float* src = qg + col * KW + ci * 8;
-          const float4 a0 = *reinterpret_cast<const float4*>(src);
-          const float4 a1 = *reinterpret_cast<const float4*>(src + 4);
-          x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-          x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+          qx[st][0] = *reinterpret_cast<const float4*>(src);
+          qx[st][1] = *reinterpret_cast<const float4*>(src + 4);
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+          qx[st][0] = qx[st][1] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        bf16x8 hi, lo;
-        split_bf16x8(x, hi, lo);
-        s_qf[wave][st][0][lane] = __builtin_bit_cast(uint4, hi);
-        s_qf[wave][st][1][lane] = __builtin_bit_cast(uint4, lo);
       }
-      wave_lds_sync();
+      auto stage_query = [&] {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const float x[8] = {qx[st][0].x, qx[st][0].y, qx[st][0].z, qx[st][0].w,
+                              qx[st][1].x, qx[st][1].y, qx[st][1].z, qx[st][1].w};
+          bf16x8 hi, lo;
+          split_bf16x8(x, hi, lo);
+          s_qf[wave][st][0][lane] = __builtin_bit_cast(uint4, hi);
+          s_qf[wave][st][1][lane] = __builtin_bit_cast(uint4, lo);
+        }
+        wave_lds_sync();
+      };
+      // With chosen page ids and at most 64 rows per chunk, lane l reads the
+      // id (and physical page) of the chunk's row l, one request per array
+      // issued with the query's; every row's lookup, the first ones and the
+      // loop's (two and three rows ahead), is then a read of a lane with no
+      // memory round trip of its own. Otherwise each lookup reads memory.
+      const bool lanes = sl != nullptr && rows_per_chunk <= kWave;
+      int lane_pg = -1, lane_ph = 0;
+      if (lanes) {
+        const int li = row0 + lane < row1 ? row0 + lane : 0;
+        lane_pg = sl[li];
+        if (sp) lane_ph = sp[li];
+      }
       auto page_of = [&](int row) -> int {
         if (row >= row1) return -1;
-        const int pg = sl ? sl[row] : row;
+        const int pg = lanes ? __builtin_amdgcn_readlane(lane_pg, row - row0) : (sl ? sl[row] : row);
         return (pg >= 0 && pg < N) ? pg : -1;
       };
       // past the last row every lane reads one shared address (on = 0);
@@ -255,7 +275,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       };
       auto row_ref = [&](int row, int pg) -> RowRef {
         if (pg < 0) return RowRef{keys, v_lat, 0, 0};
-        const size_t ph = phys_of(row, pg);
+        const size_t ph = (lanes && sp) ? static_cast<size_t>(__builtin_amdgcn_readlane(lane_ph, row - row0))
+                                        : phys_of(row, pg);
         return RowRef{keys + (ph * Hkv + g) * slab_k,
                       v_lat + (ph * Hkv + g) * slab_v + my_c * kWave * SV::CB, 1,
                       min(L - pg * kWave, kWave)};
@@ -273,14 +294,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       typename S::Raw A[4][KS];
       typename SV::Raw vc[CV];
       RowRef cur = row_ref(r, page_of(r));
+      RowRef nxt = row_ref(r + kWaves, page_of(r + kWaves));
+      int pg2 = page_of(r + 2 * kWaves);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int st = 0; st < KS; ++st) A[j][st] = S::load_stream(a_addr(cur, j, st));
 #pragma unroll
       for (int k = 0; k < CV; ++k) vc[k] = SV::load_stream(v_addr(cur, k));
-      RowRef nxt = row_ref(r + kWaves, page_of(r + kWaves));
-      int pg2 = page_of(r + 2 * kWaves);
+      stage_query();
       float lcol = 0.f;  // sum of this lane's probabilities of head col
       for (; r < row1; r += kWaves) {
         // table lookups run ahead: physical page two rows on, page id three rows on
