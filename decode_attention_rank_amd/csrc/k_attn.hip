@@ -587,9 +587,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   };
   const int nsplit = (sel && !sel_counts) ? max_splits
                                           : attn_splits(items_of, b, Hkv, ipr_log2, rows_per_chunk);
+  // B_v[g] is requested together with the records (one round trip for
+  // both) and written to LDS once the records are merged
+  constexpr int NBV = (RV * 128 * SF::ELEM_BYTES / 16 + kThreads - 1) / kThreads;
+  const int nbv = RV * Dh * SF::ELEM_BYTES / 16;
+  uint4 bv[NBV];
   if (o_out) {
     const uint8_t* Bg = B_v + static_cast<size_t>(g) * RV * Dh * SF::ELEM_BYTES;
-    for (int i = threadIdx.x; i < RV * Dh * SF::ELEM_BYTES / 16; i += kThreads) s_bv[i] = load16(Bg + i * 16);
+#pragma unroll
+    for (int it = 0; it < NBV; ++it) {
+      const int i = static_cast<int>(threadIdx.x) + it * kThreads;
+      bv[it] = load16(Bg + static_cast<size_t>(i < nbv ? i : 0) * 16);
+    }
   }
   const float* allp = partials + static_cast<size_t>(pair) * max_splits * G * PW;
   for (int i = threadIdx.x; i < G * RV; i += kThreads) {
@@ -604,14 +613,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         ll[u] = r[1];
         zz[u] = r[2 + e];
       }
+      // (selects, not a branch: the loads of every record are then used
+      // unconditionally and go out together)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (sp0 + u >= nsplit || mm[u] == kNegInf) continue;
-        const float mn = fmaxf(M, mm[u]);
+        const bool ok = sp0 + u < nsplit && mm[u] != kNegInf;
+        const float mn = ok ? fmaxf(M, mm[u]) : M;
         const float a = (M == kNegInf) ? 0.f : fast_exp2(M - mn);
         const float f = fast_exp2(mm[u] - mn);
-        Z = Z * a + f * zz[u];
-        Ls = Ls * a + f * ll[u];
+        const float zn = Z * a + f * zz[u];
+        const float ln = Ls * a + f * ll[u];
+        Z = ok ? zn : Z;
+        Ls = ok ? ln : Ls;
         M = mn;
       }
     }
@@ -628,6 +641,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     // per head. A thread takes 4 consecutive outputs of one head over a
     // contiguous 1/ES of the latent index; the ES partial sums sit in
     // adjacent lanes and are added with two-lane exchanges.
+#pragma unroll
+    for (int it = 0; it < NBV; ++it) {
+      const int i = static_cast<int>(threadIdx.x) + it * kThreads;
+      if (i < nbv) s_bv[i] = bv[it];
+    }
     __syncthreads();
     const int nq = Dh >> 2;                 // 4-output groups per head
     int es = kThreads / (G * nq);           // latent splits per group: 1 .. 8

@@ -445,21 +445,22 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     const int i = tile * 64 + wave * 16 + r;
     const bool valid = i < total_new;
     const int t_own = wave * 16 + r;  // this lane's token within the tile
-    if (kq == 0) {
-      sm.tok_page[t_own] = valid ? static_cast<int>(phys) : -1;
-      sm.tok_slot[t_own] = static_cast<int>(slot_off);
-    }
     if constexpr (ROUTED && FRAG_IS_CHUNK) {
       // fragment ks of this lane is chunk ks * KSTEP / CH + kq of the key row
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks)
         sm.kt[t_own][ks * (KSTEP / CH) + kq] = __builtin_bit_cast(uint4, kf[ks]);
     }
+    // the products use only this wave's rows; the token's page (its lookup
+    // still in flight) is needed only by the stores after the barrier
+    products(vf, kf, [] {});
+    if (kq == 0) {
+      sm.tok_page[t_own] = valid ? static_cast<int>(phys) : -1;
+      sm.tok_slot[t_own] = static_cast<int>(slot_off);
+    }
     block_lds_sync();
     const int pg = sm.tok_page[lane];  // lane = token of the tile from here on
     const size_t slot = static_cast<size_t>(sm.tok_slot[lane]);
-    products(vf, kf, [] {});
-    block_lds_sync();
     if constexpr (ROUTED && FRAG_IS_CHUNK) {
       constexpr int NCOL = CD / kWaves;  // key chunk columns per wave
       static_assert(CD % kWaves == 0, "key chunk columns split evenly over the waves");
