@@ -200,7 +200,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   constexpr int NTV = RV / 16, NTK = RK / 16;
   constexpr int CV = RV / CH, CK = RK / CH, CD = D / CH;
   __shared__ SM sm;
-  extern __shared__ int s_seq[];  // cu_new[0..batch], then lens_before[0..batch)
+  // cu_new[0 .. batch] at s_seq[0 ..], lens_before[0 .. batch) at s_seq[nb1 ..]
+  extern __shared__ int s_seq[];
+  const int nb1 = batch + 1 > kThreads ? batch + 1 : kThreads;
 
   if (static_cast<int>(blockIdx.y) < qt.qy) {  // a workgroup of query-projection tiles
     // grid column x holds KV head x's tiles, as it holds that head's encode
@@ -338,8 +340,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       return;
     }
   }
-  // this workgroup's first tile, and the W_pred rows of M (unless it comes
+  // each thread's entries of cu_new and lens_before (clamped indexes: every
+  // thread reads and later stores, so the requests are not deferred), this
+  // workgroup's first tile, and the W_pred rows of M (unless it comes
   // prepared), are requested before the set-up below
+  const int cu_first = cu_new[tid <= batch ? tid : batch];
+  const int lb_first = lens_before[tid < batch ? tid : batch - 1];
   frag_t vf[KSD], kf[KSD];
   load_tile(tile0, vf, kf);
   if constexpr (ROUTED) {
@@ -358,8 +364,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       }
     }
   }
-  for (int b = tid; b <= batch; b += kThreads) s_seq[b] = cu_new[b];
-  for (int b = tid; b < batch; b += kThreads) s_seq[batch + 1 + b] = lens_before[b];
+  s_seq[tid] = cu_first;
+  s_seq[nb1 + tid] = lb_first;
+  for (int b = tid + kThreads; b <= batch; b += kThreads) s_seq[b] = cu_new[b];
+  for (int b = tid + kThreads; b < batch; b += kThreads) s_seq[nb1 + b] = lens_before[b];
   __syncthreads();
 
   // sequence of token i: largest b with cu_new[b] <= i (offsets staged in LDS);
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       const int mid = (lo + hi) >> 1;
       if (s_seq[mid] <= i) lo = mid; else hi = mid;
     }
-    const int pos = s_seq[batch + 1 + lo] + (i - s_seq[lo]);
+    const int pos = s_seq[nb1 + lo] + (i - s_seq[lo]);
     slot_off = static_cast<size_t>(pos & (P - 1));
     return page_table + static_cast<size_t>(lo) * max_pages + (pos >> log2P);
   };
@@ -539,7 +547,7 @@ template <class S, class LS, int D, int RV, int RK, bool ROUTED>
 hipError_t launch_t(const EncodeArgs& a, hipStream_t s) {
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   const int ntiles = (a.total_new + 63) / 64;
-  const size_t lds = (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int);
+  const size_t lds = 2 * static_cast<size_t>(a.batch + 1 > kThreads ? a.batch + 1 : kThreads) * sizeof(int);
   // A persistent grid: the workgroups that fit on the device at once, each
   // looping over tiles (a second, partial round of workgroups left most of
   // the device idle behind it, and fewer, longer-lived workgroups stage the

@@ -450,6 +450,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
       // a wave-uniform test, compiled only where the residual spans 2+ steps
       const int ks_used = KSV + (ckg + 3) / 4;
       auto step_on = [&](int st) { return st <= KSV || st < ks_used; };
+      // the projected queries are requested first, all k-steps at once (a
+      // lane outside the group or past the slab reads the group's first row
+      // and gets zeros), then the first row; their fragments are formed while
+      // that row is in flight (the in-order counter lets them wait for the
+      // queries alone)
+      float4 qa[KS], qc[KS];
+      bool qhave[KS];
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const bool on_v = st < KSV;
+        const int ci = 4 * (on_v ? st : st - KSV) + kq;  // chunk within the slab
+        qhave[st] = col < G && ci < (on_v ? CV : ckg);
+        const float* src = qp + (qhave[st] ? col * W + (on_v ? 0 : RV) + ci * 8 : 0);
+        qa[st] = *reinterpret_cast<const float4*>(src);
+        qc[st] = *reinterpret_cast<const float4*>(src + 4);
+      }
       RowRef cur = row_ref(r);
 #pragma unroll
       for (int p = 0; p < NL; ++p)
@@ -457,24 +473,12 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
         for (int st = 0; st < KS; ++st)
           if (step_on(st)) A[p][st] = load16_stream(a_addr(cur, p, st));
       RowRef nxt = row_ref(r + kWaves);
-      // the query fragments are formed while the first row is in flight
       bf16x8 qhi[KS], qlo[KS];
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const bool on_v = st < KSV;
-        const int ci = 4 * (on_v ? st : st - KSV) + kq;  // chunk within the slab
-        const bool have = col < G && ci < (on_v ? CV : ckg);
-        const float* src = qp + col * W + (on_v ? 0 : RV) + ci * 8;
-        float x[8];
-        if (have) {
-          const float4 a = *reinterpret_cast<const float4*>(src);
-          const float4 c = *reinterpret_cast<const float4*>(src + 4);
-          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-          x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
-        } else {
+        float x[8] = {qa[st].x, qa[st].y, qa[st].z, qa[st].w, qc[st].x, qc[st].y, qc[st].z, qc[st].w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = 0.f;
-        }
+        for (int e = 0; e < 8; ++e) x[e] = qhave[st] ? x[e] : 0.f;
         split_bf16x8(x, qhi[st], qlo[st]);
       }
       for (; r < row1; r += kWaves) {
