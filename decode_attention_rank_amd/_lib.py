@@ -39,6 +39,7 @@ EXPORTED = (
     "kvlr_decode_attn_upproject_noalloc", "kvlr_noalloc_scratch_bytes",
     "kvlr_fit_joint_workspace_bytes", "kvlr_fit_joint_moments", "kvlr_fit_joint_solve",
     "kvlr_fold_joint_decoder", "kvlr_fit_joint", "kvlr_residual_prep_bytes", "kvlr_prepare_residual",
+    "kvlr_check_page_tables",
 )
 
 
@@ -91,6 +92,7 @@ _SIG = {
                                             _I, ctypes.c_float, _P, _P, _P, _I, _P], _I),
     "kvlr_noalloc_scratch_bytes": ([], ctypes.c_size_t),
     "kvlr_residual_prep_bytes": ([ctypes.POINTER(kvlr_shape)], ctypes.c_size_t),
+    "kvlr_check_page_tables": ([ctypes.POINTER(kvlr_shape), _P, _P, _I, _I, _P, _P], _I),
     "kvlr_prepare_residual": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors), _P,
                                ctypes.c_size_t, _P], _I),
     "kvlr_fit_joint_workspace_bytes": ([ctypes.POINTER(kvlr_shape), _I], ctypes.c_size_t),
@@ -192,6 +194,16 @@ def make_factors(A_v=None, B_v=None, A_k=None, B_k=None, W_pred=None,
 
 def kvlr_residual_prep_bytes(shape: kvlr_shape) -> int:
     return lib().kvlr_residual_prep_bytes(ctypes.byref(shape))
+
+
+KVLR_TABLE_ERR_PAGE = 1
+KVLR_TABLE_ERR_LENGTH = 2
+
+
+def kvlr_check_page_tables(shape, seq_lens, page_table, max_pages_per_seq, batch, errors, stream=None):
+    _check("kvlr_check_page_tables", lib().kvlr_check_page_tables(
+        ctypes.byref(shape), _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, batch, _ptr(errors),
+        _stream(stream)))
 
 
 def kvlr_prepare_residual(shape, factors, prep, prep_bytes, stream=None):

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // attended items (pages) of a (sequence, KV head) pair
   auto items_of = [&](int b, int g) {
-    if (!sel) return (seq_lens[b] + P - 1) >> log2P;
+    if (!sel) return (table_len(seq_lens[b], max_pages, P) + P - 1) >> log2P;
     return sel_counts ? min(max(sel_counts[b * Hkv + g], 0), k_max) : k_max;
   };
   const bool uniform = sel && !sel_counts;  // every pair walks k_max rows in max_splits chunks
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       g = local / nsplit;
       split = local - g * nsplit;
     }
-    const int L = seq_lens[b];
+    const int L = table_len(seq_lens[b], max_pages, P);
     const int N = (L + P - 1) >> log2P;
     const int n_items = items_of(b, g);
     const int nrows = (n_items + (1 << ipr_log2) - 1) >> ipr_log2;
@@ -572,7 +572,7 @@ template <class SF, int G, int RV>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float* __restrict__ partials, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_counts, int k_max,
-    int P, int log2P, int rows_per_chunk, int max_splits, int Hq, int Hkv, int Dh,
+    int P, int log2P, int max_pages, int rows_per_chunk, int max_splits, int Hq, int Hkv, int Dh,
     float* __restrict__ z_out, float* __restrict__ lse_out, const uint8_t* __restrict__ B_v,
     float* __restrict__ o_out) {
   constexpr int PW = RV + 2;
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   const int b = pair / Hkv, g = pair - b * Hkv;
   const int ipr_log2 = 6 - log2P;
   auto items_of = [&](int bb, int gg) {
-    if (!sel) return (seq_lens[bb] + P - 1) >> log2P;
+    if (!sel) return (table_len(seq_lens[bb], max_pages, P) + P - 1) >> log2P;
     return sel_counts ? min(max(sel_counts[bb * Hkv + gg], 0), k_max) : k_max;
   };
   const int nsplit = (sel && !sel_counts) ? max_splits
@@ -697,7 +697,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   using SF = std::conditional_t<S::CB == 8, BF16, S>;  // factor storage
   hipLaunchKernelGGL((merge_kernel<SF, G, RV>), dim3(a.batch * a.dm.Hkv), dim3(kThreads), 0, s,
-                     a.partials, a.seq_lens, a.sel, a.sel_counts, a.k_max, a.dm.P, log2P,
+                     a.partials, a.seq_lens, a.sel, a.sel_counts, a.k_max, a.dm.P, log2P, a.max_pages,
                      a.rows_per_chunk, a.max_splits, a.dm.Hq, a.dm.Hkv, a.dm.D, a.z_out, a.lse_out,
                      static_cast<const uint8_t*>(a.B_v), a.o_out);
   return hipGetLastError();

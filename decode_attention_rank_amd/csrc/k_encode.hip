@@ -371,24 +371,32 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   __syncthreads();
 
   // sequence of token i: largest b with cu_new[b] <= i (offsets staged in LDS);
-  // returns its page-table entry (entry 0 of sequence 0 past the last token)
-  // and the token's slot in the page
-  auto locate = [&](int tile, size_t& slot_off) -> const int32_t* {
+  // returns its physical page and the token's slot in the page, or -1 past
+  // the last token or past the end of its page-table row (the entry read
+  // then is entry 0 of sequence 0, and not used); a negative entry also
+  // gives -1, so such a token is not stored
+  auto locate = [&](int tile, size_t& slot_off) -> int {
     const int i = tile * 64 + wave * 16 + r;
     slot_off = 0;
-    if (i >= total_new) return page_table;
-    int lo = 0, hi = batch;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_seq[mid] <= i) lo = mid; else hi = mid;
+    const int32_t* e = page_table;
+    bool ok = false;
+    if (i < total_new) {
+      int lo = 0, hi = batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_seq[mid] <= i) lo = mid; else hi = mid;
+      }
+      const int pos = s_seq[nb1 + lo] + (i - s_seq[lo]);
+      slot_off = static_cast<size_t>(pos & (P - 1));
+      ok = pos >= 0 && (pos >> log2P) < max_pages;
+      if (ok) e = page_table + static_cast<size_t>(lo) * max_pages + (pos >> log2P);
     }
-    const int pos = s_seq[nb1 + lo] + (i - s_seq[lo]);
-    slot_off = static_cast<size_t>(pos & (P - 1));
-    return page_table + static_cast<size_t>(lo) * max_pages + (pos >> log2P);
+    const int v = *e;
+    return ok ? v : -1;
   };
   // the first tile's page-table entry is requested before M is formed
   size_t slot0 = 0;
-  const int phys0 = *locate(tile0, slot0);
+  const int phys0 = locate(tile0, slot0);
 
   if constexpr (ROUTED) {
     if (!mp.in) form_m();  // M = W_pred A_k [RV x RK], 16x16 tiles spread over the waves
@@ -448,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   // of bf16, 512 bytes of FP8), taking every fourth column. The original
   // keys and the latents go out together after the products: the in-order
   // memory counter then waits for a tile's stores once, not per phase.
-  auto process_cols = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+  auto process_cols = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], int phys,
                           size_t slot_off) {
     const int i = tile * 64 + wave * 16 + r;
     const bool valid = i < total_new;
@@ -463,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     // still in flight) is needed only by the stores after the barrier
     products(vf, kf, [] {});
     if (kq == 0) {
-      sm.tok_page[t_own] = valid ? static_cast<int>(phys) : -1;
+      sm.tok_page[t_own] = (valid && phys >= 0) ? phys : -1;
       sm.tok_slot[t_own] = static_cast<int>(slot_off);
     }
     block_lds_sync();
@@ -494,10 +502,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   };
 
   // one tile, f32 storage: each wave stores its 16 tokens' chunks
-  auto process_rows = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+  auto process_rows = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], int phys_id,
                           size_t slot_off) {
     const int i = tile * 64 + wave * 16 + r;
-    const bool valid = i < total_new;
+    const bool valid = i < total_new && phys_id >= 0;
+    const size_t phys = static_cast<size_t>(valid ? phys_id : 0);
     if constexpr (ROUTED) {
       if (valid) {
         uint8_t* kd = k_exact + (phys * Hkv + g) * CD * P * 16 + slot_off * 16;
@@ -526,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     }
     wave_lds_sync();
   };
-  auto process = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], size_t phys,
+  auto process = [&](int tile, const frag_t (&vf)[KSD], const frag_t (&kf)[KSD], int phys,
                      size_t slot_off) {
     if constexpr (FRAG_IS_CHUNK) process_cols(tile, vf, kf, phys, slot_off);
     else process_rows(tile, vf, kf, phys, slot_off);
@@ -537,9 +546,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     int phys = phys0;
     if (tile != tile0) {
       load_tile(tile, vf, kf);
-      phys = *locate(tile, slot);
+      phys = locate(tile, slot);
     }
-    process(tile, vf, kf, static_cast<size_t>(phys), slot);
+    process(tile, vf, kf, phys, slot);
   }
 }
 

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
   auto rpc_of = [&](int g) { return ADAPT ? kl.rpc[g] : rows_per_chunk; };
   auto splits_of = [&](int rows, int g) { return max(1, (rows + rpc_of(g) - 1) / rpc_of(g)); };
   build_chunk_prefix(batch, s_base, [&](int b) {
-    const int rows = (seq_lens[b] + kWave - 1) / kWave;
+    const int rows = (table_len(seq_lens[b], max_pages, P) + kWave - 1) / kWave;
     if (!ADAPT) return Hkv * splits_of(rows, 0);
     int n = 0;
     for (int g = 0; g < Hkv; ++g) n += splits_of(rows, g);
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int b = __builtin_amdgcn_readfirstlane(find_sequence(s_base, batch, w));
-    const int L = seq_lens[b];
+    const int L = table_len(seq_lens[b], max_pages, P);
     const int nrows = (L + kWave - 1) / kWave;
     int local = __builtin_amdgcn_readfirstlane(w - s_base[b]);
     int g, nsplit;

@@ -98,7 +98,40 @@ hipError_t up_by_rv(const UpprojArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Page tables against the cache: each sequence's length within its table
+// row, and every entry that length uses within [0, num_phys). One workgroup
+// per sequence; each wave adds its count of bad entries once.
+__global__ __launch_bounds__(256) void check_tables_kernel(const int32_t* __restrict__ seq_lens,
+                                                           const int32_t* __restrict__ page_table,
+                                                           int max_pages, int P, int num_phys,
+                                                           uint32_t* __restrict__ errors) {
+  const int b = blockIdx.x;
+  const int L = seq_lens[b];
+  if (threadIdx.x == 0 && (L < 0 || L > max_pages * P)) atomicOr(&errors[0], 2u);
+  const int n = (table_len(L, max_pages, P) + P - 1) / P;
+  uint32_t bad = 0;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const int id = page_table[static_cast<size_t>(b) * max_pages + j];
+    bad += (id < 0 || id >= num_phys) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) bad += __shfl_xor(bad, off, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0 && bad) {
+    atomicOr(&errors[0], 1u);
+    atomicAdd(&errors[1], bad);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_check_tables(const int32_t* seq_lens, const int32_t* page_table, int max_pages,
+                               int P, int num_phys, int batch, uint32_t* errors, hipStream_t s) {
+  hipError_t e = launch_zero_fill(errors, 2 * sizeof(uint32_t), s);
+  if (e != hipSuccess || batch == 0) return e;
+  hipLaunchKernelGGL(check_tables_kernel, dim3(batch), dim3(256), 0, s, seq_lens, page_table, max_pages, P,
+                     num_phys, errors);
+  return hipGetLastError();
+}
 
 hipError_t launch_qproj(const QprojArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;

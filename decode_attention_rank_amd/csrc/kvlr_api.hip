@@ -321,6 +321,19 @@ kvlr_status kvlr_prepare_residual(const kvlr_shape* shape, const kvlr_factors* f
   return hip_status(kvlr::launch_encode_prep(a, prep, as_stream(stream)));
 }
 
+kvlr_status kvlr_check_page_tables(const kvlr_shape* shape, const int32_t* seq_lens,
+                                   const int32_t* page_table, int32_t max_pages_per_seq, int32_t batch,
+                                   uint32_t* errors, void* stream) {
+  Dims dm;
+  const kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || max_pages_per_seq < 1 || max_pages_per_seq > 65536 ||
+      !ok_ptr(errors) || (batch > 0 && (!ok_ptr(seq_lens) || !ok_ptr(page_table))))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  return hip_status(kvlr::launch_check_tables(seq_lens, page_table, max_pages_per_seq, dm.P,
+                                              shape->num_phys_pages, batch, errors, as_stream(stream)));
+}
+
 kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* factors,
                                  const float* q, float* q_proj, int32_t batch, void* stream) {
   Dims dm;

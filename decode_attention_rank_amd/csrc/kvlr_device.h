@@ -166,6 +166,14 @@ __device__ inline void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo)
   lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
+// A sequence length as the kernels use it: within [0, max_pages * P], the
+// tokens its page-table row can address (a longer length is a caller error
+// that kvlr_check_page_tables reports; the kernels never index past the row).
+__device__ inline int table_len(int L, int max_pages, int P) {
+  const int cap = max_pages * P;
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
 __device__ inline uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

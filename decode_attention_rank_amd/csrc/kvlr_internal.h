@@ -150,6 +150,10 @@ hipError_t launch_encode_prep(const EncodeArgs& a, void* out, hipStream_t s);
 size_t encode_prep_bytes(const Dims& dm);
 
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+// errors[0] |= 1 for a table entry in use outside [0, num_phys), 2 for a length
+// outside [0, max_pages * P]; errors[1] = bad entries (both cleared first)
+hipError_t launch_check_tables(const int32_t* seq_lens, const int32_t* page_table, int max_pages,
+                               int P, int num_phys, int batch, uint32_t* errors, hipStream_t s);
 
 // Factor fitting: second moments of sample keys and values per KV head.
 struct FitArgs {

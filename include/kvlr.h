@@ -373,6 +373,24 @@ size_t kvlr_residual_prep_bytes(const kvlr_shape* shape);
 kvlr_status kvlr_prepare_residual(const kvlr_shape* shape, const kvlr_factors* factors,
                                   void* prep, size_t prep_bytes, void* stream);
 
+/*
+ * Page-table check, a debugging aid (not part of the decode step). The decode
+ * calls trust the page tables: they read each sequence's length only up to
+ * max_pages_per_seq * page_size tokens (never past its table row), but use the
+ * entries as given. This call checks, on the device, each sequence b of the
+ * batch: 0 <= seq_lens[b] <= max_pages_per_seq * page_size, and every entry
+ * page_table[b][j] for j < ceil(min(seq_lens[b], max_pages_per_seq *
+ * page_size) / page_size) within [0, shape->num_phys_pages).
+ *   errors  out, device uint32 [2], 16-byte aligned, cleared by this call:
+ *           errors[0] = KVLR_TABLE_ERR_* bits found, errors[1] = entries out
+ *           of range. Asynchronous on `stream`: read them after it.
+ */
+#define KVLR_TABLE_ERR_PAGE 1u    /* an entry in use outside [0, num_phys_pages) */
+#define KVLR_TABLE_ERR_LENGTH 2u  /* a length below 0 or above max_pages_per_seq * page_size */
+kvlr_status kvlr_check_page_tables(const kvlr_shape* shape, const int32_t* seq_lens,
+                                   const int32_t* page_table, int32_t max_pages_per_seq, int32_t batch,
+                                   uint32_t* errors, void* stream);
+
 /* Workspace bytes that route and attention need for this shape (host). */
 size_t kvlr_workspace_bytes(const kvlr_shape* shape, int32_t batch, int32_t max_pages_per_seq);
 

@@ -332,3 +332,20 @@ def test_residual_prep_arguments(lib):
     fm = K.make_factors(fake, fake, fake, fake, fake, fake + 8)
     assert lib.kvlr_append_encode(ctypes.byref(s), ctypes.byref(fm), ctypes.byref(c), fake, fake,
                                   fake, fake, fake, 512, 4, 4, None) == K.KVLR_ERR_INVALID_ARGUMENT
+
+
+def test_page_table_check_arguments(lib):
+    """kvlr_check_page_tables rejects bad arguments before any launch."""
+    fake = 1 << 20
+    s = _shape()
+
+    def call(shape, sl, pt, mp, b, err):
+        return lib.kvlr_check_page_tables(ctypes.byref(shape), sl, pt, mp, b, err, None)
+
+    assert call(s, fake, fake, 512, 4, None) == K.KVLR_ERR_INVALID_ARGUMENT      # no error words
+    assert call(s, fake, fake, 512, 4, fake + 4) == K.KVLR_ERR_INVALID_ARGUMENT  # misaligned
+    assert call(s, None, fake, 512, 4, fake) == K.KVLR_ERR_INVALID_ARGUMENT
+    assert call(s, fake, fake, 0, 4, fake) == K.KVLR_ERR_INVALID_ARGUMENT
+    assert call(s, fake, fake, 512, -1, fake) == K.KVLR_ERR_INVALID_ARGUMENT
+    assert call(_shape(head_dim=96), fake, fake, 512, 4, fake) == K.KVLR_ERR_UNSUPPORTED
+    assert (K.KVLR_TABLE_ERR_PAGE, K.KVLR_TABLE_ERR_LENGTH) == (1, 2)

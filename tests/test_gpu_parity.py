@@ -318,6 +318,54 @@ def test_prepared_residual_equals_per_workgroup(kw):
             H.check_encode(pre, b, g)
 
 
+def test_page_table_check_finds_bad_entries_and_lengths():
+    """kvlr_check_page_tables: clean tables give no error; entries in use
+    outside [0, num_phys) are flagged and counted (entries past a sequence's
+    pages are not looked at); a length beyond its table row is flagged."""
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
+    _say("case page-table check")
+    lens = [2112, 777, 640, 100]
+    sess = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=37)
+    err = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    pt = sess.page_table.clone()
+    K.kvlr_check_page_tables(sess.shape, sess.seq_lens_dev, pt, sess.max_pages, wl.batch, err)
+    torch.cuda.synchronize()
+    assert err[:2].tolist() == [0, 0]
+    n = [-(-L // wl.page_size) for L in lens]
+    pt[1, 3] = sess.num_phys + 5           # in use
+    pt[2, n[2] - 1] = -2                   # in use (last page)
+    pt[3, n[3]] = sess.num_phys + 9        # past sequence 3's pages: not in use
+    K.kvlr_check_page_tables(sess.shape, sess.seq_lens_dev, pt, sess.max_pages, wl.batch, err)
+    torch.cuda.synchronize()
+    assert err[:2].tolist() == [K.KVLR_TABLE_ERR_PAGE, 2]
+    long_lens = sess.seq_lens_dev.clone()
+    long_lens[0] = sess.max_pages * wl.page_size + 50
+    K.kvlr_check_page_tables(sess.shape, long_lens, sess.page_table, sess.max_pages, wl.batch, err)
+    torch.cuda.synchronize()
+    assert err[:2].tolist() == [K.KVLR_TABLE_ERR_LENGTH, 0]
+
+
+def test_lengths_past_the_table_row_are_cut_to_it():
+    """A sequence length beyond its page-table row (a caller error) is read as
+    the row's whole span: routing and attention then equal, bit for bit, the
+    step with the length set to that span, and nothing past the row is read
+    or written."""
+    wl = make_wl(G=4, d=128, rv=64, rk=32, P=64, storage="bf16", routed=True)
+    _say("case length past the table row")
+    lens = [2112, 777, 640, 100]   # sequence 0 fills its 33-page row exactly
+    sess = DecodeSession(wl, "cuda", seq_lens=lens, append_per_seq=37)
+    assert sess.max_pages * wl.page_size == lens[0]
+    sess.step()
+    sess.decode()
+    torch.cuda.synchronize()
+    ref = {n: getattr(sess, n).clone() for n in ("sel", "sel_counts", "page_scores", "z", "lse", "o")}
+    sess.seq_lens_dev[0] = lens[0] + 50
+    sess.decode()
+    torch.cuda.synchronize()
+    for n, t in ref.items():
+        assert torch.equal(getattr(sess, n), t), n
+
+
 @pytest.mark.parametrize("routed", [True, False])
 def test_chunked_append_equals_one_shot(routed):
     wl = make_wl(G=4, d=128, rv=64, rk=32 if routed else 64, P=64, storage="bf16", routed=routed)
