@@ -332,7 +332,10 @@ __device__ inline float row_score(const float (&qv)[NQ], const uint4 (&vc)[RV / 
 // per head); uniform caches keep them compile-time, so address offsets fold
 // into the load instructions.
 template <class S, int G, int RV, int RK, bool ROWPAGE, bool ADAPT = false>
-__global__ __launch_bounds__(kThreads) void route_kernel(
+#ifndef KVLR_ROUTE_WAVES_PER_EU
+#define KVLR_ROUTE_WAVES_PER_EU 1  // the least waves per SIMD the registers must allow
+#endif
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_ROUTE_WAVES_PER_EU))) void route_kernel(
     const uint8_t* __restrict__ v_lat, const uint8_t* __restrict__ k_lat,
     const float* __restrict__ q_proj, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, float* __restrict__ scores,
@@ -732,7 +735,10 @@ hipError_t by_g(const RouteArgs& a, hipStream_t s) {
 // Rows of at most 8 KB (rank_v + rank_k <= 64 with bf16 latents, <= 128 with
 // FP8) take twice as many per chunk: a chunk's fixed costs (sequence lookup,
 // query fragments, the hand-off) then weigh less per byte read.
-int route_rows_per_chunk(int row_bytes) { return row_bytes <= 8192 ? 2 * KVLR_ROUTE_RPC : KVLR_ROUTE_RPC; }
+#ifndef KVLR_ROUTE_RPC_SMALL
+#define KVLR_ROUTE_RPC_SMALL (2 * KVLR_ROUTE_RPC)  // rows of at most 8 KB
+#endif
+int route_rows_per_chunk(int row_bytes) { return row_bytes <= 8192 ? KVLR_ROUTE_RPC_SMALL : KVLR_ROUTE_RPC; }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
