@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
     uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int32_t* __restrict__ sel_counts,
     int32_t* __restrict__ sel_phys, const int32_t* __restrict__ k_pages, int Hq, int Hkv, int P,
     int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_chunk,
-    int batch, KLayout kl) {
+    int static_splits, int batch, KLayout kl) {
   constexpr int CH = S::CH;
   constexpr int CV = RV / CH;
   constexpr int CK = RK / CH;
@@ -359,22 +359,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
   // residual ranks a count that gives every chunk about the same bytes
   auto rpc_of = [&](int g) { return ADAPT ? kl.rpc[g] : rows_per_chunk; };
   auto splits_of = [&](int rows, int g) { return max(1, (rows + rpc_of(g) - 1) / rpc_of(g)); };
-  build_chunk_prefix(batch, s_base, [&](int b) {
-    const int rows = (table_len(seq_lens[b], max_pages, P) + kWave - 1) / kWave;
-    if (!ADAPT) return Hkv * splits_of(rows, 0);
-    int n = 0;
-    for (int g = 0; g < Hkv; ++g) n += splits_of(rows, g);
-    return n;
-  });
-  const int total = s_base[batch];
+  // With static_splits > 0 (one rank for every head) every pair has that
+  // many chunks, sized for the longest row the page table allows, and a
+  // chunk's pair and split follow from its index alone: the sequence length,
+  // the projected queries and the first rows' page-table entries are then
+  // requested together, with no pass over the batch's lengths first. Chunks
+  // past a sequence's rows score nothing and only take their ticket.
+  const bool fixed = !ADAPT && static_splits > 0;
+  int total;
+  if (fixed) {
+    total = batch * Hkv * static_splits;
+  } else {
+    build_chunk_prefix(batch, s_base, [&](int b) {
+      const int rows = (table_len(seq_lens[b], max_pages, P) + kWave - 1) / kWave;
+      if (!ADAPT) return Hkv * splits_of(rows, 0);
+      int n = 0;
+      for (int g = 0; g < Hkv; ++g) n += splits_of(rows, g);
+      return n;
+    });
+    total = s_base[batch];
+  }
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int b = __builtin_amdgcn_readfirstlane(find_sequence(s_base, batch, w));
+    int b, local;
+    if (fixed) {
+      const int pr = w / static_splits;
+      b = pr / Hkv;
+      local = w - b * Hkv * static_splits;
+    } else {
+      b = __builtin_amdgcn_readfirstlane(find_sequence(s_base, batch, w));
+      local = __builtin_amdgcn_readfirstlane(w - s_base[b]);
+    }
     const int L = table_len(seq_lens[b], max_pages, P);
     const int nrows = (L + kWave - 1) / kWave;
-    int local = __builtin_amdgcn_readfirstlane(w - s_base[b]);
     int g, nsplit;
-    if (!ADAPT) {
+    if (fixed) {
+      nsplit = static_splits;
+      g = local / nsplit;
+      local -= g * nsplit;
+    } else if (!ADAPT) {
       nsplit = (s_base[b + 1] - s_base[b]) / Hkv;
       g = local / nsplit;
       local -= g * nsplit;
@@ -434,10 +457,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
         const uint8_t* kb;
         int on;  // 1 for a real row
       };
+      // The entry is requested whether or not the row exists (an index within
+      // the table row, clamped), so its request does not wait for the length;
+      // a row past the chunk or the sequence reads page 0's slab at offset 0.
       auto row_ref = [&](int row) -> RowRef {
-        if (row >= row1) return RowRef{v_lat, k_lat, 0};
-        const size_t phys = static_cast<size_t>(pt[row]);
-        return RowRef{v_lat + (phys * Hkv + g) * slab_v, k_lat + phys * kpage + koff, 1};
+        const int ent = pt[min(row, max_pages - 1)];
+        const bool on = row < row1;
+        const size_t phys = on ? static_cast<size_t>(ent) : 0;
+        return RowRef{v_lat + (phys * Hkv + g) * slab_v, k_lat + phys * kpage + koff, on ? 1 : 0};
       };
       auto a_addr = [&](const RowRef& rr, int p, int st) -> const uint8_t* {
         const bool on_v = st < KSV;
@@ -674,7 +701,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                            static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                            a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel,
                            a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num,
-                           a.topk_den, a.k_max, a.rows_per_chunk, a.batch, a.kl);
+                           a.topk_den, a.k_max, a.rows_per_chunk, 0, a.batch, a.kl);
       else
         return hipErrorInvalidValue;
     } else {
@@ -682,7 +709,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
                          a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
-                         a.k_max, a.rows_per_chunk, a.batch, a.kl);
+                         a.k_max, a.rows_per_chunk, a.static_splits, a.batch, a.kl);
     }
   } else {
     if constexpr (S::CB == 8) return hipErrorInvalidValue;  // FP8 latents: 64-token pages only
@@ -691,7 +718,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
                          a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
-                         a.k_max, a.rows_per_chunk, a.batch, a.kl);
+                         a.k_max, a.rows_per_chunk, a.static_splits, a.batch, a.kl);
   }
   return hipGetLastError();
 }

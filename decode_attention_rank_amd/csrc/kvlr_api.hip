@@ -98,6 +98,9 @@ constexpr int kMaxBatch = 4096;          // per-sequence offsets and work lists 
 #define KVLR_ROUTE_GRID 2048
 #endif
 constexpr long long kPersistentGrid = KVLR_ROUTE_GRID;  // about 8 workgroups per CU
+#ifndef KVLR_ROUTE_STATIC
+#define KVLR_ROUTE_STATIC 1  // fixed chunks per pair when one workgroup per chunk fits the grid
+#endif
 #ifndef KVLR_ATTN_GRID
 #define KVLR_ATTN_GRID 1024
 #endif
@@ -414,6 +417,10 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
     chunks += static_cast<long long>(batch) * (max_rows > 0 ? ceil_div(max_rows, rpc) : 1);
   }
   a.grid = static_cast<int>(chunks < kPersistentGrid ? chunks : kPersistentGrid);
+  // every pair sized for the widest table row when that fits one workgroup
+  // per chunk: chunks of shorter sequences then only take their ticket
+  a.static_splits = (KVLR_ROUTE_STATIC && !a.kl.adaptive && chunks <= kPersistentGrid && max_rows > 0)
+                        ? ceil_div(max_rows, a.rows_per_chunk) : 0;
   return hip_status(kvlr::launch_route(a, as_stream(stream)));
 }
 

@@ -58,6 +58,7 @@ struct RouteArgs {
   KLayout kl;
   int batch;
   int rows_per_chunk;   // 64-token rows per work chunk
+  int static_splits;    // > 0: chunks per pair fixed from the table width (no pass over the lengths)
   int grid;             // persistent workgroups
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
