@@ -152,7 +152,8 @@ def measure(sess, steps: int, warmup: int, graph: bool, fused: bool, flush) -> d
     cold = event_pass(True)
 
     # each launch of the step on its own, eagerly, with events between them
-    names = ["encode_kernel"] + (["route_kernel"] if wl.routed else []) + ["attn_kernel"]
+    # routing is two launches (scores, then the top-k selection), timed apart
+    names = ["encode_kernel"] + (["route_kernel", "select_kernel"] if wl.routed else []) + ["attn_kernel"]
     if not fused and wl.value_basis != "identity":
         names.append("upproject_kernel")
     per = {n: 0.0 for n in names}
@@ -166,7 +167,10 @@ def measure(sess, steps: int, warmup: int, graph: bool, fused: bool, flush) -> d
         i += 1
         ev[i].record(stream)
         if wl.routed:
-            sess.route()
+            sess.score()
+            i += 1
+            ev[i].record(stream)
+            sess.select()
             i += 1
             ev[i].record(stream)
         if fused and wl.value_basis != "identity":

@@ -39,7 +39,7 @@ EXPORTED = (
     "kvlr_decode_attn_upproject_noalloc", "kvlr_noalloc_scratch_bytes",
     "kvlr_fit_joint_workspace_bytes", "kvlr_fit_joint_moments", "kvlr_fit_joint_solve",
     "kvlr_fold_joint_decoder", "kvlr_fit_joint", "kvlr_residual_prep_bytes", "kvlr_prepare_residual",
-    "kvlr_check_page_tables",
+    "kvlr_check_page_tables", "kvlr_score_pages", "kvlr_select_pages",
 )
 
 
@@ -82,6 +82,10 @@ _SIG = {
     "kvlr_qproj_width": ([ctypes.POINTER(kvlr_shape)], _I),
     "kvlr_route_pages": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _I, _I,
                           _I, _P, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
+    "kvlr_score_pages": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _I, _P,
+                          _I, _P], _I),
+    "kvlr_select_pages": ([ctypes.POINTER(kvlr_shape), _P, _P, _I, _P, _I, _I, _P, _I, _P, _P, _P, _I,
+                           _P], _I),
     "kvlr_decode_attn": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_cache), _P, _P, _P, _P, _I,
                           _P, _P, _P, _I, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _I, _P], _I),
     "kvlr_decode_attn_upproject": ([ctypes.POINTER(kvlr_shape), ctypes.POINTER(kvlr_factors),
@@ -261,6 +265,21 @@ def kvlr_route_pages(shape, cache, q_proj, seq_lens, page_table, max_pages_per_s
         max_pages_per_seq, topk_num, topk_den, _ptr(k_pages), k_max, _ptr(sel_pages),
         _ptr(sel_counts), _ptr(sel_phys), _ptr(page_scores), _ptr(workspace), ws_bytes, batch,
         _stream(stream)))
+
+
+def kvlr_score_pages(shape, cache, q_proj, seq_lens, page_table, max_pages_per_seq, page_scores,
+                     batch, stream=None):
+    _check("kvlr_score_pages", lib().kvlr_score_pages(
+        ctypes.byref(shape), ctypes.byref(cache), _ptr(q_proj), _ptr(seq_lens), _ptr(page_table),
+        max_pages_per_seq, _ptr(page_scores), batch, _stream(stream)))
+
+
+def kvlr_select_pages(shape, seq_lens, page_table, max_pages_per_seq, page_scores, topk_num,
+                      topk_den, k_pages, k_max, sel_pages, sel_counts, sel_phys, batch, stream=None):
+    _check("kvlr_select_pages", lib().kvlr_select_pages(
+        ctypes.byref(shape), _ptr(seq_lens), _ptr(page_table), max_pages_per_seq, _ptr(page_scores),
+        topk_num, topk_den, _ptr(k_pages), k_max, _ptr(sel_pages), _ptr(sel_counts), _ptr(sel_phys),
+        batch, _stream(stream)))
 
 
 def kvlr_decode_attn(shape, cache, q, q_proj, seq_lens, page_table, max_pages_per_seq, sel_pages,

@@ -20,6 +20,7 @@
 
 #include "kvlr_device.h"
 #include "kvlr_internal.h"
+#include "kvlr_select.h"
 
 #ifndef KVLR_ROUTE_ROLLING
 #define KVLR_ROUTE_ROLLING 1
@@ -140,57 +141,21 @@ __device__ void select_pages(float* scores, int N, int k, int k_max, int max_pag
   for (int j = N + tid; j < max_pages; j += kThreads) scores[j] = -__builtin_huge_valf();
 }
 
-// Exclusive prefix sum of v over the workgroup in thread order; also returns
-// the total. One LDS slot per wave; contains two barriers.
-__device__ inline int block_excl_sum(int v, int* total, int* lds4) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += o;
-  }
-  if (lane == kWave - 1) lds4[wave] = incl;
-  __syncthreads();
-  int before = 0, sum = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = lds4[w];
-    before += (w < wave) ? c : 0;
-    sum += c;
-  }
-  __syncthreads();
-  *total = sum;
-  return before + incl - v;
-}
-
-constexpr int kSelectLds = 4096;  // largest page count selected from LDS
-
 // select_pages for N <= kSelectLds: the order keys are read once into LDS and
-// the radix passes run there. Each pass has its own histogram (all four are
-// cleared up front), so a pass costs one barrier: after it every wave scans
-// the histogram itself and finds the same bin. The passes stop early once
-// the bin holding the k-th largest key is taken whole. The ascending
-// compaction gives thread t the contiguous pages t*per .. t*per+per-1, placed
-// by one block-wide scan of the packed (above, equal) counts. With sel_phys,
-// the sequence's page-table row is read into LDS together with the scores
-// (no extra wait), and each chosen page's physical page is written too.
+// selected there (select_keys_lds). With sel_phys, the sequence's page-table
+// row is read into LDS together with the scores (no extra wait), and each
+// chosen page's physical page is written too.
 __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max_pages,
                                  int32_t* sel, const int32_t* pt, int32_t* sel_phys) {
-  __shared__ uint32_t s_keys[kSelectLds];
-  __shared__ int32_t s_pt[kSelectLds];
-  __shared__ uint4 hist4[4][kWave];  // per pass: 256 bins, lane l owns bins 4l .. 4l+3
-  __shared__ int lds4[kWaves];
+  __shared__ SelectLds s;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
   // The scores are read with coherent device-scope loads through a global
   // (not generic) pointer, eight per thread at a time, all issued before the
   // first is used: one at a time, each would wait out a full memory latency.
   // Indices past N re-read score N-1 and are not kept.
   typedef __attribute__((address_space(1))) float gfloat;
   gfloat* gs = (gfloat*)scores;
-  if (tid < 4 * kWave) (&hist4[0][0])[tid] = make_uint4(0, 0, 0, 0);
+  select_lds_clear(s);
   for (int j0 = 0; j0 < N; j0 += 8 * kThreads) {
     float v[8];
     int32_t ph[8];
@@ -204,85 +169,18 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
     for (int u = 0; u < 8; ++u) {
       const int j = j0 + u * kThreads + tid;
       if (j < N) {
-        s_keys[j] = order_key(v[u]);
-        if (sel_phys) s_pt[j] = ph[u];
+        s.keys[j] = order_key(v[u]);
+        if (sel_phys) s.pt[j] = ph[u];
       }
     }
   }
   __syncthreads();
-
-  const bool take_all = (k >= N);
-  // the kept pages: (key & pmask) > prefix, then the kk lowest-index pages
-  // with (key & pmask) == prefix
-  uint32_t prefix = 0, pmask = 0;
-  int kk = k;
-  if (!take_all && k > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      uint32_t* h = reinterpret_cast<uint32_t*>(&hist4[pass][0]);
-      for (int j = tid; j < N; j += kThreads) {
-        const uint32_t key = s_keys[j];
-        if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // every wave: suffix sums from the top bin down, then the bin holding
-      // the kk-th largest candidate (lane 0's suffix is every candidate, so
-      // some lane qualifies)
-      const uint4 hb = hist4[pass][lane];
-      const uint32_t local = hb.x + hb.y + hb.z + hb.w;
-      uint32_t suf = local;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t o = __shfl_down(suf, off, kWave);
-        if (lane + off < kWave) suf += o;
-      }
-      const uint32_t need = static_cast<uint32_t>(kk);
-      const int top = 63 - __clzll(__ballot(suf >= need));
-      // bins 4l+3 .. 4l of lane l, scanned from the top
-      const uint32_t a3 = suf - local, a2 = a3 + hb.w, a1 = a2 + hb.z, a0 = a1 + hb.y;
-      const int d = (a3 + hb.w >= need) ? 3 : (a2 + hb.z >= need) ? 2 : (a1 + hb.y >= need) ? 1 : 0;
-      const uint32_t above = (d == 3) ? a3 : (d == 2) ? a2 : (d == 1) ? a1 : a0;
-      const uint32_t cnt = (d == 3) ? hb.w : (d == 2) ? hb.z : (d == 1) ? hb.y : hb.x;
-      const uint32_t digit = static_cast<uint32_t>(__builtin_amdgcn_readlane(4 * lane + d, top));
-      const int above_t = __builtin_amdgcn_readlane(static_cast<int>(above), top);
-      const int cnt_t = __builtin_amdgcn_readlane(static_cast<int>(cnt), top);
-      prefix |= digit << shift;
-      pmask |= 255u << shift;
-      kk -= above_t;
-      if (cnt_t == kk) break;  // the whole bin is kept: the same in every wave
+  select_keys_lds(s, N, k, [&](int pos, int j) {
+    if (pos < k_max) {
+      sel[pos] = j;
+      if (sel_phys) sel_phys[pos] = s.pt[j];
     }
-  }
-  const int per = (N + kThreads - 1) / kThreads;
-  const int jb = min(tid * per, N), je = min(jb + per, N);
-  const bool use_eq = !take_all && k > 0;
-  int n_gt = 0, n_eq = 0;
-  for (int j = jb; j < je; ++j) {
-    const uint32_t key = s_keys[j] & pmask;
-    n_gt += (take_all || key > prefix) ? 1 : 0;
-    n_eq += (use_eq && key == prefix) ? 1 : 0;
-  }
-  // one scan of both counts (each sum is at most N <= 4096 < 2^16); the
-  // equal keys are taken in index order, so the threads before this one
-  // took min(kk, equal keys before) of them
-  int tot = 0;
-  const int packed = block_excl_sum((n_gt << 16) | n_eq, &tot, lds4);
-  const int gt_before = packed >> 16, eq_before = packed & 0xffff;
-  int pos = gt_before + min(kk, eq_before);
-  int eq_rank = eq_before;
-  for (int j = jb; j < je; ++j) {
-    const uint32_t key = s_keys[j] & pmask;
-    const bool gt = take_all || key > prefix;
-    const bool eq = use_eq && key == prefix;
-    const bool take = gt || (eq && eq_rank < kk);
-    eq_rank += eq ? 1 : 0;
-    if (take) {
-      if (pos < k_max) {
-        sel[pos] = j;
-        if (sel_phys) sel_phys[pos] = s_pt[j];
-      }
-      ++pos;
-    }
-  }
+  });
   for (int i = k + tid; i < k_max; i += kThreads) {
     sel[i] = -1;
     if (sel_phys) sel_phys[i] = -1;
@@ -296,6 +194,28 @@ __device__ inline void select_top_pages(float* scores, int N, int k, int k_max, 
     select_pages_lds(scores, N, k, k_max, max_pages, sel, pt, sel_phys);
   else
     select_pages(scores, N, k, k_max, max_pages, sel, pt, sel_phys);
+}
+
+// Top-k selection of each (sequence, KV head) pair from the page scores the
+// routing launch wrote (one workgroup per pair, in a launch of its own after
+// the scores). Against selecting in the routing launch's last workgroup of
+// each pair, no routing workgroup waits for its score stores or takes a
+// ticket, and the selections run side by side once every score is written.
+__global__ __launch_bounds__(kThreads) void select_kernel(
+    float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ page_table, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_counts, int32_t* __restrict__ sel_phys,
+    const int32_t* __restrict__ k_pages, int Hkv, int P, int log2P, int max_pages, int topk_num,
+    int topk_den, int k_max) {
+  const int pair = blockIdx.x;
+  const int b = pair / Hkv;
+  const int L = table_len(seq_lens[b], max_pages, P);
+  const int N = (L + P - 1) >> log2P;
+  const int k = pages_to_keep(N, k_pages, b, topk_num, topk_den, k_max);
+  select_top_pages(scores + static_cast<size_t>(pair) * max_pages, N, k, k_max, max_pages,
+                   sel + static_cast<size_t>(pair) * k_max, page_table + static_cast<size_t>(b) * max_pages,
+                   sel_phys ? sel_phys + static_cast<size_t>(pair) * k_max : nullptr);
+  if (threadIdx.x == 0 && sel_counts) sel_counts[pair] = k;
 }
 
 // Scores of one 64-token row: acc[h] = q_hat_h . v + q_tilde_h . c per lane,
@@ -342,7 +262,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
     uint32_t* __restrict__ counters, int32_t* __restrict__ sel, int32_t* __restrict__ sel_counts,
     int32_t* __restrict__ sel_phys, const int32_t* __restrict__ k_pages, int Hq, int Hkv, int P,
     int log2P, int max_pages, int topk_num, int topk_den, int k_max, int rows_per_chunk,
-    int static_splits, int batch, KLayout kl) {
+    int static_splits, int scores_only, int batch, KLayout kl) {
   constexpr int CH = S::CH;
   constexpr int CV = RV / CH;
   constexpr int CK = RK / CH;
@@ -656,6 +576,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
       }
     }
 
+    if (scores_only) {
+      // page scores only (the selection runs where they are read): the
+      // pair's first chunk marks the pages past the sequence
+      if (split == 0)
+        for (int j = ((L + P - 1) >> log2P) + static_cast<int>(threadIdx.x); j < max_pages; j += kThreads)
+          sc[j] = -__builtin_huge_valf();
+      continue;
+    }
     // Ticket: the last chunk of this pair selects its pages.
     wait_stores_done();
     __syncthreads();
@@ -668,16 +596,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
       const int N = (L + P - 1) >> log2P;
       // pages kept: the caller's per-sequence budget, else the fraction
       // (at least one page of a non-empty sequence); at most k_max
-      int k = 0;
-      if (N > 0) {
-        if (k_pages) {
-          k = min(N, max(k_pages[b], 0));
-        } else {
-          const long long want = (static_cast<long long>(N) * topk_num + topk_den - 1) / topk_den;
-          k = static_cast<int>(min(static_cast<long long>(N), max(1LL, want)));
-        }
-        k = min(k, k_max);
-      }
+      const int k = pages_to_keep(N, k_pages, b, topk_num, topk_den, k_max);
       select_top_pages(sc, N, k, k_max, max_pages, sel + static_cast<size_t>(pair) * k_max, pt,
                        sel_phys ? sel_phys + static_cast<size_t>(pair) * k_max : nullptr);
       if (threadIdx.x == 0) {
@@ -701,7 +620,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                            static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                            a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel,
                            a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num,
-                           a.topk_den, a.k_max, a.rows_per_chunk, 0, a.batch, a.kl);
+                           a.topk_den, a.k_max, a.rows_per_chunk, 0, a.scores_only, a.batch, a.kl);
       else
         return hipErrorInvalidValue;
     } else {
@@ -709,7 +628,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
                          a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
-                         a.k_max, a.rows_per_chunk, a.static_splits, a.batch, a.kl);
+                         a.k_max, a.rows_per_chunk, a.static_splits, a.scores_only, a.batch, a.kl);
     }
   } else {
     if constexpr (S::CB == 8) return hipErrorInvalidValue;  // FP8 latents: 64-token pages only
@@ -718,7 +637,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                          static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                          a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel, a.sel_counts,
                          a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den,
-                         a.k_max, a.rows_per_chunk, a.static_splits, a.batch, a.kl);
+                         a.k_max, a.rows_per_chunk, a.static_splits, a.scores_only, a.batch, a.kl);
   }
   return hipGetLastError();
 }
@@ -767,11 +686,32 @@ hipError_t by_g(const RouteArgs& a, hipStream_t s) {
 #endif
 int route_rows_per_chunk(int row_bytes) { return row_bytes <= 8192 ? KVLR_ROUTE_RPC_SMALL : KVLR_ROUTE_RPC; }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+#ifndef KVLR_ROUTE_TICKET
+#define KVLR_ROUTE_TICKET 0  // 1: select in the routing launch (last workgroup of each pair, a ticket)
+#endif
+
+// Routing: the scoring launch, then (unless scores only) the selection
+// launch; with KVLR_ROUTE_TICKET the selection runs inside the scoring launch.
+hipError_t launch_route(const RouteArgs& a0, hipStream_t s) {
+  if (a0.batch == 0) return hipSuccess;
+  RouteArgs a = a0;
+  const bool separate = !a.scores_only && !KVLR_ROUTE_TICKET;
+  if (separate) a.scores_only = 1;
+  hipError_t e;
+  if (a.dm.lat == 2) e = by_g<FP8>(a, s);
+  else if (a.dm.lat == 0) e = by_g<BF16>(a, s);
+  else e = by_g<F32>(a, s);
+  if (e != hipSuccess || !separate) return e;
+  return launch_select(a, s);
+}
+
+hipError_t launch_select(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
-  if (a.dm.lat == 2) return by_g<FP8>(a, s);
-  if (a.dm.lat == 0) return by_g<BF16>(a, s);
-  return by_g<F32>(a, s);
+  const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
+  hipLaunchKernelGGL(select_kernel, dim3(a.batch * a.dm.Hkv), dim3(kThreads), 0, s, a.scores,
+                     a.seq_lens, a.page_table, a.sel, a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hkv,
+                     a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max);
+  return hipGetLastError();
 }
 
 }  // namespace kvlr

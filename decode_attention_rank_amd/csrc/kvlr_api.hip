@@ -356,12 +356,14 @@ kvlr_status kvlr_project_queries(const kvlr_shape* shape, const kvlr_factors* fa
   return hip_status(kvlr::launch_qproj(a, as_stream(stream)));
 }
 
-kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
-                             const int32_t* seq_lens, const int32_t* page_table,
-                             int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
-                             const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
-                             int32_t* sel_counts, int32_t* sel_phys, float* page_scores,
-                             void* workspace, size_t ws_bytes, int32_t batch, void* stream) {
+// Routing: page scores, and unless scores_only the fused top-k selection.
+static kvlr_status route_impl(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
+                              const int32_t* seq_lens, const int32_t* page_table,
+                              int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
+                              const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
+                              int32_t* sel_counts, int32_t* sel_phys, float* page_scores,
+                              void* workspace, size_t ws_bytes, int32_t batch, void* stream,
+                              bool scores_only) {
   Dims dm;
   kvlr_status st = check_shape(shape, &dm);
   if (st != KVLR_OK) return st;
@@ -370,7 +372,9 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   if (!cache || batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
   if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
   if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
-  if (k_pages) {
+  if (scores_only) {
+    // no selection: only the scores are written
+  } else if (k_pages) {
     // per-sequence budgets: the caller keeps each within [0, k_max]
     if (k_max < 1 || k_max > max_pages_per_seq || !aligned16(k_pages)) return KVLR_ERR_INVALID_ARGUMENT;
   } else {
@@ -381,15 +385,18 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   }
   if (batch == 0) return KVLR_OK;
   if (!ok_ptr(cache->v_lat) || !ok_ptr(cache->k_lat) || !ok_ptr(q_proj) || !ok_ptr(seq_lens) ||
-      !ok_ptr(page_table) || !ok_ptr(sel_pages) || !ok_ptr(workspace))
+      !ok_ptr(page_table))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (scores_only ? !ok_ptr(page_scores) : (!ok_ptr(sel_pages) || !ok_ptr(workspace)))
     return KVLR_ERR_INVALID_ARGUMENT;
   if (page_scores && !aligned16(page_scores)) return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_counts && !aligned16(sel_counts)) return KVLR_ERR_INVALID_ARGUMENT;
   if (sel_phys && !aligned16(sel_phys)) return KVLR_ERR_INVALID_ARGUMENT;
   const Plan plan = plan_for(dm, batch, max_pages_per_seq);
-  if (ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
+  if (!scores_only && ws_bytes < plan.total) return KVLR_ERR_WORKSPACE_TOO_SMALL;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   kvlr::RouteArgs a{};
+  a.scores_only = scores_only ? 1 : 0;
   st = residual_layout(dm, cache, &a.kl);
   if (st != KVLR_OK) return st;
   a.dm = dm;
@@ -407,7 +414,7 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.sel_counts = sel_counts;
   a.sel_phys = sel_phys;
   a.scores = page_scores ? page_scores : reinterpret_cast<float*>(ws + plan.route_scores);
-  a.counters = reinterpret_cast<uint32_t*>(ws + plan.route_cnt);
+  a.counters = scores_only ? nullptr : reinterpret_cast<uint32_t*>(ws + plan.route_cnt);
   a.batch = batch;
   const int max_rows = ceil_div(static_cast<long long>(max_pages_per_seq) * dm.P, 64);
   a.rows_per_chunk = kvlr::route_rows_per_chunk(route_row_bytes(dm, dm.RV + dm.RK));
@@ -422,6 +429,66 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
   a.static_splits = (KVLR_ROUTE_STATIC && !a.kl.adaptive && chunks <= kPersistentGrid && max_rows > 0)
                         ? ceil_div(max_rows, a.rows_per_chunk) : 0;
   return hip_status(kvlr::launch_route(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
+                             const int32_t* seq_lens, const int32_t* page_table,
+                             int32_t max_pages_per_seq, int32_t topk_num, int32_t topk_den,
+                             const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
+                             int32_t* sel_counts, int32_t* sel_phys, float* page_scores,
+                             void* workspace, size_t ws_bytes, int32_t batch, void* stream) {
+  return route_impl(shape, cache, q_proj, seq_lens, page_table, max_pages_per_seq, topk_num,
+                    topk_den, k_pages, k_max, sel_pages, sel_counts, sel_phys, page_scores,
+                    workspace, ws_bytes, batch, stream, false);
+}
+
+kvlr_status kvlr_select_pages(const kvlr_shape* shape, const int32_t* seq_lens,
+                              const int32_t* page_table, int32_t max_pages_per_seq,
+                              float* page_scores, int32_t topk_num, int32_t topk_den,
+                              const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
+                              int32_t* sel_counts, int32_t* sel_phys, int32_t batch, void* stream) {
+  Dims dm;
+  kvlr_status st = check_shape(shape, &dm);
+  if (st != KVLR_OK) return st;
+  if (batch < 0) return KVLR_ERR_INVALID_ARGUMENT;
+  if (batch > kMaxBatch) return KVLR_ERR_UNSUPPORTED;
+  if (max_pages_per_seq < 1 || max_pages_per_seq > 65536) return KVLR_ERR_INVALID_ARGUMENT;
+  if (k_pages) {
+    if (k_max < 1 || k_max > max_pages_per_seq || !aligned16(k_pages)) return KVLR_ERR_INVALID_ARGUMENT;
+  } else {
+    if (topk_num < 0 || topk_den < 1) return KVLR_ERR_INVALID_ARGUMENT;
+    const long long bound = (static_cast<long long>(max_pages_per_seq) * topk_num + topk_den - 1) / topk_den;
+    const long long need_k = bound < 1 ? 1 : (bound > max_pages_per_seq ? max_pages_per_seq : bound);
+    if (k_max < need_k || k_max > max_pages_per_seq) return KVLR_ERR_INVALID_ARGUMENT;
+  }
+  if (batch == 0) return KVLR_OK;
+  if (!ok_ptr(seq_lens) || !ok_ptr(page_table) || !ok_ptr(page_scores) || !ok_ptr(sel_pages))
+    return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_counts && !aligned16(sel_counts)) return KVLR_ERR_INVALID_ARGUMENT;
+  if (sel_phys && !aligned16(sel_phys)) return KVLR_ERR_INVALID_ARGUMENT;
+  kvlr::RouteArgs a{};
+  a.dm = dm;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.topk_num = topk_num;
+  a.topk_den = topk_den;
+  a.k_pages = k_pages;
+  a.k_max = k_max;
+  a.sel = sel_pages;
+  a.sel_counts = sel_counts;
+  a.sel_phys = sel_phys;
+  a.scores = page_scores;
+  a.batch = batch;
+  return hip_status(kvlr::launch_select(a, as_stream(stream)));
+}
+
+kvlr_status kvlr_score_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
+                             const int32_t* seq_lens, const int32_t* page_table,
+                             int32_t max_pages_per_seq, float* page_scores, int32_t batch,
+                             void* stream) {
+  return route_impl(shape, cache, q_proj, seq_lens, page_table, max_pages_per_seq, 1, 1, nullptr,
+                    1, nullptr, nullptr, nullptr, page_scores, nullptr, 0, batch, stream, true);
 }
 
 static kvlr_status decode_attn_impl(const kvlr_shape* shape, const kvlr_factors* factors,

@@ -59,9 +59,11 @@ struct RouteArgs {
   int batch;
   int rows_per_chunk;   // 64-token rows per work chunk
   int static_splits;    // > 0: chunks per pair fixed from the table width (no pass over the lengths)
+  int scores_only;      // 1: page scores only, no selection launch (sel outputs unused)
   int grid;             // persistent workgroups
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_select(const RouteArgs& a, hipStream_t s);  // selection alone, from a.scores
 int route_rows_per_chunk(int row_bytes);  // row_bytes: one 64-token row of [v | c] latents
 
 struct AttnArgs {

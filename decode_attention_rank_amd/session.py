@@ -213,6 +213,18 @@ class DecodeSession:
                            self.k_max, self.sel, self.sel_counts, self.sel_phys, self.page_scores,
                            self.workspace, self.ws_bytes, self.wl.batch, stream)
 
+    def score(self, stream=None):
+        """Page scores alone (kvlr_score_pages)."""
+        K.kvlr_score_pages(self.shape, self.kcache, self.q_proj, self.seq_lens_dev, self.page_table,
+                           self.max_pages, self.page_scores, self.wl.batch, stream)
+
+    def select(self, stream=None):
+        """Top-k selection alone from page_scores (kvlr_select_pages)."""
+        K.kvlr_select_pages(self.shape, self.seq_lens_dev, self.page_table, self.max_pages,
+                            self.page_scores, self.wl.topk_num, self.wl.topk_den, self.k_pages,
+                            self.k_max, self.sel, self.sel_counts, self.sel_phys, self.wl.batch,
+                            stream)
+
     def _attn_sel(self, sel, counts, phys):
         use_sel = self.sel if (self.wl.routed and sel) else None
         if counts is None:

@@ -245,6 +245,8 @@ kvlr_status kvlr_append_encode_project(const kvlr_shape* shape, const kvlr_facto
  *                workspace must not overlap.
  * Scores are unscaled; NaN inputs give an unspecified selection.
  * rank_v above 64 returns KVLR_ERR_UNSUPPORTED.
+ * Two launches: the scores (as kvlr_score_pages), then the selection (as
+ * kvlr_select_pages, one workgroup per pair).
  */
 kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
                              const int32_t* seq_lens, const int32_t* page_table,
@@ -252,6 +254,42 @@ kvlr_status kvlr_route_pages(const kvlr_shape* shape, const kvlr_cache* cache, c
                              const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
                              int32_t* sel_counts, int32_t* sel_phys, float* page_scores,
                              void* workspace, size_t ws_bytes, int32_t batch, void* stream);
+
+/*
+ * Page scores alone (KVLR_KEYS_EXACT only): kvlr_route_pages without the
+ * selection, for callers that rank or select pages themselves. BasisKV
+ * English abstract: the value latent's key prediction plus the key-specific
+ * residual score the key pages.
+ *   page_scores  out [batch][H_kv][max_pages_per_seq] float32: S[j] as
+ *                kvlr_route_pages defines it for j < N, -inf past N
+ * Other arguments as for kvlr_route_pages; no workspace is read or written.
+ * The scores are exactly those kvlr_route_pages writes (the same kernel).
+ * rank_v above 64 returns KVLR_ERR_UNSUPPORTED.
+ */
+kvlr_status kvlr_score_pages(const kvlr_shape* shape, const kvlr_cache* cache, const float* q_proj,
+                             const int32_t* seq_lens, const int32_t* page_table,
+                             int32_t max_pages_per_seq, float* page_scores, int32_t batch,
+                             void* stream);
+
+/*
+ * Top-k page selection alone, from page scores (kvlr_score_pages writes
+ * them): the second half of kvlr_route_pages, one workgroup per (sequence,
+ * KV head) pair. BasisKV English abstract: the approximate page scores
+ * decide which key pages are read; the abstract leaves how many to the
+ * caller.
+ *   page_scores  [batch][H_kv][max_pages_per_seq] float32, read; entries
+ *                past each sequence's N pages are set to -inf
+ *   seq_lens, page_table, topk_num, topk_den, k_pages, k_max, sel_pages,
+ *   sel_counts, sel_phys   as for kvlr_route_pages (same k_b, order, padding)
+ * kvlr_route_pages runs kvlr_score_pages and then this selection; the two
+ * calls in a row give exactly its outputs. NaN scores give an unspecified
+ * selection.
+ */
+kvlr_status kvlr_select_pages(const kvlr_shape* shape, const int32_t* seq_lens,
+                              const int32_t* page_table, int32_t max_pages_per_seq,
+                              float* page_scores, int32_t topk_num, int32_t topk_den,
+                              const int32_t* k_pages, int32_t k_max, int32_t* sel_pages,
+                              int32_t* sel_counts, int32_t* sel_phys, int32_t batch, void* stream);
 
 /*
  * Decode attention over the compressed cache. BasisKV English abstract:

@@ -622,3 +622,33 @@ def test_attention_walks_agree(kw):
     for o in outs[1:]:
         for n in ("z", "lse", "o"):
             assert torch.equal(o[n], outs[0][n]), n
+
+
+@pytest.mark.parametrize("kw", [dict(G=4, d=128, rv=64, rk=32, P=64, storage="bf16"),
+                                dict(G=8, d=128, rv=32, rk=32, P=64, storage="bf16", latent="fp8"),
+                                dict(G=2, d=64, rv=32, rk=16, P=32, storage="bf16"),
+                                dict(G=4, d=64, rv=16, rk=32, P=16, storage="f32")],
+                         ids=["bf16-G4", "fp8-G8", "P32", "f32-P16"])
+@pytest.mark.parametrize("budgets", [None, [1, 0, 3, 200]], ids=["fraction", "budgets"])
+def test_score_then_select_equals_routing(kw, budgets):
+    """kvlr_score_pages writes exactly the page scores kvlr_route_pages
+    writes (-inf past each sequence's pages), and kvlr_select_pages after it
+    exactly its page sets, physical pages and counts; ragged lengths, the
+    fraction and per-sequence budgets (0, 1, 3, more than N)."""
+    wl = make_wl(routed=True, **kw)
+    _say("case scores then selection", wl.name, budgets)
+    s = DecodeSession(wl, "cuda", seq_lens=LENS, append_per_seq=5, k_pages=budgets)
+    s.prepare()
+    s.route()
+    torch.cuda.synchronize()
+    names = ("page_scores", "sel", "sel_phys", "sel_counts")
+    ref = {n: getattr(s, n).clone() for n in names}
+    for n in names:
+        getattr(s, n).fill_(-7)
+    s.score()
+    torch.cuda.synchronize()
+    assert torch.equal(s.page_scores, ref["page_scores"])
+    s.select()
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(getattr(s, n), ref[n]), n
