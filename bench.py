@@ -52,6 +52,7 @@ JOINT_SAMPLES = 8192       # calibration samples of the joint decoder fit
 CSRC = os.path.join(ROOT, "decode_attention_rank_amd", "csrc")
 KERNEL_SOURCES = {
     "route_kernel": os.path.join(CSRC, "k_route.hip"),
+    "select_kernel": os.path.join(CSRC, "k_route.hip"),
     "attn_kernel": os.path.join(CSRC, "k_attn.hip"),
     "encode_kernel": os.path.join(CSRC, "k_encode.hip"),
     "moments_mfma_kernel": os.path.join(CSRC, "k_fit.hip"),

@@ -175,7 +175,7 @@ __device__ void select_pages_lds(float* scores, int N, int k, int k_max, int max
     }
   }
   __syncthreads();
-  select_keys_lds(s, N, k, [&](int pos, int j) {
+  select_keys_lds<kThreads>(s, N, k, [&](int pos, int j) {
     if (pos < k_max) {
       sel[pos] = j;
       if (sel_phys) sel_phys[pos] = s.pt[j];
@@ -201,7 +201,10 @@ __device__ inline void select_top_pages(float* scores, int N, int k, int k_max, 
 // the scores). Against selecting in the routing launch's last workgroup of
 // each pair, no routing workgroup waits for its score stores or takes a
 // ticket, and the selections run side by side once every score is written.
-__global__ __launch_bounds__(kThreads) void select_kernel(
+// NT = 1024 serves page counts of 1025 .. kSelectLds (keys in LDS, a quarter
+// of the keys per thread); NT = 256 any count.
+template <int NT>
+__global__ __launch_bounds__(NT) void select_kernel(
     float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_counts, int32_t* __restrict__ sel_phys,
@@ -212,9 +215,48 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int L = table_len(seq_lens[b], max_pages, P);
   const int N = (L + P - 1) >> log2P;
   const int k = pages_to_keep(N, k_pages, b, topk_num, topk_den, k_max);
-  select_top_pages(scores + static_cast<size_t>(pair) * max_pages, N, k, k_max, max_pages,
-                   sel + static_cast<size_t>(pair) * k_max, page_table + static_cast<size_t>(b) * max_pages,
-                   sel_phys ? sel_phys + static_cast<size_t>(pair) * k_max : nullptr);
+  float* sc = scores + static_cast<size_t>(pair) * max_pages;
+  int32_t* so = sel + static_cast<size_t>(pair) * k_max;
+  int32_t* spo = sel_phys ? sel_phys + static_cast<size_t>(pair) * k_max : nullptr;
+  const int32_t* pt = page_table + static_cast<size_t>(b) * max_pages;
+  if constexpr (NT == kThreads) {
+    select_top_pages(sc, N, k, k_max, max_pages, so, pt, spo);
+  } else {
+    // N <= kSelectLds (the host picks NT = 1024 only then): every key and
+    // table entry requested at once, then the selection in LDS
+    __shared__ SelectLds s;
+    const int tid = threadIdx.x;
+    constexpr int PER = kSelectLds / NT;
+    float v[PER];
+    int32_t ph[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = min(u * NT + tid, max(N - 1, 0));
+      v[u] = sc[j];
+      ph[u] = spo ? pt[j] : 0;
+    }
+    select_lds_clear(s);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      if (j < N) {
+        s.keys[j] = order_key(v[u]);
+        s.pt[j] = ph[u];
+      }
+    }
+    __syncthreads();
+    select_keys_lds<NT>(s, N, k, [&](int pos, int j) {
+      if (pos < k_max) {
+        so[pos] = j;
+        if (spo) spo[pos] = s.pt[j];
+      }
+    });
+    for (int i = k + tid; i < k_max; i += NT) {
+      so[i] = -1;
+      if (spo) spo[i] = -1;
+    }
+    for (int j = N + tid; j < max_pages; j += NT) sc[j] = -__builtin_huge_valf();
+  }
   if (threadIdx.x == 0 && sel_counts) sel_counts[pair] = k;
 }
 
@@ -708,9 +750,14 @@ hipError_t launch_route(const RouteArgs& a0, hipStream_t s) {
 hipError_t launch_select(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
-  hipLaunchKernelGGL(select_kernel, dim3(a.batch * a.dm.Hkv), dim3(kThreads), 0, s, a.scores,
-                     a.seq_lens, a.page_table, a.sel, a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hkv,
-                     a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max);
+  if (a.max_pages > 1024 && a.max_pages <= kSelectLds)
+    hipLaunchKernelGGL(select_kernel<1024>, dim3(a.batch * a.dm.Hkv), dim3(1024), 0, s, a.scores,
+                       a.seq_lens, a.page_table, a.sel, a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hkv,
+                       a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max);
+  else
+    hipLaunchKernelGGL(select_kernel<kThreads>, dim3(a.batch * a.dm.Hkv), dim3(kThreads), 0, s,
+                       a.scores, a.seq_lens, a.page_table, a.sel, a.sel_counts, a.sel_phys, a.k_pages,
+                       a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // Exact top-k page selection of one (sequence, KV head) pair in LDS, shared by
-// the routing kernel (the pair's last chunk selects) and the attention kernel
-// (each chunk of a pair selects, then attends its share of the kept pages).
+// the selection launch (one workgroup per pair) and the routing launch's
+// ticket form (the pair's last chunk selects).
 //
 // BasisKV: Value Latents for Communication and Key Routing, English abstract:
 // the approximate page scores decide which key pages are read. The kept set
@@ -16,8 +16,7 @@
 namespace kvlr {
 
 constexpr int kSelectLds = 4096;  // largest page count selected from LDS
-constexpr int kSelectThreads = 256;
-constexpr int kSelectWaves = kSelectThreads / kWave;
+constexpr int kSelectMaxWaves = 16;  // workgroups of up to 1024 threads
 
 // LDS of one selection: the order keys of pages 0..N-1, the same pages'
 // page-table entries (filled by callers that want physical pages), one
@@ -27,12 +26,14 @@ struct SelectLds {
   uint32_t keys[kSelectLds];
   int32_t pt[kSelectLds];
   uint4 hist4[4][kWave];
-  int lds4[kSelectWaves];
+  int lds4[kSelectMaxWaves];
 };
 
-// Exclusive prefix sum of v over the workgroup in thread order; also returns
-// the total. Two barriers.
+// Exclusive prefix sum of v over the workgroup (NT threads) in thread order;
+// also returns the total. Two barriers.
+template <int NT>
 __device__ inline int block_excl_sum(int v, int* total, int* lds4) {
+  static_assert(NT % kWave == 0 && NT / kWave <= kSelectMaxWaves, "workgroup size");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   int incl = v;
@@ -45,7 +46,7 @@ __device__ inline int block_excl_sum(int v, int* total, int* lds4) {
   __syncthreads();
   int before = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < kSelectWaves; ++w) {
+  for (int w = 0; w < NT / kWave; ++w) {
     const int c = lds4[w];
     before += (w < wave) ? c : 0;
     sum += c;
@@ -61,8 +62,9 @@ __device__ inline void select_lds_clear(SelectLds& s) {
 }
 
 // The k largest of s.keys[0..N) (N <= kSelectLds, keys published and the
-// workgroup synchronised, histograms cleared): emit(pos, j) is called once
-// for each kept page j, pos being its rank in ascending page order (0..k-1).
+// workgroup of NT threads synchronised, histograms cleared): emit(pos, j) is
+// called once for each kept page j, pos being its rank in ascending page
+// order (0..k-1).
 // k >= N keeps every page, k <= 0 none. Every thread of the workgroup calls
 // this; it contains barriers. Each pass has its own histogram, so a pass
 // costs one barrier: after it every wave scans the histogram itself and finds
@@ -70,7 +72,7 @@ __device__ inline void select_lds_clear(SelectLds& s) {
 // key is taken whole. The compaction gives thread t the contiguous pages
 // t*per .. t*per+per-1, placed by one block-wide scan of the packed (above,
 // equal) counts.
-template <class Emit>
+template <int NT, class Emit>
 __device__ void select_keys_lds(SelectLds& s, int N, int k, Emit emit) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -83,7 +85,7 @@ __device__ void select_keys_lds(SelectLds& s, int N, int k, Emit emit) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       uint32_t* h = reinterpret_cast<uint32_t*>(&s.hist4[pass][0]);
-      for (int j = tid; j < N; j += kSelectThreads) {
+      for (int j = tid; j < N; j += NT) {
         const uint32_t key = s.keys[j];
         if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
       }
@@ -115,7 +117,7 @@ __device__ void select_keys_lds(SelectLds& s, int N, int k, Emit emit) {
       if (cnt_t == kk) break;  // the whole bin is kept: the same in every wave
     }
   }
-  const int per = (N + kSelectThreads - 1) / kSelectThreads;
+  const int per = (N + NT - 1) / NT;
   const int jb = min(tid * per, N), je = min(jb + per, N);
   const bool use_eq = !take_all && k > 0;
   int n_gt = 0, n_eq = 0;
@@ -128,7 +130,7 @@ __device__ void select_keys_lds(SelectLds& s, int N, int k, Emit emit) {
   // equal keys are taken in index order, so the threads before this one
   // took min(kk, equal keys before) of them
   int tot = 0;
-  const int packed = block_excl_sum((n_gt << 16) | n_eq, &tot, s.lds4);
+  const int packed = block_excl_sum<NT>((n_gt << 16) | n_eq, &tot, s.lds4);
   const int gt_before = packed >> 16, eq_before = packed & 0xffff;
   int pos = gt_before + min(kk, eq_before);
   int eq_rank = eq_before;

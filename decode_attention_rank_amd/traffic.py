@@ -38,6 +38,7 @@ SOURCES = {
     "moments_mfma_kernel": os.path.join(ROOT, "decode_attention_rank_amd", "csrc", "k_fit.hip"),
 }
 SOURCES["merge_kernel"] = SOURCES["attn_kernel"]
+SOURCES["select_kernel"] = SOURCES["route_kernel"]
 COPY_KERNEL_HINT = "neg_kernel"
 
 # one rocprofv3 pass: eight shader-sequencer counters and the GPU-active clock
