@@ -201,8 +201,8 @@ __device__ inline void select_top_pages(float* scores, int N, int k, int k_max, 
 // the scores). Against selecting in the routing launch's last workgroup of
 // each pair, no routing workgroup waits for its score stores or takes a
 // ticket, and the selections run side by side once every score is written.
-// NT = 1024 serves page counts of 1025 .. kSelectLds (keys in LDS, a quarter
-// of the keys per thread); NT = 256 any count.
+// NT = 1024 serves tables of 1025 .. kSelectLds pages and NT = 512 tables of
+// 257 .. 1024 (keys in LDS, at most two per thread); NT = 256 any count.
 template <int NT>
 __global__ __launch_bounds__(NT) void select_kernel(
     float* __restrict__ scores, const int32_t* __restrict__ seq_lens,
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NT) void select_kernel(
     // table entry requested at once, then the selection in LDS
     __shared__ SelectLds s;
     const int tid = threadIdx.x;
-    constexpr int PER = kSelectLds / NT;
+    constexpr int PER = NT == 512 ? 2 : kSelectLds / NT;  // NT = 512: at most 1024 pages
     float v[PER];
     int32_t ph[PER];
 #pragma unroll
@@ -747,11 +747,18 @@ hipError_t launch_route(const RouteArgs& a0, hipStream_t s) {
   return launch_select(a, s);
 }
 
+#ifndef KVLR_SELECT_512
+#define KVLR_SELECT_512 1  // 512-thread selection workgroups for tables of 257 .. 1024 pages
+#endif
 hipError_t launch_select(const RouteArgs& a, hipStream_t s) {
   if (a.batch == 0) return hipSuccess;
   const int log2P = __builtin_ctz(static_cast<unsigned>(a.dm.P));
   if (a.max_pages > 1024 && a.max_pages <= kSelectLds)
     hipLaunchKernelGGL(select_kernel<1024>, dim3(a.batch * a.dm.Hkv), dim3(1024), 0, s, a.scores,
+                       a.seq_lens, a.page_table, a.sel, a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hkv,
+                       a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max);
+  else if (KVLR_SELECT_512 && a.max_pages > 256 && a.max_pages <= 1024)
+    hipLaunchKernelGGL(select_kernel<512>, dim3(a.batch * a.dm.Hkv), dim3(512), 0, s, a.scores,
                        a.seq_lens, a.page_table, a.sel, a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hkv,
                        a.dm.P, log2P, a.max_pages, a.topk_num, a.topk_den, a.k_max);
   else
