@@ -721,10 +721,11 @@ hipError_t by_g(const RouteArgs& a, hipStream_t s) {
 #define KVLR_ROUTE_RPC 64
 #endif
 // Rows of at most 8 KB (rank_v + rank_k <= 64 with bf16 latents, <= 128 with
-// FP8) take twice as many per chunk: a chunk's fixed costs (sequence lookup,
-// query fragments, the hand-off) then weigh less per byte read.
+// FP8) can take a chunk size of their own. With the selection in a launch of
+// its own a chunk's fixed costs are small, and 64 rows measured best for
+// every row size (128 kept only while each chunk ended with a ticket).
 #ifndef KVLR_ROUTE_RPC_SMALL
-#define KVLR_ROUTE_RPC_SMALL (2 * KVLR_ROUTE_RPC)  // rows of at most 8 KB
+#define KVLR_ROUTE_RPC_SMALL KVLR_ROUTE_RPC  // rows of at most 8 KB
 #endif
 int route_rows_per_chunk(int row_bytes) { return row_bytes <= 8192 ? KVLR_ROUTE_RPC_SMALL : KVLR_ROUTE_RPC; }
 
