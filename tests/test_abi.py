@@ -349,3 +349,38 @@ def test_page_table_check_arguments(lib):
     assert call(s, fake, fake, 512, -1, fake) == K.KVLR_ERR_INVALID_ARGUMENT
     assert call(_shape(head_dim=96), fake, fake, 512, 4, fake) == K.KVLR_ERR_UNSUPPORTED
     assert (K.KVLR_TABLE_ERR_PAGE, K.KVLR_TABLE_ERR_LENGTH) == (1, 2)
+
+
+def test_score_and_select_arguments(lib):
+    """kvlr_score_pages and kvlr_select_pages, the two halves of routing,
+    reject bad arguments before any launch."""
+    fake = 1 << 20
+    s = _shape()
+    c = K.make_cache(fake, fake, fake)
+    E = K.KVLR_ERR_INVALID_ARGUMENT
+
+    def score(shape, cache, qp, sl, pt, mp, ps, b):
+        return lib.kvlr_score_pages(ctypes.byref(shape), ctypes.byref(cache), qp, sl, pt, mp, ps, b, None)
+
+    assert score(s, c, fake, fake, fake, 512, None, 16) == E              # scores are the output
+    assert score(s, c, fake, fake, fake, 512, fake + 4, 16) == E          # misaligned
+    assert score(s, c, None, fake, fake, 512, fake, 16) == E              # no query images
+    assert score(s, c, fake, fake, fake, 0, fake, 16) == E                # empty table rows
+    assert score(s, c, fake, fake, fake, 512, fake, 5000) == K.KVLR_ERR_UNSUPPORTED
+    assert score(s, c, fake, fake, fake, 512, fake, 0) == K.KVLR_OK       # empty batch: no-op
+    assert score(_shape(key_mode=K.KVLR_KEYS_LATENT), c, fake, fake, fake, 512, fake, 16) == \
+        K.KVLR_ERR_UNSUPPORTED                                           # routing needs exact keys
+
+    def select(shape, sl, pt, mp, ps, num, den, kp, kmax, sel, cnt, ph, b):
+        return lib.kvlr_select_pages(ctypes.byref(shape), sl, pt, mp, ps, num, den, kp, kmax, sel, cnt,
+                                     ph, b, None)
+
+    assert select(s, fake, fake, 512, fake, 1, 8, None, 63, fake, None, None, 16) == E   # k_max below bound
+    assert select(s, fake, fake, 512, fake, 1, 8, None, 513, fake, None, None, 16) == E  # above the table
+    assert select(s, fake, fake, 512, fake, 1, 0, None, 64, fake, None, None, 16) == E   # zero denominator
+    assert select(s, fake, fake, 512, None, 1, 8, None, 64, fake, None, None, 16) == E   # no scores
+    assert select(s, fake, fake, 512, fake, 1, 8, None, 64, None, None, None, 16) == E   # no page list
+    assert select(s, fake, fake, 512, fake, 1, 8, None, 64, fake, fake + 4, None, 16) == E
+    assert select(s, fake, fake, 512, fake, 1, 8, fake, 0, fake, None, None, 16) == E    # budgets, k_max 0
+    assert select(s, fake, fake, 512, fake, 1, 8, None, 64, fake, None, None, 5000) == K.KVLR_ERR_UNSUPPORTED
+    assert select(s, fake, fake, 512, fake, 1, 8, None, 64, fake, None, None, 0) == K.KVLR_OK
