@@ -321,16 +321,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
   // residual ranks a count that gives every chunk about the same bytes
   auto rpc_of = [&](int g) { return ADAPT ? kl.rpc[g] : rows_per_chunk; };
   auto splits_of = [&](int rows, int g) { return max(1, (rows + rpc_of(g) - 1) / rpc_of(g)); };
-  // With static_splits > 0 (one rank for every head) every pair has that
-  // many chunks, sized for the longest row the page table allows, and a
-  // chunk's pair and split follow from its index alone: the sequence length,
-  // the projected queries and the first rows' page-table entries are then
-  // requested together, with no pass over the batch's lengths first. Chunks
-  // past a sequence's rows score nothing and only take their ticket.
-  const bool fixed = !ADAPT && static_splits > 0;
-  int total;
+  // With static_splits > 0 every pair has a fixed number of chunks, sized
+  // for the longest row the page table allows (static_splits chunks; with
+  // per-head ranks static_splits is the table's row count and each head
+  // splits it by its own chunk size), and a chunk's pair and split follow
+  // from its index alone: the sequence length, the projected queries and the
+  // first rows' page-table entries are then requested together, with no pass
+  // over the batch's lengths first. Chunks past a sequence's rows score
+  // nothing.
+  const bool fixed = static_splits > 0;
+  int total, per_b = 0;
   if (fixed) {
-    total = batch * Hkv * static_splits;
+    if constexpr (!ADAPT) {
+      per_b = Hkv * static_splits;
+    } else {
+      for (int g = 0; g < Hkv; ++g) per_b += splits_of(static_splits, g);
+    }
+    total = batch * per_b;
   } else {
     build_chunk_prefix(batch, s_base, [&](int b) {
       const int rows = (table_len(seq_lens[b], max_pages, P) + kWave - 1) / kWave;
@@ -345,9 +352,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     int b, local;
     if (fixed) {
-      const int pr = w / static_splits;
-      b = pr / Hkv;
-      local = w - b * Hkv * static_splits;
+      b = w / per_b;
+      local = w - b * per_b;
     } else {
       b = __builtin_amdgcn_readfirstlane(find_sequence(s_base, batch, w));
       local = __builtin_amdgcn_readfirstlane(w - s_base[b]);
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
     const int L = table_len(seq_lens[b], max_pages, P);
     const int nrows = (L + kWave - 1) / kWave;
     int g, nsplit;
-    if (fixed) {
+    if (fixed && !ADAPT) {
       nsplit = static_splits;
       g = local / nsplit;
       local -= g * nsplit;
@@ -364,11 +370,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KVLR_R
       g = local / nsplit;
       local -= g * nsplit;
     } else {
+      const int split_rows = fixed ? static_splits : nrows;
       g = 0;
-      nsplit = splits_of(nrows, 0);
+      nsplit = splits_of(split_rows, 0);
       while (local >= nsplit) {
         local -= nsplit;
-        nsplit = splits_of(nrows, ++g);
+        nsplit = splits_of(split_rows, ++g);
       }
     }
     // every value here is the same across the workgroup; saying so keeps the
@@ -662,7 +669,7 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
                            static_cast<const uint8_t*>(a.v_lat), static_cast<const uint8_t*>(a.k_lat),
                            a.q_proj, a.seq_lens, a.page_table, a.scores, a.counters, a.sel,
                            a.sel_counts, a.sel_phys, a.k_pages, a.dm.Hq, a.dm.Hkv, a.dm.P, log2P, a.max_pages, a.topk_num,
-                           a.topk_den, a.k_max, a.rows_per_chunk, 0, a.scores_only, a.batch, a.kl);
+                           a.topk_den, a.k_max, a.rows_per_chunk, a.static_splits, a.scores_only, a.batch, a.kl);
       else
         return hipErrorInvalidValue;
     } else {

@@ -426,8 +426,9 @@ static kvlr_status route_impl(const kvlr_shape* shape, const kvlr_cache* cache, 
   a.grid = static_cast<int>(chunks < kPersistentGrid ? chunks : kPersistentGrid);
   // every pair sized for the widest table row when that fits one workgroup
   // per chunk: chunks of shorter sequences then only take their ticket
-  a.static_splits = (KVLR_ROUTE_STATIC && !a.kl.adaptive && chunks <= kPersistentGrid && max_rows > 0)
-                        ? ceil_div(max_rows, a.rows_per_chunk) : 0;
+  // (with per-head ranks the kernel splits the table's rows per head)
+  a.static_splits = (KVLR_ROUTE_STATIC && chunks <= kPersistentGrid && max_rows > 0)
+                        ? (a.kl.adaptive ? max_rows : ceil_div(max_rows, a.rows_per_chunk)) : 0;
   return hip_status(kvlr::launch_route(a, as_stream(stream)));
 }
 

@@ -58,7 +58,8 @@ struct RouteArgs {
   KLayout kl;
   int batch;
   int rows_per_chunk;   // 64-token rows per work chunk
-  int static_splits;    // > 0: chunks per pair fixed from the table width (no pass over the lengths)
+  int static_splits;    // > 0: chunks per pair fixed from the table width (no pass over the lengths);
+                        // with per-head ranks, the table's rows (each head splits them itself)
   int scores_only;      // 1: page scores only, no selection launch (sel outputs unused)
   int grid;             // persistent workgroups
 };
